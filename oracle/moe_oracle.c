@@ -1,0 +1,327 @@
+/*
+ * moe_oracle.c -- plain, slow, double-precision reference of one routed-expert
+ * MoE layer at decode.
+ *
+ * TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg may load or run this code.  It shares no source with the
+ * GPU library: it reads the packed bytes through its own indexing below.
+ *
+ * What one layer computes, per token (sources are the pages' own wording,
+ * restated):
+ *   - router logits from an 8-bit router held in memory
+ *       (TurboFieldfare article, "Arsitektur eksekusi ..." and
+ *        "Proses pembuatan token": the router is 8-bit and runs on resident
+ *        weights; Colibri analysis report section 2, "Route")
+ *   - exact top-8 selection of routed experts
+ *       (Inferno README, "Current Scope"; TurboFieldfare, "Proses pembuatan
+ *        token": the 8 top expert ids; Colibri analysis section 3: exact
+ *        routing semantics by default)
+ *   - gate weights renormalised over the selected experts (softmax over the
+ *     selected logits; the pages name no formula, this is the plainest reading)
+ *   - per selected expert, its gate, up and down matrices (Inferno README,
+ *     "Model": each routed expert's gate/up/down stored next to each other),
+ *     dequantised on use from affine 4-bit, group 64, one scale and one bias
+ *     per group (TurboFieldfare, "Arsitektur eksekusi ...": MLX affine 4-bit
+ *     group 64; Colibri README, "What's implemented": dequant-on-use), then
+ *     h = silu(G x) * (U x) and y_e = D h
+ *   - an always-resident shared expert whose output is added to the routed
+ *     outputs (TurboFieldfare, "Proses pembuatan token": shared-expert branch,
+ *     then shared and routed outputs combined)
+ *   - y = sum_j w_j y_{S_j} + y_shared
+ *
+ * Parity status of each function is listed in its comment; all are pinned by
+ * tests/test_oracle_pins.py except where it says "parity unpinned".
+ *
+ * Packed expert record (hidden H, intermediate I, both multiples of 64).
+ * G and U are [I][H] (input dim H), D is [H][I] (input dim I).  Within a
+ * 16-byte run of 32 inputs, input 2m is the low nibble of byte m and input
+ * 2m+1 its high nibble.
+ *
+ *   nibble region, 3*H*I/2 bytes, I/32 blocks of 48*H bytes; block b holds
+ *   rows i in [32b, 32b+32):
+ *     +0      GU tile: for chunk c < H/32, for tile row r < 64: 16 bytes =
+ *             inputs [32c, 32c+32) of G row 32b+r (r < 32) or U row
+ *             32b+r-32 (r >= 32)
+ *     +32*H   D block: for output row o < H: 16 bytes = D[o][32b .. 32b+32)
+ *   scale/bias region at 3*H*I/2, I/64 slabs of 12*H bytes; slab g covers
+ *   i in [64g, 64g+64):
+ *     +0      (scale, bias) fp16 pairs of GU tile 2g:   [group h < H/64][row r < 64]
+ *     +4*H    (scale, bias) fp16 pairs of GU tile 2g+1: same order
+ *     +8*H    (scale, bias) fp16 pairs of D[o][64g .. 64g+64) for o < H
+ *   A weight is  W = scale * q + bias,  q the nibble in 0..15.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads used by the row loops; returns the count in effect (1 without OpenMP). */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+/* ---- number formats --------------------------------------------------- */
+
+/* IEEE binary16 -> double, exactly (normals, subnormals, zeros, inf, nan). */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1F;
+    int mant = h & 0x3FF;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)mant, -24);                 /* subnormal: m * 2^-24 */
+    else if (expo == 31)
+        v = mant ? NAN : INFINITY;
+    else
+        v = ldexp((double)(mant + 1024), expo - 25);  /* (1024+m) * 2^(e-15-10) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double, exactly: bf16 is the top half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Activations in the layer's dtype (0 = fp32, 1 = bf16 bits) -> double. */
+void oracle_act_to_f64(int act_dtype, const void *x, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        if (act_dtype == 0)
+            out[i] = (double)((const float *)x)[i];
+        else
+            out[i] = oracle_bf16_to_f64(((const uint16_t *)x)[i]);
+    }
+}
+
+/* ---- packed record indexing (see the header comment) ------------------- */
+
+static int nibble_at(const uint8_t *rec, size_t byte_off, int elem)
+{
+    uint8_t byte = rec[byte_off];
+    return (elem & 1) ? (byte >> 4) : (byte & 0x0F);
+}
+
+static size_t sb_region(int H, int I) { return (size_t)3 * H * I / 2; }
+
+/* quantised value of gate (which = 0) or up (which = 1) at row i, input k */
+static int q_gate_up(const uint8_t *rec, int H, int which, int i, int k)
+{
+    int b = i / 32, r = i % 32 + 32 * which, c = k / 32, e = k % 32;
+    size_t off = (size_t)48 * H * b + (size_t)c * 1024 + (size_t)r * 16 + e / 2;
+    return nibble_at(rec, off, e);
+}
+
+static int q_down(const uint8_t *rec, int H, int o, int i)
+{
+    int b = i / 32, e = i % 32;
+    size_t off = (size_t)48 * H * b + (size_t)32 * H + (size_t)o * 16 + e / 2;
+    return nibble_at(rec, off, e);
+}
+
+static void sb_read(const uint8_t *rec, size_t off, double *s, double *bias)
+{
+    uint16_t sv, bv;
+    memcpy(&sv, rec + off, 2);
+    memcpy(&bv, rec + off + 2, 2);
+    *s = oracle_f16_to_f64(sv);
+    *bias = oracle_f16_to_f64(bv);
+}
+
+/* scale/bias of gate (which = 0) or up (which = 1) row i, input group h */
+static void sb_gate_up(const uint8_t *rec, int H, int I, int which, int i, int h,
+                       double *s, double *bias)
+{
+    int g = i / 64, tile = (i / 32) % 2, r = i % 32 + 32 * which;
+    size_t off = sb_region(H, I) + (size_t)12 * H * g + (size_t)4 * H * tile
+               + (size_t)h * 256 + (size_t)r * 4;
+    sb_read(rec, off, s, bias);
+}
+
+static void sb_down(const uint8_t *rec, int H, int I, int o, int g, double *s, double *bias)
+{
+    size_t off = sb_region(H, I) + (size_t)12 * H * g + (size_t)8 * H + (size_t)o * 4;
+    sb_read(rec, off, s, bias);
+}
+
+size_t oracle_record_bytes(int H, int I)
+{
+    return sb_region(H, I) + (size_t)(I / 64) * 12 * H;
+}
+
+/* Dense dequantisation of one record: W = scale * q + bias per 64-group of the
+ * input dim.  G, U are [I][H] row-major, D is [H][I].  Pinned against an
+ * independently written packer and its dense source matrices. */
+void oracle_dequant_record(int H, int I, const uint8_t *rec, double *G, double *U, double *D)
+{
+    double s, bias;
+    for (int i = 0; i < I; ++i)
+        for (int k = 0; k < H; ++k) {
+            sb_gate_up(rec, H, I, 0, i, k / 64, &s, &bias);
+            G[(size_t)i * H + k] = s * q_gate_up(rec, H, 0, i, k) + bias;
+            sb_gate_up(rec, H, I, 1, i, k / 64, &s, &bias);
+            U[(size_t)i * H + k] = s * q_gate_up(rec, H, 1, i, k) + bias;
+        }
+    for (int o = 0; o < H; ++o)
+        for (int i = 0; i < I; ++i) {
+            sb_down(rec, H, I, o, i / 64, &s, &bias);
+            D[(size_t)o * I + i] = s * q_down(rec, H, o, i) + bias;
+        }
+}
+
+/* ---- the layer --------------------------------------------------------- */
+
+/* Router: logit_e = scale_e * sum_h q[e][h] * x_h  (8-bit rows, one fp16 scale
+ * per row, scale applied after the sum).  TurboFieldfare article, "Arsitektur
+ * eksekusi ...": the router is 8-bit. */
+void oracle_router_logits(int H, int E, const int8_t *rq, const uint16_t *rs,
+                          const double *x, double *logits)
+{
+    #pragma omp parallel for schedule(static)
+    for (int e = 0; e < E; ++e) {
+        double acc = 0.0;
+        for (int h = 0; h < H; ++h)
+            acc += (double)rq[(size_t)e * H + h] * x[h];
+        logits[e] = oracle_f16_to_f64(rs[e]) * acc;
+    }
+}
+
+/* Exact top-k: the first k experts in the order (logit descending, then id
+ * ascending).  Inferno README "Current Scope" and TurboFieldfare "Proses
+ * pembuatan token" fix k = 8 and exact (not approximate) selection. */
+void oracle_select_topk(int E, int k, const double *logits, int32_t *ids)
+{
+    char *taken = (char *)calloc((size_t)E, 1);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || logits[e] > logits[best])
+                best = e;            /* strict '>' keeps the lower id on ties */
+        }
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    free(taken);
+}
+
+/* Gate weights renormalised over the selected experts:
+ * w_j = exp(l_j - m) / sum_{j'} exp(l_j' - m), m = max of the selected logits.
+ * (Equal to a softmax over all experts, renormalised over the selection.) */
+void oracle_softmax_gates(int k, const double *sel_logits, double *w)
+{
+    double m = sel_logits[0], z = 0.0;
+    for (int j = 1; j < k; ++j)
+        if (sel_logits[j] > m)
+            m = sel_logits[j];
+    for (int j = 0; j < k; ++j) {
+        w[j] = exp(sel_logits[j] - m);
+        z += w[j];
+    }
+    for (int j = 0; j < k; ++j)
+        w[j] /= z;
+}
+
+double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* One expert's SwiGLU FFN on a dequantised-on-use record:
+ *   g = G x, u = U x, h = silu(g) * u, y = D h.
+ * Each 64-input group's scale and bias are decoded once and applied to every
+ * element of the group as W = scale * q + bias.  Rows are independent, so the
+ * row loops may run on several threads (OpenMP) without changing any sum.
+ * Optional outputs g, u, h (length I) for the pins; pass NULL to skip. */
+void oracle_expert_ffn(int H, int I, const uint8_t *rec, const double *x, double *y,
+                       double *g_out, double *u_out, double *h_out)
+{
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    #pragma omp parallel for schedule(static)
+    for (int i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0, sg, bg, su, bu;
+        for (int grp = 0; grp < H / 64; ++grp) {
+            sb_gate_up(rec, H, I, 0, i, grp, &sg, &bg);
+            sb_gate_up(rec, H, I, 1, i, grp, &su, &bu);
+            for (int k = 64 * grp; k < 64 * grp + 64; ++k) {
+                g += (sg * q_gate_up(rec, H, 0, i, k) + bg) * x[k];
+                u += (su * q_gate_up(rec, H, 1, i, k) + bu) * x[k];
+            }
+        }
+        h[i] = oracle_silu(g) * u;
+        if (g_out) g_out[i] = g;
+        if (u_out) u_out[i] = u;
+        if (h_out) h_out[i] = h[i];
+    }
+    #pragma omp parallel for schedule(static)
+    for (int o = 0; o < H; ++o) {
+        double acc = 0.0, s, bias;
+        for (int grp = 0; grp < I / 64; ++grp) {
+            sb_down(rec, H, I, o, grp, &s, &bias);
+            for (int i = 64 * grp; i < 64 * grp + 64; ++i)
+                acc += (s * q_down(rec, H, o, i) + bias) * h[i];
+        }
+        y[o] = acc;
+    }
+    free(h);
+}
+
+/* y = sum_j w_j * y_routed[j] + y_shared, summed in the order j = 0..k-1 and
+ * then the shared expert (weight 1, no gate).  y_shared may be NULL. */
+void oracle_combine(int k, int H, const double *w, const double *y_routed,
+                    const double *y_shared, double *y)
+{
+    for (int o = 0; o < H; ++o) {
+        double acc = 0.0;
+        for (int j = 0; j < k; ++j)
+            acc += w[j] * y_routed[(size_t)j * H + o];
+        if (y_shared)
+            acc += y_shared[o];
+        y[o] = acc;
+    }
+}
+
+/* A whole layer for one token, with every routed record reachable at
+ * pool + e * record_bytes(H, I).  shared may be NULL (no shared expert).
+ * Writes ids[k], w[k], y[H] and, if logits != NULL, logits[E]. */
+void oracle_layer_token(int H, int E, int I, int k, int I_shared,
+                        const int8_t *rq, const uint16_t *rs,
+                        const uint8_t *pool, const uint8_t *shared,
+                        const double *x, int32_t *ids, double *w, double *y,
+                        double *logits)
+{
+    double *lg = (double *)malloc(sizeof(double) * (size_t)E);
+    double *sel = (double *)malloc(sizeof(double) * (size_t)k);
+    double *yr = (double *)malloc(sizeof(double) * (size_t)k * H);
+    double *ys = shared ? (double *)malloc(sizeof(double) * (size_t)H) : NULL;
+    size_t rb = oracle_record_bytes(H, I);
+
+    oracle_router_logits(H, E, rq, rs, x, lg);
+    oracle_select_topk(E, k, lg, ids);
+    for (int j = 0; j < k; ++j)
+        sel[j] = lg[ids[j]];
+    oracle_softmax_gates(k, sel, w);
+    for (int j = 0; j < k; ++j)
+        oracle_expert_ffn(H, I, pool + (size_t)ids[j] * rb, x, yr + (size_t)j * H,
+                          NULL, NULL, NULL);
+    if (shared)
+        oracle_expert_ffn(H, I_shared, shared, x, ys, NULL, NULL, NULL);
+    oracle_combine(k, H, w, yr, ys, y);
+    if (logits)
+        memcpy(logits, lg, sizeof(double) * (size_t)E);
+    free(lg); free(sel); free(yr); free(ys);
+}

@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in copies of the oracle and check a pin catches each.
+
+Each mutant is a textual edit of oracle/moe_oracle.c compiled into a temporary
+library; the real oracle is untouched.  A mutant that passes every pin would
+mean the pins cannot tell that mistake from the right answer.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle.build as ob
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")
+
+MUTANTS = {
+    "nibble_order_swapped": ("return (elem & 1) ? (byte >> 4) : (byte & 0x0F);",
+                             "return (elem & 1) ? (byte & 0x0F) : (byte >> 4);"),
+    "gate_up_rows_swapped": ("int b = i / 32, r = i % 32 + 32 * which, c = k / 32, e = k % 32;",
+                             "int b = i / 32, r = i % 32 + 32 * (1 - which), c = k / 32, e = k % 32;"),
+    "chunk_stride": ("(size_t)c * 1024", "(size_t)c * 512"),
+    "down_bias_dropped": ("acc += (s * q_down(rec, H, o, i) + bias) * h[i];",
+                          "acc += (s * q_down(rec, H, o, i)) * h[i];"),
+    "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    "gate_up_roles_swapped": ("h[i] = oracle_silu(g) * u;", "h[i] = oracle_silu(u) * g;"),
+    "topk_tie_breaks_high_id": ("logits[e] > logits[best]", "logits[e] >= logits[best]"),
+    "gates_not_normalised": ("w[j] /= z;", "w[j] /= (double)k;"),
+    "router_scale_dropped": ("logits[e] = oracle_f16_to_f64(rs[e]) * acc;", "logits[e] = acc;"),
+    "f16_subnormal_exponent": ("v = ldexp((double)mant, -24);", "v = ldexp((double)mant, -25);"),
+    "gu_sb_tile_ignored": ("(size_t)4 * H * tile", "(size_t)4 * H * 0 * tile"),
+    "gu_sb_group_stride": ("(size_t)h * 256", "(size_t)h * 64"),
+    "down_sb_slab_ignored": ("(size_t)12 * H * g + (size_t)8 * H + (size_t)o * 4",
+                             "(size_t)8 * H + (size_t)o * 4"),
+    "down_block_offset": ("(size_t)48 * H * b + (size_t)32 * H + (size_t)o * 16",
+                          "(size_t)48 * H * b + (size_t)16 * H + (size_t)o * 16"),
+    "shared_dropped": ("acc += y_shared[o];", "acc += 0.0 * y_shared[o];"),
+    "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+}
+
+
+@pytest.fixture(scope="module")
+def src_text():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, src_text, tmp_path):
+    old, new = MUTANTS[name]
+    assert src_text.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src_text.replace(old, new)
+    src = tmp_path / "mut.c"
+    src.write_text(mutated)
+    lib = ob.build(src=str(src), out=str(tmp_path / "libmut.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches mutant {name}"
