@@ -1,0 +1,75 @@
+// moe_internal.h -- launch arguments shared by the host side of the library
+// (moe_layer.hip) and its kernels (moe_kernels.hip).  Not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kBlock = 256;        // threads per workgroup (4 waves of 64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kRouterRowsPerBlock = kWaves;  // one router row per wave
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxHidden = 8192;
+constexpr int kHParts = 1;         // fp16 parts used for the intermediate h
+
+// Prepared activations of one vector of length n (n multiple of 64):
+//   pairs [n/8][parts][4] dwords  (fp16 pairs, see moe_device.h)
+//   K     [n/64] float            1024 * sum of the fp16 values per group
+//   X     [n/64] float            sum of the unscaled values per group
+//   inv   float                   2^-e, e the vector's scale exponent
+struct RouteArgs {
+    const void* x;           // [T][H] activations
+    const int8_t* rq;        // [E][H]
+    const uint16_t* rs;      // [E] fp16
+    float* logits;           // [T][E]
+    uint32_t* ctr;           // [T] arrival counters (zero between calls)
+    int32_t* ids;            // [T][k]
+    float* w;                // [T][k]
+    uint32_t* xpairs;        // [T][H/2*XP] (written only if prep != 0)
+    float* xK;               // [T][H/64]
+    float* xX;               // [T][H/64]
+    float* xinv;             // [T]
+    int H, E, k, prep;
+};
+
+struct FfnArgs {
+    const uint8_t* experts;  // E records
+    const uint8_t* shared;   // shared record or nullptr
+    size_t rec_bytes;
+    const int32_t* ids;      // [T][k]
+    const float* w;          // [T][k] (fused combine only)
+    const uint32_t* xpairs;  // prepared x, as in RouteArgs
+    const float* xK;
+    const float* xX;
+    const float* xinv;
+    uint32_t* hpairs;        // [T][k+1][blk_max][16*kHParts]
+    float* hK;               // [T][k+1][blk_max]
+    float* hHs;              // [T][k+1][blk_max]
+    float* hinv;             // [T][k+1][blk_max]
+    float* dpart;            // [T][n_otiles][n_items][64]
+    uint32_t* dctr;          // [T][n_otiles]
+    float* y;                // [T][H] fused output (or nullptr)
+    float* eo;               // [T][k+1][H] per-expert outputs (or nullptr)
+    uint32_t* err;           // device error word
+    int H, I, Is, E, k;
+    int blk_r;               // I/32  (gate/up units per routed expert)
+    int blk_s;               // Is/32 (gate/up units of the shared expert)
+    int blk_max;             // max(blk_r, blk_s)
+    int gpw_gu;              // input groups per wave in the gate/up kernel
+    int n_otiles;            // H/64
+    int n_items;             // down work items per output tile: k + shared k-slices
+    int gi;                  // input groups (of I) per down item
+    int gpw_dn;              // input groups per wave in the down kernel
+};
+
+struct CombineArgs {
+    const float* eo;  // [T][k+1][H]
+    const float* w;   // [T][k]
+    void* y;          // [T][H]
+    int H, k, T, y_bf16;
+};
+
+}  // namespace moe

@@ -1,0 +1,415 @@
+// moe_layer.hip -- host side of libmoe_layer.so: handle, validation, workspace
+// layout and kernel launches behind the C ABI declared in include/moe_layer.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "moe_internal.h"
+#include "../../include/moe_layer.h"
+
+namespace moe {
+hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s);
+hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_layer {
+    moe_layer_desc d;
+    moe_layer_weights w;
+    size_t rec_bytes;
+    size_t shared_rec_bytes;
+    int NG;        // H / 64
+    int blk_r;     // I / 32
+    int blk_s;     // Is / 32
+    int blk_max;
+    int xparts;    // fp16 parts per activation: 1 for bf16, 2 for fp32
+    int gi;        // input groups per down item
+    int n_items;   // down items per output tile
+    int n_otiles;  // H / 64
+    int gpw_gu, gpw_dn;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// ---- per-launch event timing (moe_profile_*) ----
+enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4 };
+struct ProfRec {
+    int kid;
+    hipEvent_t a, b;
+};
+std::vector<ProfRec> g_prof;
+size_t g_prof_n = 0;
+bool g_prof_on = false;
+
+template <typename F>
+hipError_t timed(int kid, hipStream_t s, F&& launch) {
+    ProfRec* r = nullptr;
+    if (g_prof_on && g_prof_n < g_prof.size()) {
+        r = &g_prof[g_prof_n++];
+        r->kid = kid;
+        (void)hipEventRecord(r->a, s);
+    }
+    hipError_t e = launch();
+    if (r) (void)hipEventRecord(r->b, s);
+    return e;
+}
+
+moe_status fail(moe_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t err, rctr, dctr, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, total;
+};
+
+WsLayout ws_layout(const moe_layer* L, int T) {
+    WsLayout o{};
+    const int H = L->d.hidden, k = L->d.top_k;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    o.err = take(4);
+    o.rctr = take((size_t)T * 4);
+    o.dctr = take((size_t)T * L->n_otiles * 4);
+    o.xpairs = take((size_t)T * (H / 2) * L->xparts * 4);
+    o.xK = take((size_t)T * L->NG * 4);
+    o.xX = take((size_t)T * L->NG * 4);
+    o.xinv = take((size_t)T * 4);
+    o.logits = take((size_t)T * L->d.n_experts * 4);
+    const size_t nslot = (size_t)T * (k + 1) * L->blk_max;
+    o.hpairs = take(nslot * 16 * kHParts * 4);
+    o.hK = take(nslot * 4);
+    o.hHs = take(nslot * 4);
+    o.hinv = take(nslot * 4);
+    o.dpart = take((size_t)T * L->n_otiles * L->n_items * 64 * 4);
+    o.total = off;
+    return o;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_device_ptr(const void* p, const char* name) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_ERR_ARG, std::string(name) + " is not a HIP allocation");
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(MOE_ERR_ARG, std::string(name) + " is not device memory");
+    return MOE_OK;
+}
+
+RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, uint8_t* ws,
+                     const WsLayout& o, int prep) {
+    RouteArgs a{};
+    a.x = x;
+    a.rq = L->w.router_q;
+    a.rs = L->w.router_scale;
+    a.logits = (float*)(ws + o.logits);
+    a.ctr = (uint32_t*)(ws + o.rctr);
+    a.ids = ids;
+    a.w = w;
+    a.xpairs = (uint32_t*)(ws + o.xpairs);
+    a.xK = (float*)(ws + o.xK);
+    a.xX = (float*)(ws + o.xX);
+    a.xinv = (float*)(ws + o.xinv);
+    a.H = L->d.hidden;
+    a.E = L->d.n_experts;
+    a.k = L->d.top_k;
+    a.prep = prep;
+    return a;
+}
+
+FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t* ws,
+                 const WsLayout& o, float* y, float* eo) {
+    FfnArgs a{};
+    a.experts = L->w.experts;
+    a.shared = L->w.shared;
+    a.rec_bytes = L->rec_bytes;
+    a.ids = ids;
+    a.w = w;
+    a.xpairs = (const uint32_t*)(ws + o.xpairs);
+    a.xK = (const float*)(ws + o.xK);
+    a.xX = (const float*)(ws + o.xX);
+    a.xinv = (const float*)(ws + o.xinv);
+    a.hpairs = (uint32_t*)(ws + o.hpairs);
+    a.hK = (float*)(ws + o.hK);
+    a.hHs = (float*)(ws + o.hHs);
+    a.hinv = (float*)(ws + o.hinv);
+    a.dpart = (float*)(ws + o.dpart);
+    a.dctr = (uint32_t*)(ws + o.dctr);
+    a.y = y;
+    a.eo = eo;
+    a.err = (uint32_t*)(ws + o.err);
+    a.H = L->d.hidden;
+    a.I = L->d.inter;
+    a.Is = L->d.shared_inter;
+    a.E = L->d.n_experts;
+    a.k = L->d.top_k;
+    a.blk_r = L->blk_r;
+    a.blk_s = L->blk_s;
+    a.blk_max = L->blk_max;
+    a.gpw_gu = L->gpw_gu;
+    a.n_otiles = L->n_otiles;
+    a.n_items = L->n_items;
+    a.gi = L->gi;
+    a.gpw_dn = L->gpw_dn;
+    return a;
+}
+
+moe_status check_call(const moe_layer* L, const void* x, int32_t T, const void* ws) {
+    if (!L) return fail(MOE_ERR_ARG, "null layer handle");
+    if (!x) return fail(MOE_ERR_ARG, "null activations");
+    if (!ws) return fail(MOE_ERR_ARG, "null workspace");
+    if (T <= 0 || T > (1 << 20)) return fail(MOE_ERR_ARG, "n_tokens out of range");
+    if (!aligned(x, 16) || !aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "x needs 16-byte and workspace 256-byte alignment");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_expert_record_bytes(int32_t hidden, int32_t inter) {
+    if (hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64) return 0;
+    return (size_t)27 * hidden * inter / 16;
+}
+
+moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w,
+                            moe_layer_t* out) {
+    if (!desc || !w || !out) return fail(MOE_ERR_ARG, "null argument");
+    *out = nullptr;
+    const moe_layer_desc& d = *desc;
+    if (d.group != 64) return fail(MOE_ERR_SHAPE, "group must be 64");
+    if (d.hidden <= 0 || d.hidden % 64 || d.hidden > kMaxHidden)
+        return fail(MOE_ERR_SHAPE, "hidden must be a positive multiple of 64, at most 8192");
+    if (d.inter <= 0 || d.inter % 64 || d.inter > 16384)
+        return fail(MOE_ERR_SHAPE, "inter must be a positive multiple of 64, at most 16384");
+    if (d.shared_inter < 0 || d.shared_inter % 64 || d.shared_inter > 16384)
+        return fail(MOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 64, at most 16384");
+    if (d.n_experts < 1 || d.n_experts > kMaxExperts)
+        return fail(MOE_ERR_SHAPE, "n_experts must be in 1..1024");
+    if (d.top_k < 1 || d.top_k > kMaxTopK || d.top_k > d.n_experts)
+        return fail(MOE_ERR_SHAPE, "top_k must be in 1..min(16, n_experts)");
+    if (d.act_dtype != MOE_F32 && d.act_dtype != MOE_BF16)
+        return fail(MOE_ERR_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
+    if (d.gate_fn != MOE_SOFTMAX_TOPK)
+        return fail(MOE_ERR_STATE, "only MOE_SOFTMAX_TOPK is available");
+    if (d.n_slots != 0) return fail(MOE_ERR_STATE, "the expert slot cache is not available");
+    if (w->host_pool || w->slots)
+        return fail(MOE_ERR_ARG, "host_pool/slots must be NULL when n_slots = 0");
+    if (!w->router_q || !w->router_scale || !w->experts)
+        return fail(MOE_ERR_ARG, "router_q, router_scale and experts are required");
+    if ((d.shared_inter > 0) != (w->shared != nullptr))
+        return fail(MOE_ERR_ARG, "shared must be given exactly when shared_inter > 0");
+    if (!aligned(w->router_q, 16) || !aligned(w->experts, 16) ||
+        (w->shared && !aligned(w->shared, 16)) || !aligned(w->router_scale, 2))
+        return fail(MOE_ERR_ALIGN, "router_q, experts and shared need 16-byte alignment");
+    moe_status st;
+    if ((st = check_device_ptr(w->router_q, "router_q")) != MOE_OK) return st;
+    if ((st = check_device_ptr(w->router_scale, "router_scale")) != MOE_OK) return st;
+    if ((st = check_device_ptr(w->experts, "experts")) != MOE_OK) return st;
+    if (w->shared && (st = check_device_ptr(w->shared, "shared")) != MOE_OK) return st;
+
+    moe_layer* L = new (std::nothrow) moe_layer();
+    if (!L) return fail(MOE_ERR_NOMEM, "host allocation failed");
+    L->d = d;
+    L->w = *w;
+    L->rec_bytes = moe_expert_record_bytes(d.hidden, d.inter);
+    L->shared_rec_bytes = d.shared_inter ? moe_expert_record_bytes(d.hidden, d.shared_inter) : 0;
+    L->NG = d.hidden / 64;
+    L->blk_r = d.inter / 32;
+    L->blk_s = d.shared_inter / 32;
+    L->blk_max = std::max(L->blk_r, L->blk_s);
+    L->xparts = d.act_dtype == MOE_F32 ? 2 : 1;
+    L->gi = d.inter / 64;
+    const int sg = d.shared_inter / 64;
+    L->n_items = d.top_k + (sg + L->gi - 1) / L->gi;
+    L->n_otiles = d.hidden / 64;
+    L->gpw_gu = (L->NG + kWaves - 1) / kWaves;
+    L->gpw_dn = (L->gi + kWaves - 1) / kWaves;
+    if (L->gpw_gu > 32 || L->gpw_dn > 16) {
+        delete L;
+        return fail(MOE_ERR_SHAPE, "shape exceeds the kernels' per-wave register tiles");
+    }
+    *out = L;
+    return MOE_OK;
+}
+
+moe_status moe_layer_destroy(moe_layer_t layer) {
+    if (!layer) return fail(MOE_ERR_ARG, "null layer handle");
+    delete layer;
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens) {
+    if (!layer || n_tokens <= 0) return 0;
+    return ws_layout(layer, n_tokens).total;
+}
+
+moe_status moe_route_topk(moe_layer_t L, const void* x, int32_t T, int32_t* ids, float* w,
+                          void* workspace, void* stream) {
+    moe_status st = check_call(L, x, T, workspace);
+    if (st != MOE_OK) return st;
+    if (!ids || !w) return fail(MOE_ERR_ARG, "null ids or w");
+    const WsLayout o = ws_layout(L, T);
+    RouteArgs a = route_args(L, x, ids, w, (uint8_t*)workspace, o, 0);
+    hipError_t e = timed(K_ROUTE, (hipStream_t)stream, [&] { return launch_route(a, T, L->d.act_dtype == MOE_BF16, (hipStream_t)stream); });
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "router launch");
+}
+
+moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t* ids,
+                          void* workspace, float* expert_out, void* stream) {
+    moe_status st = check_call(L, x, T, workspace);
+    if (st != MOE_OK) return st;
+    if (!ids || !expert_out) return fail(MOE_ERR_ARG, "null ids or expert_out");
+    const WsLayout o = ws_layout(L, T);
+    uint8_t* ws = (uint8_t*)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    RouteArgs ra = route_args(L, x, nullptr, nullptr, ws, o, 1);
+    hipError_t e = timed(K_PREP, s, [&] { return launch_prep(ra, T, L->d.act_dtype == MOE_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    FfnArgs fa = ffn_args(L, ids, nullptr, ws, o, nullptr, expert_out);
+    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
+    if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
+    return MOE_OK;
+}
+
+moe_status moe_combine(moe_layer_t L, const float* expert_out, const float* w, int32_t T,
+                       void* y, int32_t y_dtype, void* stream) {
+    if (!L) return fail(MOE_ERR_ARG, "null layer handle");
+    if (!expert_out || !w || !y) return fail(MOE_ERR_ARG, "null expert_out, w or y");
+    if (T <= 0) return fail(MOE_ERR_ARG, "n_tokens out of range");
+    if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "bad y_dtype");
+    CombineArgs a{expert_out, w, y, L->d.hidden, L->d.top_k, T, y_dtype == MOE_BF16};
+    hipError_t e = timed(K_COMBINE, (hipStream_t)stream, [&] { return launch_combine(a, (hipStream_t)stream); });
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+}
+
+moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* ids, float* w,
+                             float* y, void* workspace, void* stream) {
+    moe_status st = check_call(L, x, T, workspace);
+    if (st != MOE_OK) return st;
+    if (!ids || !w || !y) return fail(MOE_ERR_ARG, "null ids, w or y");
+    const WsLayout o = ws_layout(L, T);
+    uint8_t* ws = (uint8_t*)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    RouteArgs ra = route_args(L, x, ids, w, ws, o, 1);
+    hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    FfnArgs fa = ffn_args(L, ids, w, ws, o, y, nullptr);
+    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
+    if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
+    return MOE_OK;
+}
+
+moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const void* x,
+                             int64_t x_stride, int32_t T, int32_t* ids, float* w, float* y,
+                             int64_t y_stride, void* workspace, void* stream) {
+    if (!layers || n_layers <= 0) return fail(MOE_ERR_ARG, "no layers");
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer* L = layers[l];
+        if (!L) return fail(MOE_ERR_ARG, "null layer handle in stack");
+        const size_t esz = L->d.act_dtype == MOE_BF16 ? 2 : 4;
+        const void* xl = (const uint8_t*)x + (size_t)l * x_stride * esz;
+        moe_status st = moe_layer_forward(layers[l], xl, T, ids + (size_t)l * T * L->d.top_k,
+                                          w + (size_t)l * T * L->d.top_k,
+                                          y + (size_t)l * y_stride, workspace, stream);
+        if (st != MOE_OK) return st;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_poll_device_error(moe_layer_t L, void* workspace, void* stream) {
+    if (!L || !workspace) return fail(MOE_ERR_ARG, "null layer or workspace");
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t* errp = (uint32_t*)((uint8_t*)workspace + ws_layout(L, 1).err);
+    uint32_t host = 0;
+    hipError_t e = hipMemcpyAsync(&host, errp, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = launch_clear_word(errp, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "device error poll");
+    return host ? fail(MOE_ERR_DEVICE, "a kernel saw an expert id outside [0, n_experts)") : MOE_OK;
+}
+
+moe_status moe_profile_start(int32_t capacity) {
+    if (capacity <= 0 || capacity > (1 << 22)) return fail(MOE_ERR_ARG, "bad profile capacity");
+    for (auto& r : g_prof) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    g_prof.clear();
+    g_prof_n = 0;
+    try {
+        g_prof.resize((size_t)capacity);
+    } catch (...) {
+        return fail(MOE_ERR_NOMEM, "profile buffer");
+    }
+    for (auto& r : g_prof) {
+        hipError_t e = hipEventCreate(&r.a);
+        if (e == hipSuccess) e = hipEventCreate(&r.b);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    g_prof_on = true;
+    return MOE_OK;
+}
+
+moe_status moe_profile_stop(void) {
+    g_prof_on = false;
+    return MOE_OK;
+}
+
+int32_t moe_profile_read(int32_t* kernel_ids, float* ms, int32_t max_records) {
+    if (!kernel_ids || !ms || max_records < 0) return fail(MOE_ERR_ARG, "null profile output");
+    const int32_t n = (int32_t)std::min<size_t>(g_prof_n, (size_t)max_records);
+    for (int32_t i = 0; i < n; ++i) {
+        hipError_t e = hipEventSynchronize(g_prof[i].b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_prof[i].a, g_prof[i].b);
+        if (e != hipSuccess) return hip_fail(e, "profile read");
+        kernel_ids[i] = g_prof[i].kid;
+    }
+    g_prof_n = 0;
+    return n;
+}
+
+const char* moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_ARG: return "MOE_ERR_ARG";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        case MOE_ERR_NOMEM: return "MOE_ERR_NOMEM";
+        case MOE_ERR_NOT_PINNED: return "MOE_ERR_NOT_PINNED";
+        case MOE_ERR_STATE: return "MOE_ERR_STATE";
+        case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+/*
+ * moe_layer.h -- C ABI of the MI355X routed-expert MoE layer library
+ * (libmoe_layer.so, built for gfx950).
+ *
+ * One layer of a mixture-of-experts FFN at decode, as the out-of-core engines
+ * on the source pages run it: an 8-bit router, exact top-k expert selection
+ * with gate weights renormalised over the selection, a SwiGLU FFN per selected
+ * expert over affine 4-bit group-64 weights (one fp16 scale and one fp16 bias
+ * per 64 inputs) dequantised on use, and an always-resident shared expert
+ * added to the weighted sum of the routed outputs.
+ *   - exact top-8 routed experts: Inferno README, "Current Scope"
+ *   - 8-bit router, MLX affine 4-bit group-64 experts, shared expert computed
+ *     while routed experts are fetched, outputs combined afterwards:
+ *     TurboFieldfare article, "Arsitektur eksekusi yang mengurangi memori" and
+ *     "Proses pembuatan token"
+ *   - gate, up and down matrices of an expert stored next to each other:
+ *     Inferno README, "Model" (ExpertPack)
+ *   - dequantisation on use, batch-union of experts in prefill: Colibri README,
+ *     "What's implemented"
+ *   - never run an expert whose weights are missing, never substitute zeros:
+ *     Colibri analysis report, section 6
+ *
+ * Conventions
+ *   - Every pointer argument named as "device" must point to GPU memory
+ *     (hipMalloc / torch CUDA tensors) on the current device.  Host pointers
+ *     are named "host".  Nothing here takes ownership of caller memory.
+ *   - Compute calls enqueue work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and return without waiting.  Argument errors are
+ *     detected on the host before anything is enqueued; faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - A handle is not thread-safe; calls on one handle must be issued from one
+ *     thread and, while they share a workspace, on one stream.
+ *   - Status codes are int32: MOE_OK (0) or a negative MOE_ERR_*.
+ *     moe_last_error() gives a thread-local detail string for the last failure.
+ *
+ * Packed expert record (hidden H, intermediate I; H and I multiples of 64).
+ * Matrices G (gate) and U (up) are [I][H] with input dim H; D (down) is [H][I]
+ * with input dim I.  Inputs are quantised in groups of 64 consecutive inputs:
+ * W = scale * q + bias, q in 0..15.  Within a 16-byte run of 32 inputs, input
+ * 2m is the low nibble of byte m and input 2m+1 the high nibble.
+ *   nibble region (3*H*I/2 bytes): I/32 blocks of 48*H bytes; block b covers
+ *   rows i in [32b, 32b+32):
+ *     +0     GU tile: for chunk c < H/32, for tile row r < 64: 16 bytes holding
+ *            inputs [32c, 32c+32) of G row 32b+r (r < 32) or U row 32b+r-32
+ *     +32*H  D block: for output row o < H: 16 bytes = D[o][32b .. 32b+32)
+ *   scale/bias region (at 3*H*I/2; I/64 slabs of 12*H bytes); slab g covers
+ *   rows/inputs i in [64g, 64g+64):
+ *     +0     (scale, bias) fp16 pairs of GU tile 2g, [group h < H/64][row r < 64]
+ *     +4*H   the same for GU tile 2g+1
+ *     +8*H   (scale, bias) of D[o][64g .. 64g+64) for o < H
+ *   Record size: 27*H*I/16 bytes (0.5625 bytes per weight).  A layer's routed
+ *   records lie back to back: record e at experts + e * moe_expert_record_bytes.
+ * Router: rows q[E][H] int8, row-major, and one fp16 scale per row;
+ *   logit_e = scale_e * sum_h q[e][h] * x_h.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = -1,        /* null or inconsistent argument                    */
+    MOE_ERR_SHAPE = -2,      /* H or I not a multiple of 64, top_k > n_experts... */
+    MOE_ERR_ALIGN = -3,      /* pointer not 16-byte aligned                      */
+    MOE_ERR_HIP = -4,        /* a HIP runtime call failed (detail in last_error) */
+    MOE_ERR_NOMEM = -5,      /* host or device allocation failed                 */
+    MOE_ERR_NOT_PINNED = -6, /* host pool is not page-locked host memory         */
+    MOE_ERR_STATE = -7,      /* call not valid for this handle's configuration   */
+    MOE_ERR_DEVICE = -8      /* a kernel reported bad input (e.g. expert id out of range) */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };                 /* activation / output dtypes */
+enum { MOE_SOFTMAX_TOPK = 0, MOE_SIGMOID_TOPK = 1 }; /* gate functions            */
+
+typedef struct moe_layer_desc {
+    int32_t hidden;        /* H, multiple of 64                                   */
+    int32_t n_experts;     /* E routed experts, 1..1024                           */
+    int32_t inter;         /* I, routed expert intermediate size, multiple of 64  */
+    int32_t top_k;         /* k, 1..min(E, 16)                                    */
+    int32_t shared_inter;  /* intermediate size of the shared expert, 0 = none    */
+    int32_t group;         /* quantisation group; must be 64                      */
+    int32_t act_dtype;     /* MOE_F32 or MOE_BF16 activations x                   */
+    int32_t gate_fn;       /* MOE_SOFTMAX_TOPK (renormalised softmax over the top-k) */
+    int32_t n_slots;       /* 0 = every routed record resident in HBM             */
+    int32_t reserved[7];
+} moe_layer_desc;
+
+typedef struct moe_layer_weights {
+    const int8_t* router_q;       /* device, [E][H] int8                              */
+    const uint16_t* router_scale; /* device, [E] fp16 bits                            */
+    const uint8_t* experts;       /* device, E packed records back to back            */
+    const uint8_t* shared;        /* device, one packed record of (H, shared_inter), or NULL */
+    const uint8_t* host_pool;     /* reserved for the slot cache; must be NULL when n_slots = 0 */
+    uint8_t* slots;               /* reserved for the slot cache; must be NULL when n_slots = 0 */
+} moe_layer_weights;
+
+typedef struct moe_layer* moe_layer_t;
+
+/* Bytes of one packed record of (hidden, inter): 27*hidden*inter/16, or 0 if
+ * either is not a positive multiple of 64. */
+size_t moe_expert_record_bytes(int32_t hidden, int32_t inter);
+
+/* Validates desc and weights and builds a handle.  The handle borrows the
+ * weight pointers (they must outlive it) and owns only host metadata.
+ * Launches nothing.  Errors: ARG, SHAPE, ALIGN, STATE, NOMEM. */
+moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w,
+                            moe_layer_t* out);
+moe_status moe_layer_destroy(moe_layer_t layer);
+
+/* Device workspace bytes needed by the compute calls for n_tokens tokens.
+ * The workspace must be zero-filled before its first use; every call returns
+ * its internal counters to zero, so it can be reused without clearing.  Two
+ * calls that overlap in time must not share a workspace. */
+size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens);
+
+/* Router + exact top-k + gates for n_tokens tokens.
+ *   x   device [T][H] in desc.act_dtype
+ *   ids device [T][k] int32 out: selected experts, by logit descending, ties to
+ *       the lower id
+ *   w   device [T][k] fp32 out: exp(l_j - l_max) / sum over the selection
+ * Errors: ARG, ALIGN, HIP. */
+moe_status moe_route_topk(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
+                          float* w, void* workspace, void* stream);
+
+/* Per-expert SwiGLU outputs for the given selection.
+ *   ids        device [T][k] int32 (values outside [0, E) set the device error
+ *              flag, see moe_poll_device_error, and make that slot's output NaN)
+ *   expert_out device [T][k+1][H] fp32 out: row j < k is D_e silu(G_e x)*(U_e x)
+ *              for e = ids[t][j]; row k is the shared expert (zeros if none)
+ * Errors: ARG, ALIGN, HIP. */
+moe_status moe_expert_ffn(moe_layer_t layer, const void* x, int32_t n_tokens,
+                          const int32_t* ids, void* workspace, float* expert_out, void* stream);
+
+/* y[t] = sum_{j<k} w[t][j] * expert_out[t][j] + expert_out[t][k], summed in
+ * that order.  y device [T][H] of y_dtype (MOE_F32 or MOE_BF16, round to
+ * nearest even).  Errors: ARG, ALIGN, HIP. */
+moe_status moe_combine(moe_layer_t layer, const float* expert_out, const float* w,
+                       int32_t n_tokens, void* y, int32_t y_dtype, void* stream);
+
+/* The whole layer in one call: route, experts, combine, with the per-expert
+ * outputs reduced inside the FFN kernels (no expert_out round trip).
+ * ids, w as moe_route_topk; y device [T][H] fp32.  Errors: ARG, ALIGN, HIP. */
+moe_status moe_layer_forward(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
+                             float* w, float* y, void* workspace, void* stream);
+
+/* n_layers layers one after another on one stream, layer l reading x_l and
+ * writing y_l (strides in elements: x_stride for x, y_stride for y, k-strided
+ * ids/w per layer), each layer ordered after the previous one's output.  The
+ * workspace must be sized for the largest layer.  Errors as moe_layer_forward. */
+moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const void* x,
+                             int64_t x_stride, int32_t n_tokens, int32_t* ids, float* w,
+                             float* y, int64_t y_stride, void* workspace, void* stream);
+
+/* Reads and clears the device error flag kept in `workspace` (synchronises
+ * `stream`).  MOE_OK if no kernel reported bad input since the last poll,
+ * MOE_ERR_DEVICE otherwise. */
+moe_status moe_poll_device_error(moe_layer_t layer, void* workspace, void* stream);
+
+/* Measurement support.  While profiling is on, every kernel the library
+ * launches is bracketed by two hipEvents recorded on its launch stream, up to
+ * `capacity` launches.  moe_profile_read synchronises those events and writes,
+ * per recorded launch, the kernel id (0 router/top-k, 1 activation prep,
+ * 2 gate/up, 3 down/combine-in-place, 4 combine) and the elapsed milliseconds;
+ * it returns the number of records (or a negative status) and clears them.
+ * Profiling state is process-wide and not thread-safe; do not profile inside
+ * stream capture.  Errors: ARG, HIP, NOMEM. */
+moe_status moe_profile_start(int32_t capacity);
+moe_status moe_profile_stop(void);
+int32_t moe_profile_read(int32_t* kernel_ids, float* ms, int32_t max_records);
+
+const char* moe_status_str(moe_status s);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYER_H */

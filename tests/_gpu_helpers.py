@@ -1,0 +1,78 @@
+"""Shared pieces of the GPU tests: building layers on the device from the seeded
+generator, and oracle references computed from the generator's CPU output only
+(nothing the GPU path produced is fed to the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+import synth.gpu
+
+Y_TOL = 2e-3   # max |y - y_ref| / max |y_ref| per token
+W_TOL = 1e-6   # max |w - w_ref|
+GAP = 1e-4     # required separation of the top-(k+1) oracle logits
+
+
+def rel_err(y, y_ref) -> float:
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    return float(np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-30))
+
+
+def gap_ok(logits: np.ndarray, k: int) -> bool:
+    s = np.sort(logits)[::-1][:k + 1]
+    return bool(np.all(-np.diff(s) > GAP))
+
+
+class DeviceLayer:
+    """One layer's weights on the GPU (router from numpy, records from the GPU
+    fill) plus the host copies the oracle needs (router only; records are
+    regenerated on the CPU on demand)."""
+
+    def __init__(self, seed, layer, H, E, I, k, Is, act, dev="cuda"):
+        from bit_routed_expert_moe_amd import Layer, record_bytes
+        self.seed, self.layer, self.H, self.E, self.I, self.k, self.Is, self.act = \
+            seed, layer, H, E, I, k, Is, act
+        self.rq, self.rs = synth.router(seed, layer, E, H)
+        self.pool = torch.empty(E * record_bytes(H, I), dtype=torch.uint8, device=dev)
+        synth.gpu.fill_records(self.pool, H, I, seed, layer, 0, E)
+        self.shared = None
+        if Is:
+            self.shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
+            synth.gpu.fill_records(self.shared, H, Is, seed, layer, -1, 1)
+        self.layer_obj = Layer(H, E, I, k, Is, torch.from_numpy(self.rq).to(dev),
+                               torch.from_numpy(self.rs.view(np.float16)).to(dev), self.pool,
+                               self.shared, act=act)
+        self._rec_cache = {}
+
+    def record(self, e: int) -> np.ndarray:
+        if e not in self._rec_cache:
+            if e == synth.SHARED_INDEX:
+                self._rec_cache[e] = synth.expert_record(self.seed, self.layer, e, self.H, self.Is)
+            else:
+                self._rec_cache[e] = synth.expert_record(self.seed, self.layer, e, self.H, self.I)
+        return self._rec_cache[e]
+
+    def natural_token(self, orc, step: int, max_attempts: int = 200):
+        """Seeded N(0,1) activations for (layer, step), redrawn until the oracle's
+        top-(k+1) logits are separated by more than GAP.  Returns (raw, float64)."""
+        for a in range(max_attempts):
+            x = synth.activations(self.seed, self.layer, step, self.H, attempt=a)[0]
+            xq = synth.quantize_act(x, self.act)
+            xd = orc.act_to_f64(self.act, xq)
+            if gap_ok(orc.router_logits(self.rq, self.rs, xd), self.k):
+                return xq, xd
+        raise RuntimeError("no well-separated token found")
+
+    def oracle(self, orc, xd: np.ndarray):
+        ids, w, lg = orc.route(self.rq, self.rs, xd, self.k)
+        yr = np.stack([orc.expert_ffn(self.H, self.I, self.record(int(e)), xd) for e in ids])
+        ys = orc.expert_ffn(self.H, self.Is, self.record(synth.SHARED_INDEX), xd) if self.Is else None
+        return ids, w, orc.combine(w, yr, ys), yr, ys
+
+
+def to_dev(xq: np.ndarray, act: str, dev="cuda") -> torch.Tensor:
+    if act == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(xq).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(xq, dtype=np.float32)).to(dev)

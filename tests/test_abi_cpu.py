@@ -1,0 +1,88 @@
+"""The C ABI without a GPU: the library loads, exports every function declared
+in include/moe_layer.h, and rejects bad descriptors on the host before any HIP
+call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from bit_routed_expert_moe_amd import layer as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_record_bytes_formula():
+    lib = L.lib()
+    for H, I in [(64, 64), (256, 128), (2816, 704), (6144, 2048)]:
+        assert lib.moe_expert_record_bytes(H, I) == 27 * H * I // 16
+    for H, I in [(0, 64), (64, 0), (100, 64), (64, 96), (-64, 64)]:
+        assert lib.moe_expert_record_bytes(H, I) == 0
+
+
+def test_status_strings():
+    lib = L.lib()
+    for code, name in L.STATUS.items():
+        assert lib.moe_status_str(code).decode() == name
+
+
+def _create(desc, weights):
+    h = C.c_void_p()
+    st = L.lib().moe_layer_create(C.byref(desc), C.byref(weights), C.byref(h))
+    return st, L.lib().moe_last_error().decode()
+
+
+GOOD = dict(hidden=256, n_experts=32, inter=128, top_k=8, shared_inter=256, group=64,
+            act_dtype=1, gate_fn=0, n_slots=0)
+FAKE = dict(router_q=0x10000, router_scale=0x20000, experts=0x30000, shared=0x40000)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(group=32), -2), (dict(hidden=100), -2), (dict(hidden=0), -2), (dict(hidden=16384), -2),
+    (dict(inter=96), -2), (dict(shared_inter=100), -2), (dict(n_experts=0), -2),
+    (dict(n_experts=2048), -2), (dict(top_k=0), -2), (dict(top_k=33), -2),
+    (dict(n_experts=4, top_k=5), -2), (dict(act_dtype=7), -1), (dict(gate_fn=1), -7),
+    (dict(n_slots=16), -7),
+])
+def test_create_rejects_bad_descriptor(change, status):
+    d = L.Desc(**{**GOOD, **change})
+    w = L.Weights(**FAKE)
+    st, msg = _create(d, w)
+    assert st == status, msg
+    assert msg
+
+
+def test_create_rejects_missing_and_misaligned_pointers():
+    d = L.Desc(**GOOD)
+    assert _create(d, L.Weights(**{**FAKE, "experts": None}))[0] == -1
+    assert _create(d, L.Weights(**{**FAKE, "shared": None}))[0] == -1
+    d0 = L.Desc(**{**GOOD, "shared_inter": 0})
+    assert _create(d0, L.Weights(**FAKE))[0] == -1            # shared given but size 0
+    assert _create(d, L.Weights(**{**FAKE, "experts": 0x30008}))[0] == -3
+    assert _create(d, L.Weights(**{**FAKE, "router_q": 0x10004}))[0] == -3
+    assert _create(d, L.Weights(**{**FAKE, "host_pool": 0x50000}))[0] == -1
+
+
+def test_null_handles():
+    lib = L.lib()
+    assert lib.moe_layer_destroy(None) == -1
+    assert lib.moe_workspace_bytes(None, 1) == 0
+    assert lib.moe_layer_forward(None, None, 1, None, None, None, None, None) == -1
+    assert lib.moe_stack_forward(None, 0, None, 0, 1, None, None, None, 0, None, None) == -1

@@ -1,0 +1,72 @@
+"""Full-size workloads on the GPU, checked against the oracle on sampled tokens.
+
+* Gemma-4-A4B-scale stack: hidden 2816, 128 experts of intermediate 704, top-8,
+  shared expert 2112, 30 layers (13.2 GB of records), bf16 activations, run
+  through moe_stack_forward exactly as bench.py times it.
+* GLM-scale layer: hidden 6144, 256 experts of intermediate 2048, top-8, shared
+  2048 (5.5 GB), activations drawn so the choice follows Zipf(1.1).
+The oracle regenerates the records it selects on the CPU from the seeded
+generator; nothing the GPU computed is given to it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu_helpers import W_TOL, Y_TOL, DeviceLayer, gap_ok, rel_err, to_dev
+from bit_routed_expert_moe_amd import stack_forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def test_gemma_stack_full_size(orc):
+    wl = synth.WORKLOADS["gemma_a4b_h2816_e128_l30"]
+    L, H = wl.n_layers, wl.hidden
+    layers = [DeviceLayer(wl.seed, l, H, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
+              for l in range(L)]
+    ws = layers[0].layer_obj.workspace(1)
+    worst_y = worst_w = 0.0
+    for step in range(2):
+        toks = [dl.natural_token(orc, step) for dl in layers]
+        x = to_dev(np.stack([t[0] for t in toks])[:, None, :], wl.act)  # [L][1][H]
+        ids, w, y = stack_forward([dl.layer_obj for dl in layers], x, ws)
+        ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+        for l, dl in enumerate(layers):
+            rid, rw, ry, _, _ = dl.oracle(orc, toks[l][1])
+            assert ids[l, 0].tolist() == rid.tolist(), f"step {step} layer {l}"
+            worst_w = max(worst_w, float(np.max(np.abs(w[l, 0] - rw))))
+            worst_y = max(worst_y, rel_err(y[l, 0], ry))
+    print(f"gemma stack: 2 steps x {L} layers, max |w err| {worst_w:.2e}, max rel y err {worst_y:.2e}")
+    assert worst_w <= W_TOL and worst_y <= Y_TOL
+
+
+def test_glm_layer_zipf_full_size(orc):
+    wl = synth.WORKLOADS["glm_h6144_e256_l40_zipf"]
+    dl = DeviceLayer(wl.seed, 0, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
+    Wd = dl.rq.astype(np.float64) * dl.rs.view(np.float16).astype(np.float64)[:, None]
+    zr = synth.ZipfRealiser(Wd, wl.zipf_s, wl.seed, 0)
+    xs_q, xs_d = [], []
+    for step in range(4):
+        for a in range(50):
+            xq = synth.quantize_act(zr.activations(step, a)[0], wl.act)
+            xd = orc.act_to_f64(wl.act, xq)
+            if gap_ok(orc.router_logits(dl.rq, dl.rs, xd), wl.top_k):
+                break
+        xs_q.append(xq); xs_d.append(xd)
+    ids, w, y = dl.layer_obj.forward(to_dev(np.stack(xs_q), wl.act))
+    ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+    worst = 0.0
+    for t in range(len(xs_d)):
+        rid, rw, ry, _, _ = dl.oracle(orc, xs_d[t])
+        assert ids[t].tolist() == rid.tolist()
+        assert np.max(np.abs(w[t] - rw)) <= W_TOL
+        worst = max(worst, rel_err(y[t], ry))
+    print(f"glm zipf layer: {len(xs_d)} tokens, max rel y err {worst:.2e}")
+    assert worst <= Y_TOL
