@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Decode throughput of the routed-expert MoE layer on one MI355X (gfx950).
+
+A step is one decode token (batch 1) through every layer of the workload's
+stack: router + exact top-8 + gates, the 8 selected experts' dequant-fused
+SwiGLU, the shared expert and the weighted combine, layer after layer on one
+stream (layer l+1 starts after layer l's output is written).  Inputs are
+synthetic and seeded (synth/): random 4-bit records filled on the GPU, int8
+routers, N(0,1) bf16 activations, a distinct input for each of the workload's
+decode steps.  Timed: exactly --steps steps, replayed as hipGraphs of
+--graph-chunk steps, bracketed by synchronisations.
+
+Printed (stdout, one JSON line): decode tokens/s per MoE layer (value), the
+whole-stack tokens/s, achieved HBM GB/s on algorithmic bytes (router + 8
+selected records + shared record per token-layer) against the 8 TB/s peak,
+a roofline entry for the dominant kernel (gate/up) from a live per-kernel
+hipEvent pass, and the CPU oracle timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+# HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs (profiles/k_gate_up_gemma_stack_counters.md), each scaled by
+# the same counter's reading for a 1 GiB device copy (FETCH x2.0, WRITE x1.0).
+# Valid only for the kernel source they were taken on; None once it changes.
+TRAFFIC_SOURCE_SHA256 = "43385aefecdbd8b3"  # first 16 hex digits of csrc/moe_kernels.hip when measured
+TRAFFIC = {
+    # FETCH_SIZE 12154.6 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): 24931430,
+}
+
+
+def traffic_for(workload, kernel):
+    import hashlib
+    src = os.path.join(ROOT, "bit_routed_expert_moe_amd", "csrc", "moe_kernels.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_SOURCE_SHA256:
+            return None
+    return TRAFFIC.get((workload, kernel))
+METRIC = "decode tokens/s per MoE layer + achieved HBM GB/s vs peak (batch 1, top-8)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gu_bytes(H, I):
+    """gate+up half of a record: nibbles I*H bytes + scale/bias I*H/8 bytes."""
+    return 9 * H * I // 8
+
+
+def down_bytes(H, I):
+    return 9 * H * I // 16
+
+
+def make_inputs(wl, layer, S):
+    """[S][T][H] activations for one layer (float64) from the seeded generator."""
+    import synth
+    if wl.routing == "zipf":
+        q, rs = synth.router(wl.seed, layer, wl.n_experts, wl.hidden)
+        W = q.astype(np.float64) * rs.view(np.float16).astype(np.float64)[:, None]
+        zr = synth.ZipfRealiser(W, wl.zipf_s, wl.seed, layer)
+        return np.stack([zr.activations(s) for s in range(S)])
+    return np.stack([synth.activations(wl.seed, layer, s, wl.hidden, wl.n_tokens) for s in range(S)])
+
+
+def cpu_baseline(wl, xs_host, seconds):
+    """The CPU oracle on the first token-layers of the same inputs, until about
+    `seconds` of oracle compute have been spent (record generation excluded)."""
+    import oracle
+    import synth
+    orc = oracle.default()
+    threads = orc.set_threads(len(os.sched_getaffinity(0)))
+    H, I, Is, k = wl.hidden, wl.inter, wl.shared_inter, wl.top_k
+    spent, n = 0.0, 0
+    S, L = xs_host.shape[0], xs_host.shape[1]
+    routers = {}
+    for s in range(S):
+        for l in range(L):
+            if l not in routers:
+                routers[l] = synth.router(wl.seed, l, wl.n_experts, H)
+            rq, rs = routers[l]
+            for t in range(wl.n_tokens):
+                xd = orc.act_to_f64(wl.act, xs_host[s, l, t])
+                t0 = time.perf_counter()
+                ids, w, _ = orc.route(rq, rs, xd, k)
+                spent += time.perf_counter() - t0
+                recs = [synth.expert_record(wl.seed, l, int(e), H, I) for e in ids]
+                shared = synth.expert_record(wl.seed, l, synth.SHARED_INDEX, H, Is) if Is else None
+                t0 = time.perf_counter()
+                yr = np.stack([orc.expert_ffn(H, I, r, xd) for r in recs])
+                ys = orc.expert_ffn(H, Is, shared, xd) if Is else None
+                orc.combine(w, yr, ys)
+                spent += time.perf_counter() - t0
+                n += 1
+            if spent >= seconds:
+                return {"value": n / spent, "unit": "tok/s per layer", "cores": threads,
+                        "kind": "oracle",
+                        "sample": f"{n} token-layers (steps 0.., layers in order) of the same "
+                                  f"inputs; fp64 plain-loop oracle, OpenMP over rows; record "
+                                  f"regeneration excluded; {spent:.1f} s of oracle compute"}
+    return {"value": n / max(spent, 1e-9), "unit": "tok/s per layer", "cores": threads,
+            "kind": "oracle", "sample": f"{n} token-layers, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="gemma_a4b_h2816_e128_l30")
+    ap.add_argument("--graph-chunk", type=int, default=16)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of hipGraphs")
+    ap.add_argument("--profile-steps", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (for scaling the "
+                         "FETCH_SIZE/WRITE_SIZE counters) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU hot path only; runs on more than one GPU are "
+              "not part of this build (see the sharding note in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
+    import synth
+    import synth.gpu
+    from bit_routed_expert_moe_amd import KernelTimer, Layer, record_bytes, stack_forward
+
+    wl = synth.WORKLOADS[args.workload]
+    if wl.n_slots or wl.n_tokens != 1:
+        print(f"workload {wl.name} is not a resident decode stack", file=sys.stderr)
+        sys.exit(2)
+    H, E, I, k, Is, L, T = (wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter,
+                            wl.n_layers, wl.n_tokens)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    t_setup = time.time()
+    rb = record_bytes(H, I)
+    layers, keep = [], []
+    for l in range(L):
+        rq, rs = synth.router(wl.seed, l, E, H)
+        pool = torch.empty(E * rb, dtype=torch.uint8, device=dev)
+        synth.gpu.fill_records(pool, H, I, wl.seed, l, 0, E)
+        shared = None
+        if Is:
+            shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
+            synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
+        layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
+                            torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act))
+    S = wl.steps
+    xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][T][H]
+    xs_q = synth.quantize_act(xs_host, wl.act)
+    if wl.act == "bf16":
+        xs = torch.from_numpy(xs_q.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        xs = torch.from_numpy(xs_q).to(dev)
+    ws = layers[0].workspace(T)
+    ids = torch.empty(S, L, T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(S, L, T, k, dtype=torch.float32, device=dev)
+    y = torch.empty(S, L, T, H, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f} s: {L} layers, {E} experts of {rb} B, "
+        f"{S} distinct steps")
+
+    def run_step(s):
+        stack_forward(layers, xs[s], ws, out=(ids[s], w[s], y[s]))
+
+    run_step(0)
+    torch.cuda.synchronize()
+
+    K, W = args.steps, args.warmup
+    G = 1 if args.no_graph else math.gcd(args.graph_chunk, math.gcd(K, S))
+    units = []  # callables, each running G consecutive steps
+    if args.no_graph:
+        units = [(lambda s=s: run_step(s)) for s in range(S)]
+    else:
+        for c0 in range(0, S, G):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(c0, c0 + G):
+                    run_step(s)
+            units.append(g.replay)
+    n_units = len(units)
+    for i in range((W + G - 1) // G):
+        units[i % n_units]()
+    torch.cuda.synchronize()
+
+    start = (W + G - 1) // G
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K // G + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(K // G):
+        units[(start + i) % n_units]()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) / G for i in range(K // G)])
+    ms_per_step = total_ms / K
+    log(f"timed {K} steps in {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), graphs of {G} steps")
+
+    tl_bytes = wl.token_layer_bytes
+    step_bytes = L * T * tl_bytes
+    layer_tok_s = L * T / (ms_per_step * 1e-3)
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # live per-kernel hipEvent pass over the same steps, launched eagerly
+    P = min(args.profile_steps, S)
+    with KernelTimer(capacity=P * L * 4 + 64) as kt:
+        for s in range(P):
+            run_step(s)
+    recs = kt.read()
+    torch.cuda.synchronize()
+    # event-pair overhead: the same bracketing around an empty kernel on the same stream
+    empty = []
+    for _ in range(64):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(0)
+        e1.record()
+        e1.synchronize()
+        empty.append(e0.elapsed_time(e1))
+    ev_overhead_ms = float(np.median(empty))
+    kbytes = {"route": T * (E * H + 2 * E),
+              "gate_up": T * (k * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0)),
+              "down_combine": T * (k * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0))}
+    kernels = {}
+    for name in sorted({r[0] for r in recs}):
+        ms = np.array([m for n_, m in recs if n_ == name])
+        net = max(float(ms.mean()) - ev_overhead_ms, 1e-6)
+        ent = {"launches": int(ms.size), "avg_us": round(net * 1e3, 3),
+               "avg_us_raw": round(float(ms.mean()) * 1e3, 3),
+               "p50_us_raw": round(float(np.median(ms)) * 1e3, 3)}
+        if name in kbytes:
+            ent["alg_bytes"] = int(kbytes[name])
+            ent["gbps"] = round(kbytes[name] / (net * 1e-3) / 1e9, 1)
+        kernels[name] = ent
+    gu = kernels["gate_up"]
+    roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(wl.name, "k_gate_up"),
+                "kernel": "k_gate_up", "alg_bytes_per_launch": gu["alg_bytes"],
+                "avg_launch_us": gu["avg_us"], "event_pair_overhead_us": round(ev_overhead_ms * 1e3, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, xs_q, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(layer_tok_s, 1), "unit": "tok/s per layer",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
+                   "shared_inter": Is, "layers": L, "batch": T, "act": wl.act,
+                   "routing": wl.routing, "graph_chunk": G},
+        "stack_tok_s": round(T / (ms_per_step * 1e-3), 2),
+        "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
+        "alg_bytes_per_token_layer": tl_bytes,
+        "step_ms_p50": round(float(np.percentile(per_step, 50)), 5),
+        "step_ms_p95": round(float(np.percentile(per_step, 95)), 5),
+        "step_ms_p99": round(float(np.percentile(per_step, 99)), 5),
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -86,14 +86,88 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Max over all 64 lanes (DPP within rows, then the 4 row results); every lane
+// gets the same value.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x124>(v));
+    v = fmaxf(v, dpp<0x128>(v));
+    const int iv = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48))));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = readlane_u32((uint32_t)u, lane), hi = readlane_u32((uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+// Sum over all 64 lanes in double, fixed order; every lane gets the same value.
 __device__ __forceinline__ double wave_sum_d(double v) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x124>(v);
+    v += dpp_f64<0x128>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Max of 64-bit unsigned keys over all 64 lanes; every lane gets the result.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#define MOE_MAX_STEP(CTRL)                                                          \
+    {                                                                               \
+        const uint64_t o = (uint64_t)dpp_u32<CTRL>((uint32_t)v) |                   \
+                           ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32);    \
+        v = o > v ? o : v;                                                          \
+    }
+    MOE_MAX_STEP(0xB1)
+    MOE_MAX_STEP(0x4E)
+    MOE_MAX_STEP(0x124)
+    MOE_MAX_STEP(0x128)
+#undef MOE_MAX_STEP
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t o = (uint64_t)readlane_u32((uint32_t)v, 16 * r) |
+                           ((uint64_t)readlane_u32((uint32_t)(v >> 32), 16 * r) << 32);
+        m = o > m ? o : m;
+    }
+    return m;
+}
+
+// Sort key of (logit, id): larger logit first, then lower id.  -0 is folded
+// into +0 so equal logits compare equal.
+__device__ __forceinline__ uint64_t topk_key(float v, int id) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+    uint32_t u = (uint32_t)(key >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __builtin_bit_cast(float, u);
+}
+__device__ __forceinline__ int topk_key_id(uint64_t key) {
+    return (int)(0xFFFFFFFFu - (uint32_t)key);
 }
 
 __device__ __forceinline__ int wave_id() {

@@ -9,17 +9,23 @@ namespace moe {
 
 constexpr int kBlock = 256;        // threads per workgroup (4 waves of 64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kRouterRowsPerBlock = kWaves;  // one router row per wave
+constexpr int kRouterRowsPerWave = 2;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxHidden = 8192;
 constexpr int kHParts = 1;         // fp16 parts used for the intermediate h
+constexpr int kMaxDownGroups = 64; // input groups (of I) per down work item
+constexpr int kMaxGateUpGroupsPerWave = 32;
+constexpr int kCounterStride = 64;  // arrival counters 256 bytes apart (own cache lines)
+constexpr int kDepth = 8;           // weight groups in flight per wave in k_gate_up
+constexpr int kMaxSharedItems = 8;  // down work items of the shared expert
+constexpr int kMaxItems = kMaxTopK + kMaxSharedItems;
 
 // Prepared activations of one vector of length n (n multiple of 64):
 //   pairs [n/8][parts][4] dwords  (fp16 pairs, see moe_device.h)
 //   K     [n/64] float            1024 * sum of the fp16 values per group
 //   X     [n/64] float            sum of the unscaled values per group
-//   inv   float                   2^-e, e the vector's scale exponent
+//   inv   [n/64] float            2^-e, e the group's scale exponent
 struct RouteArgs {
     const void* x;           // [T][H] activations
     const int8_t* rq;        // [E][H]
@@ -31,7 +37,7 @@ struct RouteArgs {
     uint32_t* xpairs;        // [T][H/2*XP] (written only if prep != 0)
     float* xK;               // [T][H/64]
     float* xX;               // [T][H/64]
-    float* xinv;             // [T]
+    float* xinv;             // [T][H/64]
     int H, E, k, prep;
 };
 
@@ -39,8 +45,11 @@ struct FfnArgs {
     const uint8_t* experts;  // E records
     const uint8_t* shared;   // shared record or nullptr
     size_t rec_bytes;
-    const int32_t* ids;      // [T][k]
-    const float* w;          // [T][k] (fused combine only)
+    const int32_t* ids;      // [T][k] selection (read by k_down; by k_gate_up unless logits)
+    const float* w;          // [T][k] gate weights (fused combine only)
+    const float* logits;     // [T][E]: if set, k_gate_up selects the experts itself
+    int32_t* ids_out;        // [T][k] written by k_gate_up's first workgroup when logits is set
+    float* w_out;            // [T][k]
     const uint32_t* xpairs;  // prepared x, as in RouteArgs
     const float* xK;
     const float* xX;
@@ -50,7 +59,7 @@ struct FfnArgs {
     float* hHs;              // [T][k+1][blk_max]
     float* hinv;             // [T][k+1][blk_max]
     float* dpart;            // [T][n_otiles][n_items][64]
-    uint32_t* dctr;          // [T][n_otiles]
+    uint32_t* dctr;          // [T][n_otiles][kCounterStride]
     float* y;                // [T][H] fused output (or nullptr)
     float* eo;               // [T][k+1][H] per-expert outputs (or nullptr)
     uint32_t* err;           // device error word
@@ -61,7 +70,8 @@ struct FfnArgs {
     int gpw_gu;              // input groups per wave in the gate/up kernel
     int n_otiles;            // H/64
     int n_items;             // down work items per output tile: k + shared k-slices
-    int gi;                  // input groups (of I) per down item
+    int gi;                  // input groups (of I) per routed down item (= I/64)
+    int gis;                 // input groups per shared down item
     int gpw_dn;              // input groups per wave in the down kernel
 };
 

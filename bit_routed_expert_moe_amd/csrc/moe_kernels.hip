@@ -1,136 +1,110 @@
 // moe_kernels.hip -- gfx950 kernels of the routed-expert MoE layer.
 //
-//   k_route       router GEMV (int8 rows x activations), then, in the last
-//                 workgroup to finish for a token, exact top-k and the gate
-//                 weights; optionally prepares the activations for the FFN.
-//   k_prep        activation preparation alone (for moe_expert_ffn).
+//   k_route       router GEMV (int8 rows x activations), two rows per wave,
+//                 every load issued before any use; one extra workgroup per
+//                 token prepares the activations for the FFN kernels.
+//   k_topk        exact top-k and gate weights from the logits (API route).
+//   k_prep        activation preparation alone (API expert FFN).
 //   k_gate_up     one workgroup per (token, expert slot, block of 32 rows of
-//                 I): streams the 64-row gate/up tile, h = silu(g) * u, writes
-//                 h prepared as fp16 pairs for the down kernel.
+//                 I).  For routed slots in the fused path it first selects its
+//                 expert itself (exact top-k over the logits); then it streams
+//                 the 64-row gate/up tile, h = silu(g) * u, and writes h
+//                 prepared as fp16 pairs for the down kernel.
 //   k_down        one workgroup per (token, 64 output rows, work item), a work
 //                 item being one routed expert or a k-slice of the shared one;
 //                 the last item to finish for an output tile sums the items in
 //                 a fixed order into per-expert outputs and/or the combined y.
 //   k_combine     y = sum_j w_j * eo_j + eo_shared.
 //
-// Every weight byte is read once per token with 16-byte loads, lane = row of a
-// 64-row tile, so one wave instruction reads 1 KB of contiguous record bytes.
+// Every weight byte is read once per token with 16-byte nontemporal loads,
+// lane = row of a 64-row tile, so one wave instruction reads 1 KB of
+// contiguous record bytes.  Small inputs (activations, logits) are loaded
+// before the weights so that the weights can be consumed in arrival order.
 // Sums across waves and workgroups are done in a fixed order: reruns are
-// bit-identical.
+// bit-identical.  The one hand-off inside a kernel (k_down's last arrival)
+// uses agent-scope coherent stores and loads plus an arrival counter, so no
+// L2 write-back or invalidate is needed.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// activation preparation (all threads of the block take part)
-// xs: the vector in LDS as fp32; writes pairs/K/X/inv for one vector.
+// activation preparation of one 64-input group by one wave (lane = input).
+// Each group gets its own power-of-two scale 2^e so that its largest value
+// lands below 2^14 in fp16; odd positions of each 8-set are also divided by 16
+// to pair with the x16 nibble slots.  Writes the group's 16*XP pair dwords,
+// K = 1024 * sum of the fp16 values (in double), X = sum of the inputs and
+// inv = 2^-e.
 // ---------------------------------------------------------------------------
-template <int XP>
-__device__ void prep_vector(const float* xs, int n, float max_abs, uint32_t* pairs, float* Kg,
-                            float* Xg, float* inv_out) {
-    const int e = act_exponent(max_abs);
-    const float sc = ldexpf(1.0f, e);
-    const int nsets = n / 8;
-    for (int s0 = 0; s0 < nsets; s0 += kBlock) {
-        const int s = s0 + (int)threadIdx.x;
-        const bool ok = s < nsets;
-        double ksum = 0.0;
-        float xsum = 0.0f;
-        if (ok) {
-            uint32_t hi[8], lo[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const float a = xs[8 * s + p];
-                const float v = a * sc * ((p & 1) ? 0.0625f : 1.0f);
-                const _Float16 h = (_Float16)v;
-                const float hf = (float)h;
-                const _Float16 l = (_Float16)(v - hf);
-                hi[p] = __builtin_bit_cast(uint16_t, h);
-                lo[p] = __builtin_bit_cast(uint16_t, l);
-                ksum += (double)hf;
-                if (XP == 2) ksum += (double)(float)l;
-                xsum += a;
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                pairs[(s * XP + 0) * 4 + m] = hi[m] | (hi[m + 4] << 16);
-                if (XP == 2) pairs[(s * XP + 1) * 4 + m] = lo[m] | (lo[m + 4] << 16);
-            }
-        }
-        // sum the 8 sets of each 64-group: 8 consecutive threads
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) {
-            ksum += __shfl_xor(ksum, off, 64);
-            xsum += __shfl_xor(xsum, off, 64);
-        }
-        if (ok && (s & 7) == 0) {
-            Kg[s >> 3] = (float)(1024.0 * ksum);
-            Xg[s >> 3] = xsum;
-        }
+template <int XP, bool BF16>
+__device__ void prep_group(const void* x, int t, int H, int g, uint32_t* pairs, float* K,
+                           float* X, float* inv) {
+    const int lane = threadIdx.x & 63;
+    const size_t i = (size_t)t * H + 64 * g + lane;
+    const float v = BF16 ? bf16_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
+    const int e = act_exponent(wave_max(fabsf(v)));
+    const int p = lane & 7, set = lane >> 3;
+    const float vs = v * ldexpf(1.0f, e) * ((p & 1) ? 0.0625f : 1.0f);
+    const _Float16 hi = (_Float16)vs;
+    const _Float16 lo = (_Float16)(vs - (float)hi);
+    const double kd = wave_sum_d((double)(float)hi + (XP == 2 ? (double)(float)lo : 0.0));
+    const float xs = wave_sum(v);
+    const uint32_t bh = __builtin_bit_cast(uint16_t, hi), bl = __builtin_bit_cast(uint16_t, lo);
+    const uint32_t ph = __shfl_down(bh, 4, 64), pl = __shfl_down(bl, 4, 64);
+    uint32_t* gp = pairs + ((size_t)t * (H / 8) + 8 * g) * XP * 4;
+    if (p < 4) {
+        gp[(set * XP + 0) * 4 + p] = bh | (ph << 16);
+        if (XP == 2) gp[(set * XP + 1) * 4 + p] = bl | (pl << 16);
     }
-    if (threadIdx.x == 0) *inv_out = ldexpf(1.0f, -e);
-}
-
-// loads x[t] into LDS as fp32 and returns max |x| (block-wide)
-template <bool BF16>
-__device__ float stage_x(const void* x, int t, int H, float* xs, float* red4) {
-    float mx = 0.0f;
-    for (int i = threadIdx.x; i < H; i += kBlock) {
-        const float v = BF16 ? bf16_to_f32(((const uint16_t*)x)[(size_t)t * H + i])
-                             : ((const float*)x)[(size_t)t * H + i];
-        xs[i] = v;
-        mx = fmaxf(mx, fabsf(v));
+    if (lane == 0) {
+        const size_t gi = (size_t)t * (H / 64) + g;
+        K[gi] = (float)(1024.0 * kd);
+        X[gi] = xs;
+        inv[gi] = ldexpf(1.0f, -e);
     }
-    mx = wave_max(mx);
-    if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
-    return mx;
 }
 
 // ---------------------------------------------------------------------------
 // exact top-k over E <= 1024 logits by one wave, then the renormalised softmax
 // gates.  Order: logit descending, ties to the lower id.
 // ---------------------------------------------------------------------------
-__device__ void topk_softmax_wave(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
+template <int Q>  // key slots per lane: E <= 64 * Q
+__device__ void topk_softmax_wave(const float* lg, int E, int k, int32_t* ids_out, float* w_out,
+                                  int want = -1, int* want_id = nullptr) {
     const int lane = threadIdx.x & 63;
-    float v[kMaxExperts / 64];
+    uint64_t key[Q];
+    const int nq = (E + 63) / 64;
+    // all loads first, unconditionally (clamped index), keys afterwards: one round trip
+    float lv[Q];
 #pragma unroll
-    for (int q = 0; q < kMaxExperts / 64; ++q) {
+    for (int q = 0; q < Q; ++q) lv[q] = lg[min(lane + 64 * q, E - 1)];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
         const int e = lane + 64 * q;
-        v[q] = e < E ? lg[e] : -INFINITY;
+        key[q] = (q < nq && e < E) ? topk_key(lv[q], e) : 0;  // 0 sorts below every real key
     }
-    uint32_t taken = 0;
-    float sel_l = -INFINITY;
+    float sel_l = 0.0f;
     int sel_id = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
+        uint64_t best = 0;
 #pragma unroll
-        for (int q = 0; q < kMaxExperts / 64; ++q) {
-            const int e = lane + 64 * q;
-            const bool cand = e < E && !((taken >> q) & 1u);
-            if (cand && (v[q] > bv || (v[q] == bv && e < bi))) {
-                bv = v[q];
-                bi = e;
-            }
-        }
+        for (int q = 0; q < Q; ++q)
+            if (q < nq) best = key[q] > best ? key[q] : best;
+        const uint64_t m = wave_max_u64(best);
+        const int id = topk_key_id(m);
+        if ((id & 63) == lane) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
+            for (int q = 0; q < Q; ++q)
+                if (q == (id >> 6)) key[q] = 0;
         }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
         if (lane == j) {
-            sel_l = bv;
-            sel_id = bi;
+            sel_l = topk_key_value(m);
+            sel_id = id;
         }
     }
+    if (want_id && lane == want) *want_id = sel_id;
+    if (!ids_out) return;
     const float m = __shfl(sel_l, 0, 64);  // the first pick is the largest
     const float ex = lane < k ? expf(sel_l - m) : 0.0f;
     float z = 0.0f;
@@ -142,94 +116,152 @@ __device__ void topk_softmax_wave(const float* lg, int E, int k, int32_t* ids_ou
 }
 
 // ---------------------------------------------------------------------------
-// k_route: grid (ceil(E/4), T), one router row per wave.
+// k_route: grid (ceil(E / (4*kRouterRowsPerWave)) [+1 prep block], T).
 // ---------------------------------------------------------------------------
+constexpr int kRouterChunksPerLane = kMaxHidden / 16 / 64;  // 16-byte chunks per lane
+
 template <int XP, bool BF16>
 __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
-    extern __shared__ float xs[];  // [H]
-    __shared__ float red4[kWaves];
-    __shared__ int is_last;
     const int t = blockIdx.y;
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    const float mx = stage_x<BF16>(a.x, t, a.H, xs, red4);
-
-    const int e = blockIdx.x * kRouterRowsPerBlock + wave;
-    if (e < a.E) {
+    const int gw = blockIdx.x * kWaves + wave;
+    if (a.prep) {
+        for (int g = gw; g < a.H / 64; g += gridDim.x * kWaves)
+            prep_group<XP, BF16>(a.x, t, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+    }
+    const int row0 = gw * kRouterRowsPerWave;
+    if (row0 >= a.E) return;
+    const int nch = a.H / 16;
+    constexpr int CPL = kRouterChunksPerLane;
+    constexpr int XV = BF16 ? 2 : 4;  // 16-byte loads per 16 activations
+    u32x4 xr[CPL][XV];
+    u32x4 wr[kRouterRowsPerWave][CPL];
+    const u32x4* xb = (const u32x4*)((const uint8_t*)a.x + (size_t)t * a.H * (BF16 ? 2 : 4));
+    const int ncl = (nch + 63) / 64;  // chunk rounds in use (uniform)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        if (i < ncl) {
+            const int c = min(lane + 64 * i, nch - 1);
+#pragma unroll
+            for (int v = 0; v < XV; ++v) xr[i][v] = xb[c * XV + v];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kRouterRowsPerWave; ++r) {
+        const int e = min(row0 + r, a.E - 1);
         const u32x4* row = (const u32x4*)(a.rq + (size_t)e * a.H);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            if (i < ncl) wr[r][i] = ldg_nt(row + min(lane + 64 * i, nch - 1));
+    }
+#pragma unroll
+    for (int r = 0; r < kRouterRowsPerWave; ++r) {
+        const int e = row0 + r;
         float acc = 0.0f;
-        for (int c = lane; c < a.H / 16; c += 64) {
-            const u32x4 q = ldg_nt(row + c);
-            const float* xv = xs + 16 * c;
-            const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            if (e < a.E && c < nch) {
+                float xf[16];
 #pragma unroll
-                for (int bsel = 0; bsel < 4; ++bsel) {
-                    const int qv = (int)(int8_t)(qq[d] >> (8 * bsel));
-                    acc = fmaf((float)qv, xv[4 * d + bsel], acc);
+                for (int v = 0; v < XV; ++v) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t word = xr[i][v][d];
+                        if (BF16) {
+                            xf[8 * v + 2 * d] = __builtin_bit_cast(float, word << 16);
+                            xf[8 * v + 2 * d + 1] = __builtin_bit_cast(float, word & 0xFFFF0000u);
+                        } else {
+                            xf[4 * v + d] = __builtin_bit_cast(float, word);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t q = wr[r][i][d];
+#pragma unroll
+                    for (int bsel = 0; bsel < 4; ++bsel)
+                        acc = fmaf((float)(int)(int8_t)(q >> (8 * bsel)), xf[4 * d + bsel], acc);
                 }
             }
         }
         acc = wave_sum(acc);
-        if (lane == 0) {
+        if (lane == 0 && e < a.E)
             a.logits[(size_t)t * a.E + e] = acc * (float)__builtin_bit_cast(_Float16, a.rs[e]);
-            __threadfence();
-        }
-    }
-    if (a.prep && blockIdx.x == 0) {
-        prep_vector<XP>(xs, a.H, mx, a.xpairs + (size_t)t * (a.H / 2) * XP,
-                        a.xK + (size_t)t * (a.H / 64), a.xX + (size_t)t * (a.H / 64), a.xinv + t);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t prev = atomicAdd(a.ctr + t, 1u);
-        is_last = prev == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    if (wave == 0) {
-        topk_softmax_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k,
-                          a.w + (size_t)t * a.k);
-        if (lane == 0) a.ctr[t] = 0;
     }
 }
 
-// k_prep: grid (T); prepares x[t] for the FFN kernels.
+// k_topk: grid (T), one wave: ids/w from the logits written by k_route.
+template <int Q>
+__global__ __launch_bounds__(64) void k_topk(RouteArgs a) {
+    const int t = blockIdx.x;
+    topk_softmax_wave<Q>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k,
+                         a.w + (size_t)t * a.k);
+}
+
+// k_prep: grid (ceil(H/256), T); one wave per 64-input group.
 template <int XP, bool BF16>
 __global__ __launch_bounds__(kBlock) void k_prep(RouteArgs a) {
-    extern __shared__ float xs[];
-    __shared__ float red4[kWaves];
-    const int t = blockIdx.x;
-    const float mx = stage_x<BF16>(a.x, t, a.H, xs, red4);
-    prep_vector<XP>(xs, a.H, mx, a.xpairs + (size_t)t * (a.H / 2) * XP,
-                    a.xK + (size_t)t * (a.H / 64), a.xX + (size_t)t * (a.H / 64), a.xinv + t);
+    const int g = blockIdx.x * kWaves + wave_id();
+    if (g < a.H / 64) prep_group<XP, BF16>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
 }
 
 // ---------------------------------------------------------------------------
 // k_gate_up: grid (k*blk_r + blk_s, T).  Lane = row of the 64-row GU tile
 // (rows 0..31 gate, 32..63 up); waves split the H/64 input groups.
 // ---------------------------------------------------------------------------
-template <int XP, int MAXG>
+constexpr int kXPrepVecsPerThread = kMaxHidden / 8 * 2 / kBlock;  // 16-byte vectors
+
+template <int XP, int MAXG, int Q>
 __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     extern __shared__ uint32_t smem[];
     const int H = a.H, NG = H / 64;
     uint32_t* xp = smem;                                 // [H/2*XP]
     float* sK = (float*)(xp + (H / 2) * XP);             // [NG]
     float* sX = sK + NG;                                 // [NG]
-    float* red = sX + NG;                                // [4][64]
-    __shared__ float s_inv;
+    float* sI = sX + NG;                                 // [NG]
+    float* red = sI + NG;                                // [4][64]
+    __shared__ int s_expert;
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int t = blockIdx.y, u = blockIdx.x;
-    int j, b, Ie;
-    const uint8_t* rec;
+    const bool routed = u < a.k * a.blk_r;
+    const int j = routed ? u / a.blk_r : a.k;
+    const int b = routed ? u - j * a.blk_r : u - a.k * a.blk_r;
+
+    // 1. the prepared activations of token t, into registers first
+    const int nvec = (H / 8) * XP;  // 16-byte vectors of pairs
+    const u32x4* gx = (const u32x4*)(a.xpairs + (size_t)t * (H / 2) * XP);
+    // Loads are unconditional with clamped addresses so that the number of
+    // loads in flight is static and every use waits only for its own data.
+    u32x4 xv[kXPrepVecsPerThread];
+#pragma unroll
+    for (int i = 0; i < kXPrepVecsPerThread; ++i)
+        xv[i] = gx[min((int)threadIdx.x + kBlock * i, nvec - 1)];
+    const int gq = min((int)threadIdx.x, NG - 1);
+    const float kx = a.xK[(size_t)t * NG + gq];
+    const float xx = a.xX[(size_t)t * NG + gq];
+    const float xi = a.xinv[(size_t)t * NG + gq];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. which expert
     bool bad = false;
-    if (u < a.k * a.blk_r) {
-        j = u / a.blk_r;
-        b = u - j * a.blk_r;
-        int e = a.ids[(size_t)t * a.k + j];
+    const uint8_t* rec;
+    int Ie;
+    if (routed) {
+        int e;
+        if (a.logits) {
+            if (wave == 0) {
+                const bool first = u == 0;
+                topk_softmax_wave<Q>(a.logits + (size_t)t * a.E, a.E, a.k,
+                                  first ? a.ids_out + (size_t)t * a.k : nullptr,
+                                  first ? a.w_out + (size_t)t * a.k : nullptr, j, &s_expert);
+            }
+            __syncthreads();
+            e = s_expert;
+        } else {
+            e = a.ids[(size_t)t * a.k + j];
+        }
         if (e < 0 || e >= a.E) {
             bad = true;
             e = 0;
@@ -237,8 +269,6 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
         rec = a.experts + (size_t)e * a.rec_bytes;
         Ie = a.I;
     } else {
-        j = a.k;
-        b = u - a.k * a.blk_r;
         rec = a.shared;
         Ie = a.Is;
     }
@@ -248,56 +278,67 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     const int g0 = wave * a.gpw_gu;
     const int g1 = min(NG, g0 + a.gpw_gu);
 
-    // issue every weight load of this wave before touching LDS
-    u32x4 W[2 * MAXG];
-    uint32_t SB[MAXG];
+    // 3. weight stream: a ring of kDepth groups in flight per wave.  Loads are
+    // unconditional (clamped to a valid group) and kept in program order, so
+    // each group's compute waits only for that group's loads.
+    constexpr int D = kDepth < MAXG ? kDepth : MAXG;
+    u32x4 W[D][2];
+    uint32_t SB[D];
 #pragma unroll
-    for (int q = 0; q < MAXG; ++q) {
-        const int g = g0 + q;
-        if (g < g1) {
-            W[2 * q] = ldg_nt((const u32x4*)(tile + (size_t)(2 * g) * 1024));
-            W[2 * q + 1] = ldg_nt((const u32x4*)(tile + (size_t)(2 * g + 1) * 1024));
-            SB[q] = ldg_nt((const uint32_t*)(sbt + (size_t)g * 256));
-        }
+    for (int q = 0; q < D; ++q) {
+        const int g = min(g0 + q, NG - 1);
+        W[q][0] = ldg_nt((const u32x4*)(tile + (size_t)(2 * g) * 1024));
+        W[q][1] = ldg_nt((const u32x4*)(tile + (size_t)(2 * g + 1) * 1024));
+        SB[q] = ldg_nt((const uint32_t*)(sbt + (size_t)g * 256));
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // stage the prepared activations of token t
-    {
-        const uint32_t* gx = a.xpairs + (size_t)t * (H / 2) * XP;
-        for (int i = threadIdx.x; i < (H / 2) * XP; i += kBlock) xp[i] = gx[i];
-        for (int i = threadIdx.x; i < NG; i += kBlock) {
-            sK[i] = a.xK[(size_t)t * NG + i];
-            sX[i] = a.xX[(size_t)t * NG + i];
-        }
-        if (threadIdx.x == 0) s_inv = a.xinv[t];
+    // 4. activations to LDS (waits only for the loads issued before the weights)
+#pragma unroll
+    for (int i = 0; i < kXPrepVecsPerThread; ++i) {
+        const int v = threadIdx.x + kBlock * i;
+        if (v < nvec) ((u32x4*)xp)[v] = xv[i];
+    }
+    if ((int)threadIdx.x < NG) {
+        sK[threadIdx.x] = kx;
+        sX[threadIdx.x] = xx;
+        sI[threadIdx.x] = xi;
     }
     __syncthreads();
 
+    // 5. dequantised dot products, group by group as the weights arrive
     float rs = 0.0f, rb = 0.0f;
 #pragma unroll
     for (int q = 0; q < MAXG; ++q) {
+        const int slot = q % D;
         const int g = g0 + q;
         if (g < g1) {
             float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const u32x4 wv = W[2 * q + half];
-                const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+                const u32x4 wv = W[slot][half];
                 const uint32_t* xc = xp + (size_t)(2 * g + half) * 16 * XP;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                    for (int p = 0; p < XP; ++p) dot_nib8(wd[m], xc + (m * XP + p) * 4, a0, a1);
+                    for (int p = 0; p < XP; ++p) dot_nib8(wv[m], xc + (m * XP + p) * 4, a0, a1);
                 }
             }
-            rs = fmaf(f16lo(SB[q]), (a0 + a1) - sK[g], rs);
-            rb = fmaf(f16hi(SB[q]), sX[g], rb);
+            rs = fmaf(f16lo(SB[slot]) * sI[g], (a0 + a1) - sK[g], rs);
+            rb = fmaf(f16hi(SB[slot]), sX[g], rb);
         }
+        if (q + D < MAXG) {  // refill the slot just consumed
+            const int gn = min(g0 + q + D, NG - 1);
+            W[slot][0] = ldg_nt((const u32x4*)(tile + (size_t)(2 * gn) * 1024));
+            W[slot][1] = ldg_nt((const u32x4*)(tile + (size_t)(2 * gn + 1) * 1024));
+            SB[slot] = ldg_nt((const uint32_t*)(sbt + (size_t)gn * 256));
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    red[wave * 64 + lane] = fmaf(rs, s_inv, rb);
+    red[wave * 64 + lane] = rs + rb;
     __syncthreads();
     if (wave != 0) return;
 
-    // wave 0: gate/up sums in wave order, h = silu(g) * u, then h prepared
+    // 6. wave 0: gate/up sums in wave order, h = silu(g) * u, then h prepared
     float h = 0.0f;
     if (lane < 32) {
         float g = 0.0f, uu = 0.0f;
@@ -336,12 +377,10 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
 // ---------------------------------------------------------------------------
 // k_down: grid (n_otiles * n_items, T).  Lane = output row of a 64-row tile;
 // waves split the item's input groups (64 inputs of I = two h blocks).
-// mode bit 0: write per-expert outputs eo; bit 1: write combined y.
 // ---------------------------------------------------------------------------
 template <int MAXG>
 __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     extern __shared__ uint32_t smem[];
-    __shared__ int is_last;
     const int H = a.H;
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int t = blockIdx.y;
@@ -360,8 +399,8 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
         j = a.k;
         rec = a.shared;
         Ie = a.Is;
-        ga = (item - a.k) * a.gi;
-        gb = min(ga + a.gi, a.Is / 64);
+        ga = (item - a.k) * a.gis;
+        gb = min(ga + a.gis, a.Is / 64);
     }
     const int o = ot * 64 + lane;
     const int g0 = ga + wave * a.gpw_dn;
@@ -369,33 +408,47 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     const uint8_t* dblk = rec + (size_t)32 * H + (size_t)o * 16;
     const uint8_t* dsb = rec + (size_t)3 * H * Ie / 2 + (size_t)8 * H + (size_t)o * 4;
 
-    u32x4 W[2 * MAXG];
-    uint32_t SB[MAXG];
-#pragma unroll
-    for (int q = 0; q < MAXG; ++q) {
-        const int g = g0 + q;
-        if (g < g1) {
-            W[2 * q] = ldg_nt((const u32x4*)(dblk + (size_t)48 * H * (2 * g)));
-            W[2 * q + 1] = ldg_nt((const u32x4*)(dblk + (size_t)48 * H * (2 * g + 1)));
-            SB[q] = ldg_nt((const uint32_t*)(dsb + (size_t)12 * H * g));
-        }
-    }
-    // stage h of (t, j), blocks [2ga, 2gb)
+    // h of (t, j), blocks [2ga, 2gb): loaded before the weights
     const int nb = 2 * (gb - ga);
     uint32_t* sp = smem;                             // [nb][16*kHParts]
     float* sK = (float*)(sp + nb * 16 * kHParts);    // [nb]
     float* sH = sK + nb;                             // [nb]
     float* sI = sH + nb;                             // [nb]
     float* red = sI + nb;                            // [4][64]
-    {
-        const size_t slot0 = ((size_t)t * (a.k + 1) + j) * a.blk_max + 2 * ga;
-        const uint32_t* gp = a.hpairs + slot0 * 16 * kHParts;
-        for (int i = threadIdx.x; i < nb * 16 * kHParts; i += kBlock) sp[i] = gp[i];
-        for (int i = threadIdx.x; i < nb; i += kBlock) {
-            sK[i] = a.hK[slot0 + i];
-            sH[i] = a.hHs[slot0 + i];
-            sI[i] = a.hinv[slot0 + i];
-        }
+    const size_t slot0 = ((size_t)t * (a.k + 1) + j) * a.blk_max + 2 * ga;
+    // at most 2 * kMaxDownGroups h blocks per item (<= kBlock), 4*kHParts vectors each
+    constexpr int HV = (2 * kMaxDownGroups * 4 * kHParts + kBlock - 1) / kBlock;
+    const u32x4* gp = (const u32x4*)(a.hpairs + slot0 * 16 * kHParts);
+    const int nvec = nb * 4 * kHParts;
+    // unconditional loads with clamped addresses (static count in flight)
+    u32x4 hv[HV];
+#pragma unroll
+    for (int i = 0; i < HV; ++i) hv[i] = gp[min((int)threadIdx.x + kBlock * i, nvec - 1)];
+    const int bq = min((int)threadIdx.x, nb - 1);
+    const float hk = a.hK[slot0 + bq];
+    const float hs = a.hHs[slot0 + bq];
+    const float hi = a.hinv[slot0 + bq];
+    __builtin_amdgcn_sched_barrier(0);
+
+    u32x4 W[2 * MAXG];
+    uint32_t SB[MAXG];
+#pragma unroll
+    for (int q = 0; q < MAXG; ++q) {
+        const int g = min(g0 + q, gb - 1);  // past this wave's range: re-read a valid group
+        W[2 * q] = ldg_nt((const u32x4*)(dblk + (size_t)48 * H * (2 * g)));
+        W[2 * q + 1] = ldg_nt((const u32x4*)(dblk + (size_t)48 * H * (2 * g + 1)));
+        SB[q] = ldg_nt((const uint32_t*)(dsb + (size_t)12 * H * g));
+        __builtin_amdgcn_sched_barrier(0);  // keep issue order = consumption order
+    }
+#pragma unroll
+    for (int i = 0; i < HV; ++i) {
+        const int v = threadIdx.x + kBlock * i;
+        if (v < nvec) ((u32x4*)sp)[v] = hv[i];
+    }
+    if ((int)threadIdx.x < nb) {
+        sK[threadIdx.x] = hk;
+        sH[threadIdx.x] = hs;
+        sI[threadIdx.x] = hi;
     }
     __syncthreads();
 
@@ -409,14 +462,13 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
             for (int half = 0; half < 2; ++half) {
                 const int lb = 2 * (g - ga) + half;  // local h block
                 const u32x4 wv = W[2 * q + half];
-                const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
                 const uint32_t* hc = sp + (size_t)lb * 16 * kHParts;
                 float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
 #pragma unroll
                     for (int p = 0; p < kHParts; ++p)
-                        dot_nib8(wd[m], hc + (m * kHParts + p) * 4, a0, a1);
+                        dot_nib8(wv[m], hc + (m * kHParts + p) * 4, a0, a1);
                 }
                 part = fmaf((a0 + a1) - sK[lb], sI[lb], part);
             }
@@ -427,34 +479,49 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     }
     red[wave * 64 + lane] = row;
     __syncthreads();
-    if (wave == 0) {
-        float r = 0.0f;
+    if (wave != 0) return;
+
+    // wave 0: this item's partial, then the arrival count for the output tile
+    float r = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) r += red[w * 64 + lane];
-        a.dpart[(((size_t)t * a.n_otiles + ot) * a.n_items + item) * 64 + lane] = r;
-        __threadfence();
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t prev = atomicAdd(a.dctr + (size_t)t * a.n_otiles + ot, 1u);
-        is_last = prev == (uint32_t)a.n_items - 1;
-    }
-    __syncthreads();
-    if (!is_last || wave != 0) return;
-    __threadfence();
-    const float* dp = a.dpart + ((size_t)t * a.n_otiles + ot) * a.n_items * 64 + lane;
+    for (int w = 0; w < kWaves; ++w) r += red[w * 64 + lane];
+    float* dp = a.dpart + ((size_t)t * a.n_otiles + ot) * a.n_items * 64 + lane;
+    __hip_atomic_store(dp + item * 64, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // the coherent store above has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    uint32_t* ctr = a.dctr + ((size_t)t * a.n_otiles + ot) * kCounterStride;
+    uint32_t prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0, 64);
+    if (prev != (uint32_t)a.n_items - 1) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    // last arrival: load every item's partial and the gate weights first, then
+    // sum the items in a fixed order
+    float pv[kMaxItems], wv[kMaxTopK];
+#pragma unroll
+    for (int it = 0; it < kMaxItems; ++it)
+        pv[it] = __hip_atomic_load(dp + min(it, a.n_items - 1) * 64, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int jj = 0; jj < kMaxTopK; ++jj)
+        wv[jj] = a.w ? a.w[(size_t)t * a.k + min(jj, a.k - 1)] : 0.0f;
     float ys = 0.0f;
-    for (int jj = 0; jj < a.k; ++jj) {
-        const float v = dp[jj * 64];
-        if (a.eo) a.eo[((size_t)t * (a.k + 1) + jj) * H + o] = v;
-        ys = fmaf(a.w ? a.w[(size_t)t * a.k + jj] : 0.0f, v, ys);
+#pragma unroll
+    for (int jj = 0; jj < kMaxTopK; ++jj) {
+        if (jj < a.k) {
+            if (a.eo) a.eo[((size_t)t * (a.k + 1) + jj) * H + o] = pv[jj];
+            ys = fmaf(wv[jj], pv[jj], ys);
+        }
     }
     float es = 0.0f;
-    for (int it = a.k; it < a.n_items; ++it) es += dp[it * 64];
+#pragma unroll
+    for (int it = 0; it < kMaxItems; ++it)
+        if (it >= a.k && it < a.n_items) es += pv[it];
     if (a.eo) a.eo[((size_t)t * (a.k + 1) + a.k) * H + o] = es;
     if (a.y) a.y[(size_t)t * H + o] = ys + es;
-    if (lane == 0) a.dctr[(size_t)t * a.n_otiles + ot] = 0;
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // k_combine: grid (ceil(H/256), T)
@@ -477,31 +544,41 @@ __global__ void k_clear_word(uint32_t* p) { *p = 0u; }
 // host-side launchers (called from moe_layer.hip)
 // ---------------------------------------------------------------------------
 hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
-    const dim3 grid((a.E + kRouterRowsPerBlock - 1) / kRouterRowsPerBlock, T);
-    const size_t sh = (size_t)a.H * sizeof(float);
+    const int rpb = kWaves * kRouterRowsPerWave;
+    int nb = (a.E + rpb - 1) / rpb;
+    if (a.prep) nb = max(nb, (a.H / 64 + kWaves - 1) / kWaves);
+    const dim3 grid(nb, T);
     if (act_bf16)
-        hipLaunchKernelGGL((k_route<1, true>), grid, dim3(kBlock), sh, s, a);
+        hipLaunchKernelGGL((k_route<1, true>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_route<2, false>), grid, dim3(kBlock), sh, s, a);
+        hipLaunchKernelGGL((k_route<2, false>), grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const RouteArgs& a, int T, hipStream_t s) {
+    if (a.E <= 64) hipLaunchKernelGGL(k_topk<1>, dim3(T), dim3(64), 0, s, a);
+    else if (a.E <= 128) hipLaunchKernelGGL(k_topk<2>, dim3(T), dim3(64), 0, s, a);
+    else if (a.E <= 256) hipLaunchKernelGGL(k_topk<4>, dim3(T), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
-    const size_t sh = (size_t)a.H * sizeof(float);
+    const dim3 grid((a.H / 64 + kWaves - 1) / kWaves, T);
     if (act_bf16)
-        hipLaunchKernelGGL((k_prep<1, true>), dim3(T), dim3(kBlock), sh, s, a);
+        hipLaunchKernelGGL((k_prep<1, true>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_prep<2, false>), dim3(T), dim3(kBlock), sh, s, a);
+        hipLaunchKernelGGL((k_prep<2, false>), grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
-template <int XP>
-static hipError_t launch_gu_xp(const FfnArgs& a, int T, hipStream_t s) {
+template <int XP, int Q>
+static hipError_t launch_gu_xq(const FfnArgs& a, int T, hipStream_t s) {
     const dim3 grid(a.k * a.blk_r + a.blk_s, T);
     const int NG = a.H / 64;
-    const size_t sh = ((size_t)(a.H / 2) * XP + 2 * NG + kWaves * 64) * 4;
+    const size_t sh = ((size_t)(a.H / 2) * XP + 3 * NG + kWaves * 64) * 4;
     const int m = a.gpw_gu;
-#define MOE_GU(MG) hipLaunchKernelGGL((k_gate_up<XP, MG>), grid, dim3(kBlock), sh, s, a)
+#define MOE_GU(MG) hipLaunchKernelGGL((k_gate_up<XP, MG, Q>), grid, dim3(kBlock), sh, s, a)
     if (m <= 4) MOE_GU(4);
     else if (m <= 8) MOE_GU(8);
     else if (m <= 12) MOE_GU(12);
@@ -512,13 +589,22 @@ static hipError_t launch_gu_xp(const FfnArgs& a, int T, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int XP>
+static hipError_t launch_gu_xp(const FfnArgs& a, int T, hipStream_t s) {
+    if (!a.logits) return launch_gu_xq<XP, 1>(a, T, s);  // no selection in the kernel
+    if (a.E <= 64) return launch_gu_xq<XP, 1>(a, T, s);
+    if (a.E <= 128) return launch_gu_xq<XP, 2>(a, T, s);
+    if (a.E <= 256) return launch_gu_xq<XP, 4>(a, T, s);
+    return launch_gu_xq<XP, 16>(a, T, s);
+}
+
 hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, hipStream_t s) {
     return xparts == 2 ? launch_gu_xp<2>(a, T, s) : launch_gu_xp<1>(a, T, s);
 }
 
 hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {
     const dim3 grid(a.n_otiles * a.n_items, T);
-    const int nb = 2 * a.gi;  // blocks staged per item (upper bound)
+    const int nb = 2 * max(a.gi, a.gis);  // blocks staged per item (upper bound)
     const size_t sh = ((size_t)nb * (16 * kHParts + 3) + kWaves * 64) * 4;
     const int m = a.gpw_dn;
 #define MOE_DN(MG) hipLaunchKernelGGL((k_down<MG>), grid, dim3(kBlock), sh, s, a)

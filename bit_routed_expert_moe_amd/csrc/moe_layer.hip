@@ -15,6 +15,7 @@
 namespace moe {
 hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s);
 hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s);
+hipError_t launch_topk(const RouteArgs& a, int T, hipStream_t s);
 hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
@@ -33,7 +34,8 @@ struct moe_layer {
     int blk_s;     // Is / 32
     int blk_max;
     int xparts;    // fp16 parts per activation: 1 for bf16, 2 for fp32
-    int gi;        // input groups per down item
+    int gi;        // input groups per routed down item
+    int gis;       // input groups per shared down item
     int n_items;   // down items per output tile
     int n_otiles;  // H / 64
     int gpw_gu, gpw_dn;
@@ -44,7 +46,7 @@ namespace {
 thread_local std::string g_last_error;
 
 // ---- per-launch event timing (moe_profile_*) ----
-enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4 };
+enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4, K_TOPK = 5 };
 struct ProfRec {
     int kid;
     hipEvent_t a, b;
@@ -92,11 +94,11 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     };
     o.err = take(4);
     o.rctr = take((size_t)T * 4);
-    o.dctr = take((size_t)T * L->n_otiles * 4);
+    o.dctr = take((size_t)T * L->n_otiles * kCounterStride * 4);
     o.xpairs = take((size_t)T * (H / 2) * L->xparts * 4);
     o.xK = take((size_t)T * L->NG * 4);
     o.xX = take((size_t)T * L->NG * 4);
-    o.xinv = take((size_t)T * 4);
+    o.xinv = take((size_t)T * L->NG * 4);
     o.logits = take((size_t)T * L->d.n_experts * 4);
     const size_t nslot = (size_t)T * (k + 1) * L->blk_max;
     o.hpairs = take(nslot * 16 * kHParts * 4);
@@ -144,8 +146,13 @@ RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, 
 }
 
 FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t* ws,
-                 const WsLayout& o, float* y, float* eo) {
+                 const WsLayout& o, float* y, float* eo, bool select) {
     FfnArgs a{};
+    if (select) {  // k_gate_up selects from the logits and writes ids/w itself
+        a.logits = (const float*)(ws + o.logits);
+        a.ids_out = const_cast<int32_t*>(ids);
+        a.w_out = const_cast<float*>(w);
+    }
     a.experts = L->w.experts;
     a.shared = L->w.shared;
     a.rec_bytes = L->rec_bytes;
@@ -176,6 +183,7 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.n_otiles = L->n_otiles;
     a.n_items = L->n_items;
     a.gi = L->gi;
+    a.gis = L->gis;
     a.gpw_dn = L->gpw_dn;
     return a;
 }
@@ -206,8 +214,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     if (d.group != 64) return fail(MOE_ERR_SHAPE, "group must be 64");
     if (d.hidden <= 0 || d.hidden % 64 || d.hidden > kMaxHidden)
         return fail(MOE_ERR_SHAPE, "hidden must be a positive multiple of 64, at most 8192");
-    if (d.inter <= 0 || d.inter % 64 || d.inter > 16384)
-        return fail(MOE_ERR_SHAPE, "inter must be a positive multiple of 64, at most 16384");
+    if (d.inter <= 0 || d.inter % 64 || d.inter > 64 * kMaxDownGroups)
+        return fail(MOE_ERR_SHAPE, "inter must be a positive multiple of 64, at most 4096");
     if (d.shared_inter < 0 || d.shared_inter % 64 || d.shared_inter > 16384)
         return fail(MOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 64, at most 16384");
     if (d.n_experts < 1 || d.n_experts > kMaxExperts)
@@ -247,11 +255,12 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     L->xparts = d.act_dtype == MOE_F32 ? 2 : 1;
     L->gi = d.inter / 64;
     const int sg = d.shared_inter / 64;
-    L->n_items = d.top_k + (sg + L->gi - 1) / L->gi;
+    L->gis = std::max(L->gi, (sg + kMaxSharedItems - 1) / kMaxSharedItems);
+    L->n_items = d.top_k + (sg + L->gis - 1) / L->gis;
+    L->gpw_dn = (std::max(L->gi, L->gis) + kWaves - 1) / kWaves;
     L->n_otiles = d.hidden / 64;
     L->gpw_gu = (L->NG + kWaves - 1) / kWaves;
-    L->gpw_dn = (L->gi + kWaves - 1) / kWaves;
-    if (L->gpw_gu > 32 || L->gpw_dn > 16) {
+    if (L->gpw_gu > kMaxGateUpGroupsPerWave || std::max(L->gi, L->gis) > kMaxDownGroups) {
         delete L;
         return fail(MOE_ERR_SHAPE, "shape exceeds the kernels' per-wave register tiles");
     }
@@ -277,8 +286,11 @@ moe_status moe_route_topk(moe_layer_t L, const void* x, int32_t T, int32_t* ids,
     if (!ids || !w) return fail(MOE_ERR_ARG, "null ids or w");
     const WsLayout o = ws_layout(L, T);
     RouteArgs a = route_args(L, x, ids, w, (uint8_t*)workspace, o, 0);
-    hipError_t e = timed(K_ROUTE, (hipStream_t)stream, [&] { return launch_route(a, T, L->d.act_dtype == MOE_BF16, (hipStream_t)stream); });
-    return e == hipSuccess ? MOE_OK : hip_fail(e, "router launch");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(a, T, L->d.act_dtype == MOE_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    e = timed(K_TOPK, s, [&] { return launch_topk(a, T, s); });
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "top-k launch");
 }
 
 moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t* ids,
@@ -292,7 +304,7 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     RouteArgs ra = route_args(L, x, nullptr, nullptr, ws, o, 1);
     hipError_t e = timed(K_PREP, s, [&] { return launch_prep(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "prep launch");
-    FfnArgs fa = ffn_args(L, ids, nullptr, ws, o, nullptr, expert_out);
+    FfnArgs fa = ffn_args(L, ids, nullptr, ws, o, nullptr, expert_out, false);
     if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
     if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
@@ -320,7 +332,7 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     RouteArgs ra = route_args(L, x, ids, w, ws, o, 1);
     hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "router launch");
-    FfnArgs fa = ffn_args(L, ids, w, ws, o, y, nullptr);
+    FfnArgs fa = ffn_args(L, ids, w, ws, o, y, nullptr, true);
     if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
     if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;

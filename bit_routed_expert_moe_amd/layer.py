@@ -25,7 +25,7 @@ EXPORTS = ["moe_expert_record_bytes", "moe_layer_create", "moe_layer_destroy",
            "moe_layer_forward", "moe_stack_forward", "moe_poll_device_error",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
            "moe_status_str", "moe_last_error"]
-KERNEL_NAMES = {0: "route_topk", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine"}
+KERNEL_NAMES = {0: "route", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine", 5: "topk"}
 
 
 class MoeError(RuntimeError):

@@ -80,9 +80,9 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };                 /* activation / output dtype
 enum { MOE_SOFTMAX_TOPK = 0, MOE_SIGMOID_TOPK = 1 }; /* gate functions            */
 
 typedef struct moe_layer_desc {
-    int32_t hidden;        /* H, multiple of 64                                   */
+    int32_t hidden;        /* H, multiple of 64, <= 8192                          */
     int32_t n_experts;     /* E routed experts, 1..1024                           */
-    int32_t inter;         /* I, routed expert intermediate size, multiple of 64  */
+    int32_t inter;         /* I, routed expert intermediate size, multiple of 64, <= 4096 */
     int32_t top_k;         /* k, 1..min(E, 16)                                    */
     int32_t shared_inter;  /* intermediate size of the shared expert, 0 = none    */
     int32_t group;         /* quantisation group; must be 64                      */
@@ -166,8 +166,8 @@ moe_status moe_poll_device_error(moe_layer_t layer, void* workspace, void* strea
 /* Measurement support.  While profiling is on, every kernel the library
  * launches is bracketed by two hipEvents recorded on its launch stream, up to
  * `capacity` launches.  moe_profile_read synchronises those events and writes,
- * per recorded launch, the kernel id (0 router/top-k, 1 activation prep,
- * 2 gate/up, 3 down/combine-in-place, 4 combine) and the elapsed milliseconds;
+ * per recorded launch, the kernel id (0 router, 1 activation prep, 2 gate/up,
+ * 3 down with in-place combine, 4 combine, 5 top-k) and the elapsed milliseconds;
  * it returns the number of records (or a negative status) and clears them.
  * Profiling state is process-wide and not thread-safe; do not profile inside
  * stream capture.  Errors: ARG, HIP, NOMEM. */
