@@ -116,6 +116,103 @@ def cpu_baseline(wl, xs_host, seconds):
             "kind": "oracle", "sample": f"{n} token-layers, {spent:.1f} s"}
 
 
+def run_cached(args, wl):
+    """Out-of-core decode: each layer keeps wl.n_slots HBM slots filled from a
+    pinned host pool of all its experts (LFU).  Launched eagerly: every layer
+    synchronises the host on its expert ids."""
+    import torch
+    import synth
+    import synth.gpu
+    from bit_routed_expert_moe_amd import Layer, record_bytes
+
+    H, E, I, k, Is, L = wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.n_layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    rb = record_bytes(H, I)
+    t_setup = time.time()
+    layers, keep = [], []
+    staging = torch.empty(E * rb, dtype=torch.uint8, device=dev)
+    for l in range(L):
+        rq, rs = synth.router(wl.seed, l, E, H)
+        synth.gpu.fill_records(staging, H, I, wl.seed, l, 0, E)
+        host = torch.empty(E * rb, dtype=torch.uint8, pin_memory=True)
+        host.copy_(staging)
+        shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
+        synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
+        slots = torch.zeros(wl.n_slots * rb, dtype=torch.uint8, device=dev)
+        layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
+                            torch.from_numpy(rs.view(np.float16)).to(dev), None, shared,
+                            act=wl.act, n_slots=wl.n_slots, host_pool=host, slots=slots))
+    del staging
+    S = wl.steps
+    xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][1][H]
+    xs = torch.from_numpy(synth.quantize_act(xs_host, wl.act).view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = layers[0].workspace(1)
+    ids = torch.empty(L, 1, k, dtype=torch.int32, device=dev)
+    w = torch.empty(L, 1, k, dtype=torch.float32, device=dev)
+    y = torch.empty(L, 1, H, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f} s: {L} layers x {E} experts in pinned host memory "
+        f"({L * E * rb / 1e9:.2f} GB), {wl.n_slots} slots per layer")
+
+    def run_step(s):
+        for l in range(L):
+            layers[l].forward(xs[s, l], ws, out=(ids[l], w[l], y[l]))
+
+    # pinned host -> device bandwidth in the same run (1 GiB, the bound's denominator)
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d_gbs = 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    W = min(args.warmup, S)
+    K = min(args.steps, S - W)
+    for s in range(W):
+        run_step(s)
+    torch.cuda.synchronize()
+    h0 = sum(l_.cache_stats()[0] for l_ in layers)
+    m0 = sum(l_.cache_stats()[1] for l_ in layers)
+    t0 = time.perf_counter()
+    for s in range(W, W + K):
+        run_step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h1 = sum(l_.cache_stats()[0] for l_ in layers)
+    m1 = sum(l_.cache_stats()[1] for l_ in layers)
+    ms_per_step = wall * 1e3 / K
+    hit_timed = (h1 - h0) / max(1, (h1 - h0) + (m1 - m0))
+    hit_all = h1 / max(1, h1 + m1)
+    miss_bytes_step = (m1 - m0) / K * rb
+    hbm_bytes_step = L * wl.token_layer_bytes + miss_bytes_step  # reads + slot writes
+    bound_ms = max(hbm_bytes_step / (PEAK_HBM_GBS * 1e9), miss_bytes_step / (h2d_gbs * 1e9)) * 1e3
+    out = {
+        "metric": METRIC, "value": round(L / (ms_per_step * 1e-3), 1), "unit": "tok/s per layer",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
+                   "shared_inter": Is, "layers": L, "batch": 1, "act": wl.act,
+                   "routing": wl.routing, "n_slots": wl.n_slots},
+        "stack_tok_s": round(1e3 / ms_per_step, 2),
+        "hit_rate_timed": round(hit_timed, 4), "hit_rate_all_steps": round(hit_all, 4),
+        "miss_bytes_per_step": int(miss_bytes_step), "h2d_gbps": round(h2d_gbs, 1),
+        "roofline": {"bound": "pcie", "achieved": round(miss_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+                     "peak": round(h2d_gbs, 1), "unit": "GB/s",
+                     "frac": round(bound_ms / ms_per_step, 4), "traffic": None,
+                     "note": "frac = max(HBM bytes / 8 TB/s, miss bytes / measured H2D) / step time"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,8 +250,10 @@ def main():
     from bit_routed_expert_moe_amd import KernelTimer, Layer, record_bytes, stack_forward
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.n_slots or wl.n_tokens != 1:
-        print(f"workload {wl.name} is not a resident decode stack", file=sys.stderr)
+    if wl.n_slots:
+        return run_cached(args, wl)
+    if wl.n_tokens != 1:
+        print(f"workload {wl.name} is not a decode stack", file=sys.stderr)
         sys.exit(2)
     H, E, I, k, Is, L, T = (wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter,
                             wl.n_layers, wl.n_tokens)

@@ -45,6 +45,9 @@ struct FfnArgs {
     const uint8_t* experts;  // E records
     const uint8_t* shared;   // shared record or nullptr
     size_t rec_bytes;
+    const uint8_t* slots;    // slot cache: n_slots records (nullptr = resident pool)
+    const int32_t* slot_ids; // [T][k] slot holding each selected expert (with slots)
+    int unit_offset;         // k_gate_up: first unit of this launch (split launches)
     const int32_t* ids;      // [T][k] selection (read by k_down; by k_gate_up unless logits)
     const float* w;          // [T][k] gate weights (fused combine only)
     const float* logits;     // [T][E]: if set, k_gate_up selects the experts itself

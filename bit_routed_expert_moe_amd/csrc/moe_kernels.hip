@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     __shared__ int s_expert;
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int t = blockIdx.y, u = blockIdx.x;
+    const int t = blockIdx.y, u = blockIdx.x + a.unit_offset;
     const bool routed = u < a.k * a.blk_r;
     const int j = routed ? u / a.blk_r : a.k;
     const int b = routed ? u - j * a.blk_r : u - a.k * a.blk_r;
@@ -266,7 +266,8 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
             bad = true;
             e = 0;
         }
-        rec = a.experts + (size_t)e * a.rec_bytes;
+        rec = a.slots ? a.slots + (size_t)a.slot_ids[(size_t)t * a.k + j] * a.rec_bytes
+                      : a.experts + (size_t)e * a.rec_bytes;
         Ie = a.I;
     } else {
         rec = a.shared;
@@ -391,7 +392,8 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
         j = item;
         int e = a.ids[(size_t)t * a.k + j];
         if (e < 0 || e >= a.E) e = 0;  // h of this slot is NaN already
-        rec = a.experts + (size_t)e * a.rec_bytes;
+        rec = a.slots ? a.slots + (size_t)a.slot_ids[(size_t)t * a.k + j] * a.rec_bytes
+                      : a.experts + (size_t)e * a.rec_bytes;
         Ie = a.I;
         ga = 0;
         gb = a.I / 64;
@@ -573,8 +575,8 @@ hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
 }
 
 template <int XP, int Q>
-static hipError_t launch_gu_xq(const FfnArgs& a, int T, hipStream_t s) {
-    const dim3 grid(a.k * a.blk_r + a.blk_s, T);
+static hipError_t launch_gu_xq(const FfnArgs& a, int T, int n_units, hipStream_t s) {
+    const dim3 grid(n_units, T);
     const int NG = a.H / 64;
     const size_t sh = ((size_t)(a.H / 2) * XP + 3 * NG + kWaves * 64) * 4;
     const int m = a.gpw_gu;
@@ -590,16 +592,18 @@ static hipError_t launch_gu_xq(const FfnArgs& a, int T, hipStream_t s) {
 }
 
 template <int XP>
-static hipError_t launch_gu_xp(const FfnArgs& a, int T, hipStream_t s) {
-    if (!a.logits) return launch_gu_xq<XP, 1>(a, T, s);  // no selection in the kernel
-    if (a.E <= 64) return launch_gu_xq<XP, 1>(a, T, s);
-    if (a.E <= 128) return launch_gu_xq<XP, 2>(a, T, s);
-    if (a.E <= 256) return launch_gu_xq<XP, 4>(a, T, s);
-    return launch_gu_xq<XP, 16>(a, T, s);
+static hipError_t launch_gu_xp(const FfnArgs& a, int T, int n, hipStream_t s) {
+    if (!a.logits) return launch_gu_xq<XP, 1>(a, T, n, s);  // no selection in the kernel
+    if (a.E <= 64) return launch_gu_xq<XP, 1>(a, T, n, s);
+    if (a.E <= 128) return launch_gu_xq<XP, 2>(a, T, n, s);
+    if (a.E <= 256) return launch_gu_xq<XP, 4>(a, T, n, s);
+    return launch_gu_xq<XP, 16>(a, T, n, s);
 }
 
-hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, hipStream_t s) {
-    return xparts == 2 ? launch_gu_xp<2>(a, T, s) : launch_gu_xp<1>(a, T, s);
+// units [a.unit_offset, a.unit_offset + n_units) of the k*blk_r routed + blk_s shared units
+hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, int n_units, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    return xparts == 2 ? launch_gu_xp<2>(a, T, n_units, s) : launch_gu_xp<1>(a, T, n_units, s);
 }
 
 hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {

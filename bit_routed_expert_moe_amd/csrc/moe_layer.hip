@@ -16,7 +16,7 @@ namespace moe {
 hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s);
 hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s);
 hipError_t launch_topk(const RouteArgs& a, int T, hipStream_t s);
-hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, int n_units, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
@@ -24,9 +24,29 @@ hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
 
 using namespace moe;
 
+// HBM expert-slot cache of one layer: n_slots device records filled on a
+// side stream from a pinned host pool of all E records.  LFU: every selection
+// adds one to its expert's count (never decayed); a miss always enters, into a
+// free slot if any (lowest index), otherwise replacing the resident expert that
+// the current token did not select with the smallest count, then the least
+// recently used, then the lowest slot.
+struct SlotCache {
+    int n_slots = 0;
+    std::vector<int32_t> slot_of;     // [E], -1 when not resident
+    std::vector<int32_t> expert_in;   // [n_slots], -1 when free
+    std::vector<uint64_t> count;      // [E]
+    std::vector<uint64_t> last_use;   // [n_slots]
+    uint64_t tick = 0, hits = 0, misses = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_ids = nullptr, ev_copies = nullptr;
+    int32_t* h_ids = nullptr;         // pinned staging [k]
+    int32_t* h_slots = nullptr;       // pinned staging [k]
+};
+
 struct moe_layer {
     moe_layer_desc d;
     moe_layer_weights w;
+    SlotCache cache;
     size_t rec_bytes;
     size_t shared_rec_bytes;
     int NG;        // H / 64
@@ -80,7 +100,8 @@ moe_status hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t err, rctr, dctr, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, total;
+    size_t err, rctr, dctr, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
+        total;
 };
 
 WsLayout ws_layout(const moe_layer* L, int T) {
@@ -106,6 +127,7 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     o.hHs = take(nslot * 4);
     o.hinv = take(nslot * 4);
     o.dpart = take((size_t)T * L->n_otiles * L->n_items * 64 * 4);
+    o.slot_ids = take((size_t)T * k * 4);
     o.total = off;
     return o;
 }
@@ -156,6 +178,10 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.experts = L->w.experts;
     a.shared = L->w.shared;
     a.rec_bytes = L->rec_bytes;
+    if (L->cache.n_slots) {
+        a.slots = L->w.slots;
+        a.slot_ids = (const int32_t*)(ws + o.slot_ids);
+    }
     a.ids = ids;
     a.w = w;
     a.xpairs = (const uint32_t*)(ws + o.xpairs);
@@ -197,6 +223,83 @@ moe_status check_call(const moe_layer* L, const void* x, int32_t T, const void* 
     return MOE_OK;
 }
 
+// Routed + shared FFN of one decode token through the slot cache.  ids are on
+// the device (written earlier on `s`).  The host reads them, updates the LFU,
+// copies the missing records into their slots on the side stream, runs the
+// shared expert's gate/up meanwhile, then the routed gate/up and the down
+// kernel once the copies have landed.
+moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayout& o,
+                      uint8_t* ws, hipStream_t s) {
+    SlotCache& c = L->cache;
+    const int k = L->d.top_k;
+    hipError_t e = hipMemcpyAsync(c.h_ids, ids, sizeof(int32_t) * k, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(c.ev_ids, s);
+    if (e == hipSuccess) e = hipEventSynchronize(c.ev_ids);
+    if (e != hipSuccess) return hip_fail(e, "reading the selected experts");
+    ++c.tick;
+    for (int j = 0; j < k; ++j) {
+        const int ex = c.h_ids[j];
+        if (ex < 0 || ex >= L->d.n_experts)
+            return fail(MOE_ERR_ARG, "selected expert id out of range");
+    }
+    bool copies = false;
+    for (int j = 0; j < k; ++j) {
+        const int ex = c.h_ids[j];
+        c.count[ex] += 1;
+        int slot = c.slot_of[ex];
+        if (slot >= 0) {
+            ++c.hits;
+        } else {
+            ++c.misses;
+            for (int q = 0; q < c.n_slots && slot < 0; ++q)
+                if (c.expert_in[q] < 0) slot = q;
+            if (slot < 0) {
+                for (int q = 0; q < c.n_slots; ++q) {
+                    const int r = c.expert_in[q];
+                    bool selected = false;
+                    for (int jj = 0; jj < k; ++jj) selected |= c.h_ids[jj] == r;
+                    if (selected) continue;
+                    if (slot < 0 || c.count[r] < c.count[c.expert_in[slot]] ||
+                        (c.count[r] == c.count[c.expert_in[slot]] &&
+                         c.last_use[q] < c.last_use[slot]))
+                        slot = q;
+                }
+                c.slot_of[c.expert_in[slot]] = -1;
+            }
+            c.expert_in[slot] = ex;
+            c.slot_of[ex] = slot;
+            if (!copies) {  // the side stream must not overwrite a slot still being read
+                if ((e = hipStreamWaitEvent(c.side, c.ev_ids, 0)) != hipSuccess)
+                    return hip_fail(e, "side stream wait");
+                copies = true;
+            }
+            e = hipMemcpyAsync(L->w.slots + (size_t)slot * L->rec_bytes,
+                               L->w.host_pool + (size_t)ex * L->rec_bytes, L->rec_bytes,
+                               hipMemcpyHostToDevice, c.side);
+            if (e != hipSuccess) return hip_fail(e, "expert copy into its slot");
+        }
+        c.last_use[slot] = c.tick;
+        c.h_slots[j] = slot;
+    }
+    e = hipMemcpyAsync(ws + o.slot_ids, c.h_slots, sizeof(int32_t) * k, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "slot table copy");
+    const int routed_units = k * L->blk_r;
+    fa.unit_offset = routed_units;  // shared expert first, overlapping the copies
+    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, 1, L->xparts, L->blk_s, s); })) != hipSuccess)
+        return hip_fail(e, "gate/up launch");
+    if (copies) {
+        if ((e = hipEventRecord(c.ev_copies, c.side)) != hipSuccess ||
+            (e = hipStreamWaitEvent(s, c.ev_copies, 0)) != hipSuccess)
+            return hip_fail(e, "copy ordering");
+    }
+    fa.unit_offset = 0;
+    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, 1, L->xparts, routed_units, s); })) != hipSuccess)
+        return hip_fail(e, "gate/up launch");
+    if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, 1, s); })) != hipSuccess)
+        return hip_fail(e, "down launch");
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,21 +329,36 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         return fail(MOE_ERR_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
     if (d.gate_fn != MOE_SOFTMAX_TOPK)
         return fail(MOE_ERR_STATE, "only MOE_SOFTMAX_TOPK is available");
-    if (d.n_slots != 0) return fail(MOE_ERR_STATE, "the expert slot cache is not available");
-    if (w->host_pool || w->slots)
+    if (d.n_slots < 0 || d.n_slots > (1 << 20)) return fail(MOE_ERR_SHAPE, "bad n_slots");
+    if (d.n_slots > 0 && d.n_slots < d.top_k)
+        return fail(MOE_ERR_SHAPE, "n_slots must be at least top_k");
+    if (d.n_slots == 0 && (w->host_pool || w->slots))
         return fail(MOE_ERR_ARG, "host_pool/slots must be NULL when n_slots = 0");
-    if (!w->router_q || !w->router_scale || !w->experts)
+    if (d.n_slots > 0 && (!w->host_pool || !w->slots))
+        return fail(MOE_ERR_ARG, "n_slots > 0 needs host_pool and slots");
+    if (!w->router_q || !w->router_scale || (!w->experts && d.n_slots == 0))
         return fail(MOE_ERR_ARG, "router_q, router_scale and experts are required");
+    if ((w->slots && !aligned(w->slots, 16)) || (w->host_pool && !aligned(w->host_pool, 16)))
+        return fail(MOE_ERR_ALIGN, "slots and host_pool need 16-byte alignment");
     if ((d.shared_inter > 0) != (w->shared != nullptr))
         return fail(MOE_ERR_ARG, "shared must be given exactly when shared_inter > 0");
-    if (!aligned(w->router_q, 16) || !aligned(w->experts, 16) ||
+    if (!aligned(w->router_q, 16) || (w->experts && !aligned(w->experts, 16)) ||
         (w->shared && !aligned(w->shared, 16)) || !aligned(w->router_scale, 2))
         return fail(MOE_ERR_ALIGN, "router_q, experts and shared need 16-byte alignment");
     moe_status st;
     if ((st = check_device_ptr(w->router_q, "router_q")) != MOE_OK) return st;
     if ((st = check_device_ptr(w->router_scale, "router_scale")) != MOE_OK) return st;
-    if ((st = check_device_ptr(w->experts, "experts")) != MOE_OK) return st;
+    if (w->experts && (st = check_device_ptr(w->experts, "experts")) != MOE_OK) return st;
     if (w->shared && (st = check_device_ptr(w->shared, "shared")) != MOE_OK) return st;
+    if (w->slots && (st = check_device_ptr(w->slots, "slots")) != MOE_OK) return st;
+    if (w->host_pool) {
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, w->host_pool) != hipSuccess ||
+            attr.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_NOT_PINNED, "host_pool must be page-locked host memory (hipHostMalloc)");
+        }
+    }
 
     moe_layer* L = new (std::nothrow) moe_layer();
     if (!L) return fail(MOE_ERR_NOMEM, "host allocation failed");
@@ -264,12 +382,36 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         delete L;
         return fail(MOE_ERR_SHAPE, "shape exceeds the kernels' per-wave register tiles");
     }
+    if (d.n_slots > 0) {
+        SlotCache& c = L->cache;
+        c.n_slots = d.n_slots;
+        c.slot_of.assign(d.n_experts, -1);
+        c.expert_in.assign(d.n_slots, -1);
+        c.count.assign(d.n_experts, 0);
+        c.last_use.assign(d.n_slots, 0);
+        hipError_t e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_ids, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_copies, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipHostMalloc((void**)&c.h_ids, sizeof(int32_t) * d.top_k, 0);
+        if (e == hipSuccess) e = hipHostMalloc((void**)&c.h_slots, sizeof(int32_t) * d.top_k, 0);
+        if (e != hipSuccess) {
+            moe_layer_destroy(L);
+            return hip_fail(e, "slot cache setup");
+        }
+    }
     *out = L;
     return MOE_OK;
 }
 
 moe_status moe_layer_destroy(moe_layer_t layer) {
     if (!layer) return fail(MOE_ERR_ARG, "null layer handle");
+    SlotCache& c = layer->cache;
+    if (c.side) (void)hipStreamSynchronize(c.side);
+    if (c.h_ids) (void)hipHostFree(c.h_ids);
+    if (c.h_slots) (void)hipHostFree(c.h_slots);
+    if (c.ev_ids) (void)hipEventDestroy(c.ev_ids);
+    if (c.ev_copies) (void)hipEventDestroy(c.ev_copies);
+    if (c.side) (void)hipStreamDestroy(c.side);
     delete layer;
     return MOE_OK;
 }
@@ -297,6 +439,7 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
                           void* workspace, float* expert_out, void* stream) {
     moe_status st = check_call(L, x, T, workspace);
     if (st != MOE_OK) return st;
+    if (L->cache.n_slots && T != 1) return fail(MOE_ERR_STATE, "the slot cache runs one token per call");
     if (!ids || !expert_out) return fail(MOE_ERR_ARG, "null ids or expert_out");
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
@@ -305,7 +448,9 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     hipError_t e = timed(K_PREP, s, [&] { return launch_prep(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "prep launch");
     FfnArgs fa = ffn_args(L, ids, nullptr, ws, o, nullptr, expert_out, false);
-    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (L->cache.n_slots) return cached_ffn(L, ids, fa, o, ws, s);
+    const int units = L->d.top_k * L->blk_r + L->blk_s;
+    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, units, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
     if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
@@ -325,6 +470,7 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
                              float* y, void* workspace, void* stream) {
     moe_status st = check_call(L, x, T, workspace);
     if (st != MOE_OK) return st;
+    if (L->cache.n_slots && T != 1) return fail(MOE_ERR_STATE, "the slot cache runs one token per call");
     if (!ids || !w || !y) return fail(MOE_ERR_ARG, "null ids, w or y");
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
@@ -332,8 +478,14 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     RouteArgs ra = route_args(L, x, ids, w, ws, o, 1);
     hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "router launch");
+    if (L->cache.n_slots) {
+        if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
+            return hip_fail(e, "top-k launch");
+        return cached_ffn(L, ids, ffn_args(L, ids, w, ws, o, y, nullptr, false), o, ws, s);
+    }
     FfnArgs fa = ffn_args(L, ids, w, ws, o, y, nullptr, true);
-    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
+    const int units = L->d.top_k * L->blk_r + L->blk_s;
+    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, units, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
     if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
@@ -352,6 +504,14 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
                                           y + (size_t)l * y_stride, workspace, stream);
         if (st != MOE_OK) return st;
     }
+    return MOE_OK;
+}
+
+moe_status moe_cache_stats(moe_layer_t L, uint64_t* hits, uint64_t* misses) {
+    if (!L || !hits || !misses) return fail(MOE_ERR_ARG, "null argument");
+    if (!L->cache.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    *hits = L->cache.hits;
+    *misses = L->cache.misses;
     return MOE_OK;
 }
 

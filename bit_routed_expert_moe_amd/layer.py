@@ -22,7 +22,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIG
 
 EXPORTS = ["moe_expert_record_bytes", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_stack_forward", "moe_poll_device_error",
+           "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_poll_device_error",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
            "moe_status_str", "moe_last_error"]
 KERNEL_NAMES = {0: "route", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine", 5: "topk"}
@@ -69,6 +69,7 @@ def lib() -> C.CDLL:
         L.moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
         L.moe_stack_forward.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, i64, vp, vp]
         L.moe_poll_device_error.argtypes = [vp, vp, vp]
+        L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = C.c_char_p
         L.moe_last_error.restype = C.c_char_p
@@ -77,7 +78,8 @@ def lib() -> C.CDLL:
         L.moe_profile_read.restype = i32
         for f in ["moe_layer_create", "moe_layer_destroy", "moe_route_topk", "moe_expert_ffn",
                   "moe_combine", "moe_layer_forward", "moe_stack_forward",
-                  "moe_poll_device_error", "moe_profile_start", "moe_profile_stop"]:
+                  "moe_poll_device_error", "moe_profile_start", "moe_profile_stop",
+                  "moe_cache_stats"]:
             getattr(L, f).restype = i32
         _LIB = L
     return _LIB
@@ -114,20 +116,33 @@ class Layer:
     experts       uint8 [E * record_bytes(H, inter)]
     shared        uint8 [record_bytes(H, shared_inter)] or None
     act           "bf16" or "f32" activations
+    n_slots       > 0: HBM slot cache of that many records, filled from
+    host_pool     pinned uint8 CPU tensor of all E records, into
+    slots         uint8 CUDA tensor [n_slots * record_bytes(H, inter)]
+                  (experts may then be None)
     """
 
     def __init__(self, hidden: int, n_experts: int, inter: int, top_k: int, shared_inter: int,
-                 router_q: torch.Tensor, router_scale: torch.Tensor, experts: torch.Tensor,
-                 shared: torch.Tensor | None, act: str = "bf16"):
+                 router_q: torch.Tensor, router_scale: torch.Tensor,
+                 experts: torch.Tensor | None, shared: torch.Tensor | None, act: str = "bf16",
+                 n_slots: int = 0, host_pool: torch.Tensor | None = None,
+                 slots: torch.Tensor | None = None):
         self.hidden, self.n_experts, self.inter = hidden, n_experts, inter
         self.top_k, self.shared_inter, self.act = top_k, shared_inter, act
-        self._keep = (router_q, router_scale, experts, shared)
+        self.n_slots = n_slots
+        self._keep = (router_q, router_scale, experts, shared, host_pool, slots)
         d = Desc(hidden, n_experts, inter, top_k, shared_inter, 64,
-                 MOE_BF16 if act == "bf16" else MOE_F32, MOE_SOFTMAX_TOPK, 0)
+                 MOE_BF16 if act == "bf16" else MOE_F32, MOE_SOFTMAX_TOPK, n_slots)
+        hp = None
+        if host_pool is not None:
+            if host_pool.is_cuda or not host_pool.is_pinned() or not host_pool.is_contiguous():
+                raise ValueError("host_pool must be a contiguous pinned CPU tensor")
+            hp = host_pool.data_ptr()
         w = Weights(_dev(router_q, "router_q", torch.int8),
                     _dev(router_scale, "router_scale"),
-                    _dev(experts, "experts", torch.uint8),
-                    None if shared is None else _dev(shared, "shared", torch.uint8), None, None)
+                    None if experts is None else _dev(experts, "experts", torch.uint8),
+                    None if shared is None else _dev(shared, "shared", torch.uint8), hp,
+                    None if slots is None else _dev(slots, "slots", torch.uint8))
         h = C.c_void_p()
         _check(lib().moe_layer_create(C.byref(d), C.byref(w), C.byref(h)))
         self.handle = h
@@ -191,6 +206,11 @@ class Layer:
                                        _dev(w, "w", torch.float32), _dev(y, "y", torch.float32),
                                        _dev(ws, "workspace"), _stream()))
         return ids, w, y
+
+    def cache_stats(self):
+        h, m = C.c_uint64(), C.c_uint64()
+        _check(lib().moe_cache_stats(self.handle, C.byref(h), C.byref(m)))
+        return int(h.value), int(m.value)
 
     def poll_error(self, ws: torch.Tensor):
         _check(lib().moe_poll_device_error(self.handle, _dev(ws, "workspace"), _stream()))

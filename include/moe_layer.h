@@ -88,7 +88,8 @@ typedef struct moe_layer_desc {
     int32_t group;         /* quantisation group; must be 64                      */
     int32_t act_dtype;     /* MOE_F32 or MOE_BF16 activations x                   */
     int32_t gate_fn;       /* MOE_SOFTMAX_TOPK (renormalised softmax over the top-k) */
-    int32_t n_slots;       /* 0 = every routed record resident in HBM             */
+    int32_t n_slots;       /* 0 = every routed record resident in HBM; otherwise the
+                              number of HBM expert slots of the slot cache (>= top_k) */
     int32_t reserved[7];
 } moe_layer_desc;
 
@@ -97,8 +98,10 @@ typedef struct moe_layer_weights {
     const uint16_t* router_scale; /* device, [E] fp16 bits                            */
     const uint8_t* experts;       /* device, E packed records back to back            */
     const uint8_t* shared;        /* device, one packed record of (H, shared_inter), or NULL */
-    const uint8_t* host_pool;     /* reserved for the slot cache; must be NULL when n_slots = 0 */
-    uint8_t* slots;               /* reserved for the slot cache; must be NULL when n_slots = 0 */
+    const uint8_t* host_pool;     /* n_slots > 0: page-locked host memory (hipHostMalloc)
+                                     holding all E records back to back; else NULL */
+    uint8_t* slots;               /* n_slots > 0: device, n_slots records; else NULL.
+                                     The library overwrites slots as experts enter. */
 } moe_layer_weights;
 
 typedef struct moe_layer* moe_layer_t;
@@ -157,6 +160,25 @@ moe_status moe_layer_forward(moe_layer_t layer, const void* x, int32_t n_tokens,
 moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const void* x,
                              int64_t x_stride, int32_t n_tokens, int32_t* ids, float* w,
                              float* y, int64_t y_stride, void* workspace, void* stream);
+
+/* HBM expert-slot cache (n_slots > 0), the out-of-core decode of the pages:
+ * TurboFieldfare article, "Proses pembuatan token" (the 8 ids are matched
+ * against a 16-slot LFU per layer, misses are read while the shared expert is
+ * computed, outputs combined after the reads); Inferno README, "Memory
+ * Strategy" (hit: execute from the slot; miss: read, place in a slot, execute).
+ * With a slot cache, moe_layer_forward and moe_expert_ffn take one token per
+ * call (else MOE_ERR_STATE) and synchronise the host on that token's expert
+ * ids.  Policy: each selection adds one to its expert's count (never
+ * decayed); a miss always enters, into the lowest free slot if any, else in
+ * place of the resident expert not selected by the current token with the
+ * smallest count, then the least recently used, then the lowest slot.
+ * Misses are copied with hipMemcpyAsync from host_pool on a side stream owned
+ * by the handle while the shared expert's gate/up runs; the routed kernels
+ * wait for the copies.  The handle owns the side stream, two events and two
+ * small page-locked staging buffers.  Results are bit-identical to the
+ * resident path for the same records.
+ * moe_cache_stats returns the hits and misses so far.  Errors: ARG, STATE. */
+moe_status moe_cache_stats(moe_layer_t layer, uint64_t* hits, uint64_t* misses);
 
 /* Reads and clears the device error flag kept in `workspace` (synchronises
  * `stream`).  MOE_OK if no kernel reported bad input since the last poll,

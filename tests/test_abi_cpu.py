@@ -59,7 +59,7 @@ FAKE = dict(router_q=0x10000, router_scale=0x20000, experts=0x30000, shared=0x40
     (dict(inter=96), -2), (dict(shared_inter=100), -2), (dict(n_experts=0), -2),
     (dict(n_experts=2048), -2), (dict(top_k=0), -2), (dict(top_k=33), -2),
     (dict(n_experts=4, top_k=5), -2), (dict(act_dtype=7), -1), (dict(gate_fn=1), -7),
-    (dict(n_slots=16), -7),
+    (dict(n_slots=4), -2), (dict(n_slots=16), -1), (dict(n_slots=-1), -2),
 ])
 def test_create_rejects_bad_descriptor(change, status):
     d = L.Desc(**{**GOOD, **change})
