@@ -78,6 +78,30 @@ struct FfnArgs {
     int gpw_dn;              // input groups per wave in the down kernel
 };
 
+constexpr int kTileRows = 16;         // rows (tokens) per MFMA tile in the prefill path
+constexpr int kPrefillMinTokens = 4;  // calls with at least this many tokens group by expert
+
+struct PrefillArgs {
+    const void* x;           // [T][H] activations
+    const int32_t* ids;      // [T][k]
+    const uint8_t* experts;
+    const uint8_t* shared;
+    size_t rec_bytes;
+    uint16_t* x16;           // [XP][T][H] fp16 parts of x * 2^e (per 64-group e), slot order
+    float* xsum;             // [T][H/64] sum of each group's inputs
+    float* xinv;             // [T][H/64] 2^-e
+    int32_t* pair_tok;       // [P] token of each expert-sorted (token, slot) pair
+    int32_t* pair_slot;      // [P] slot j of each sorted pair
+    int4* tiles;             // [tile_cap] {expert or -1 (shared), first row, rows, 0}
+    int32_t* n_tiles;        // [1]
+    uint16_t* h16;           // [P + T][Imax] fp16 h * 2^e (per 64-group e), slot order
+    float* hsum;             // [P + T][Imax/64]
+    float* hinv;             // [P + T][Imax/64]
+    float* eo;               // [T][k+1][H] per-slot expert outputs
+    uint32_t* err;           // device error word
+    int H, E, I, Is, k, T, P, Imax, tile_cap, xparts;
+};
+
 struct CombineArgs {
     const float* eo;  // [T][k+1][H]
     const float* w;   // [T][k]

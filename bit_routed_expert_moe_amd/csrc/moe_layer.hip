@@ -20,6 +20,8 @@ hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, int n_units, hipS
 hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
+hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s);
+hipError_t launch_prefill_ffn(const PrefillArgs& a, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -66,7 +68,8 @@ namespace {
 thread_local std::string g_last_error;
 
 // ---- per-launch event timing (moe_profile_*) ----
-enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4, K_TOPK = 5 };
+enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4, K_TOPK = 5,
+       K_PREFILL = 6 };
 struct ProfRec {
     int kid;
     hipEvent_t a, b;
@@ -101,7 +104,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
     size_t err, rctr, dctr, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
-        total;
+        x16, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, total;
+    int tile_cap;
 };
 
 WsLayout ws_layout(const moe_layer* L, int T) {
@@ -128,6 +132,23 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     o.hinv = take(nslot * 4);
     o.dpart = take((size_t)T * L->n_otiles * L->n_items * 64 * 4);
     o.slot_ids = take((size_t)T * k * 4);
+    if (T >= kPrefillMinTokens) {
+        const size_t P = (size_t)T * k;
+        const int Imax = std::max(L->d.inter, L->d.shared_inter);
+        o.tile_cap = (int)(std::min<size_t>((size_t)L->d.n_experts, P) + (P + kTileRows - 1) / kTileRows +
+                           (T + kTileRows - 1) / kTileRows);
+        o.x16 = take((size_t)L->xparts * T * H * 2);
+        o.pxsum = take((size_t)T * (H / 64) * 4);
+        o.pxinv = take((size_t)T * (H / 64) * 4);
+        o.pair_tok = take(P * 4);
+        o.pair_slot = take(P * 4);
+        o.tiles = take((size_t)o.tile_cap * 16);
+        o.n_tiles = take(4);
+        o.h16 = take((P + T) * Imax * 2);
+        o.phsum = take((P + T) * (Imax / 64) * 4);
+        o.phinv = take((P + T) * (Imax / 64) * 4);
+        o.eo = take((size_t)T * (k + 1) * H * 4);
+    }
     o.total = off;
     return o;
 }
@@ -211,6 +232,39 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.gi = L->gi;
     a.gis = L->gis;
     a.gpw_dn = L->gpw_dn;
+    return a;
+}
+
+PrefillArgs prefill_args(const moe_layer* L, const void* x, const int32_t* ids, uint8_t* ws,
+                         const WsLayout& o, int T, float* eo) {
+    PrefillArgs a{};
+    a.x = x;
+    a.ids = ids;
+    a.experts = L->w.experts;
+    a.shared = L->w.shared;
+    a.rec_bytes = L->rec_bytes;
+    a.x16 = (uint16_t*)(ws + o.x16);
+    a.xsum = (float*)(ws + o.pxsum);
+    a.xinv = (float*)(ws + o.pxinv);
+    a.pair_tok = (int32_t*)(ws + o.pair_tok);
+    a.pair_slot = (int32_t*)(ws + o.pair_slot);
+    a.tiles = (int4*)(ws + o.tiles);
+    a.n_tiles = (int32_t*)(ws + o.n_tiles);
+    a.h16 = (uint16_t*)(ws + o.h16);
+    a.hsum = (float*)(ws + o.phsum);
+    a.hinv = (float*)(ws + o.phinv);
+    a.eo = eo;
+    a.err = (uint32_t*)(ws + o.err);
+    a.H = L->d.hidden;
+    a.E = L->d.n_experts;
+    a.I = L->d.inter;
+    a.Is = L->d.shared_inter;
+    a.k = L->d.top_k;
+    a.T = T;
+    a.P = T * L->d.top_k;
+    a.Imax = std::max(L->d.inter, L->d.shared_inter);
+    a.tile_cap = o.tile_cap;
+    a.xparts = L->xparts;
     return a;
 }
 
@@ -444,6 +498,14 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
+    if (T >= kPrefillMinTokens) {
+        PrefillArgs pa = prefill_args(L, x, ids, ws, o, T, expert_out);
+        hipError_t e = timed(K_PREFILL, s, [&] {
+            hipError_t r = launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s);
+            return r != hipSuccess ? r : launch_prefill_ffn(pa, s);
+        });
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "prefill launch");
+    }
     RouteArgs ra = route_args(L, x, nullptr, nullptr, ws, o, 1);
     hipError_t e = timed(K_PREP, s, [&] { return launch_prep(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "prep launch");
@@ -475,9 +537,23 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
-    RouteArgs ra = route_args(L, x, ids, w, ws, o, 1);
+    RouteArgs ra = route_args(L, x, ids, w, ws, o, T >= kPrefillMinTokens ? 0 : 1);
     hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "router launch");
+    if (T >= kPrefillMinTokens) {
+        if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
+            return hip_fail(e, "top-k launch");
+        PrefillArgs pa = prefill_args(L, x, ids, ws, o, T, (float*)(ws + o.eo));
+        if ((e = timed(K_PREFILL, s, [&] {
+                 hipError_t r = launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s);
+                 return r != hipSuccess ? r : launch_prefill_ffn(pa, s);
+             })) != hipSuccess)
+            return hip_fail(e, "prefill launch");
+        CombineArgs ca{(const float*)(ws + o.eo), w, y, L->d.hidden, L->d.top_k, T, 0};
+        if ((e = timed(K_COMBINE, s, [&] { return launch_combine(ca, s); })) != hipSuccess)
+            return hip_fail(e, "combine launch");
+        return MOE_OK;
+    }
     if (L->cache.n_slots) {
         if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
             return hip_fail(e, "top-k launch");

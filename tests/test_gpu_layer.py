@@ -60,10 +60,17 @@ def test_tiny_layer_many_tokens(orc):
     xq = np.stack([t[0] for t in toks]); xd = [t[1] for t in toks]
     ids, w, y = dl.layer_obj.forward(to_dev(xq, wl.act))
     check_tokens(dl, orc, xq, xd, ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy(), "tiny T=192")
-    for t in range(8):
-        i1, w1, y1 = dl.layer_obj.forward(to_dev(xq[t:t + 1], wl.act))
-        assert torch.equal(i1.cpu()[0], ids.cpu()[t])
-        assert torch.equal(y1.cpu()[0], y.cpu()[t]), "a token's result depends on the batch"
+    # batches of 4 or more tokens take the grouped path, smaller ones the decode
+    # path: within a path a token's result does not depend on its batch
+    i8, w8, y8 = dl.layer_obj.forward(to_dev(xq[100:108], wl.act))
+    assert torch.equal(i8, ids[100:108]) and torch.equal(y8, y[100:108]), \
+        "a token's result depends on the batch"
+    i2, _, y2 = dl.layer_obj.forward(to_dev(xq[:2], wl.act))
+    for t in range(2):
+        i1, _, y1 = dl.layer_obj.forward(to_dev(xq[t:t + 1], wl.act))
+        assert torch.equal(i1[0], i2[t]) and torch.equal(y1[0], y2[t])
+    check_tokens(dl, orc, xq[:2], xd[:2], i2.cpu().numpy(), w[:2].cpu().numpy(),
+                 y2.cpu().numpy(), "tiny T=2 (decode path)")
 
 
 def test_api_calls_match_fused_forward_bitwise(orc):

@@ -70,3 +70,35 @@ def test_glm_layer_zipf_full_size(orc):
         worst = max(worst, rel_err(y[t], ry))
     print(f"glm zipf layer: {len(xs_d)} tokens, max rel y err {worst:.2e}")
     assert worst <= Y_TOL
+
+
+def test_glm_prefill_chunk_full_size(orc):
+    """GLM-scale 128-token chunk through the grouped path: every token's ids and
+    gate weights against the oracle router, outputs on 4 sampled tokens (the
+    oracle regenerates each selected record on the CPU, about a second each),
+    and the whole chunk's result permuted exactly with its tokens."""
+    wl = synth.WORKLOADS["glm_prefill_h6144_e256_t128"]
+    dl = DeviceLayer(wl.seed, 0, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
+    toks = [dl.natural_token(orc, s) for s in range(wl.n_tokens)]
+    xq = np.stack([t[0] for t in toks])
+    ws = dl.layer_obj.workspace(wl.n_tokens)
+    ids, w, y = dl.layer_obj.forward(to_dev(xq, wl.act), ws)
+    ids_h, w_h, y_h = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+    worst_w = 0.0
+    for t, (_, xd) in enumerate(toks):
+        rid, rw, _ = orc.route(dl.rq, dl.rs, xd, wl.top_k)
+        assert ids_h[t].tolist() == rid.tolist(), f"token {t}"
+        worst_w = max(worst_w, float(np.max(np.abs(w_h[t] - rw))))
+    assert worst_w <= W_TOL
+    worst_y = 0.0
+    for t in (0, 41, 86, 127):
+        _, _, ry, _, _ = dl.oracle(orc, toks[t][1])
+        worst_y = max(worst_y, rel_err(y_h[t], ry))
+        print(f"glm prefill token {t}: rel y err {rel_err(y_h[t], ry):.2e}", flush=True)
+    print(f"glm prefill chunk: {wl.n_tokens} tokens, max |w err| {worst_w:.2e}, "
+          f"max rel y err (sampled) {worst_y:.2e}")
+    assert worst_y <= Y_TOL
+    perm = np.random.default_rng(2).permutation(wl.n_tokens)
+    ids2, w2, y2 = dl.layer_obj.forward(to_dev(xq[perm], wl.act), ws)
+    p = torch.from_numpy(perm).cuda()
+    assert torch.equal(ids[p], ids2) and torch.equal(w[p], w2) and torch.equal(y[p], y2)
