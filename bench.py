@@ -69,7 +69,7 @@ def down_bytes(H, I):
 def make_inputs(wl, layer, S):
     """[S][T][H] activations for one layer (float64) from the seeded generator."""
     import synth
-    if wl.routing == "zipf":
+    if wl.routing in ("zipf", "uniform"):
         q, rs = synth.router(wl.seed, layer, wl.n_experts, wl.hidden)
         W = q.astype(np.float64) * rs.view(np.float16).astype(np.float64)[:, None]
         zr = synth.ZipfRealiser(W, wl.zipf_s, wl.seed, layer)
@@ -213,6 +213,194 @@ def run_cached(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def run_prefill(args, wl):
+    """Prefill chunks: a step is one chunk of wl.n_tokens tokens through one layer
+    (router, top-k, grouping by expert, grouped gate/up and down, combine).
+    Steps cycle over --prefill-layers layers of distinct weights, so a layer's
+    records are not served from a cache between its steps."""
+    import torch
+    import synth
+    import synth.gpu
+    from bit_routed_expert_moe_amd import KernelTimer, Layer, record_bytes
+
+    H, E, I, k, Is, T = wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.n_tokens
+    NL, C = args.prefill_layers, args.prefill_chunks
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    rb, rbs = record_bytes(H, I), (record_bytes(H, Is) if Is else 0)
+    t_setup = time.time()
+    layers, pools = [], []
+    for l in range(NL):
+        rq, rs = synth.router(wl.seed, l, E, H)
+        pool = torch.empty(E * rb, dtype=torch.uint8, device=dev)
+        synth.gpu.fill_records(pool, H, I, wl.seed, l, 0, E)
+        shared = None
+        if Is:
+            shared = torch.empty(rbs, dtype=torch.uint8, device=dev)
+            synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
+        pools.append((pool, shared, rq, rs))
+        layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
+                            torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act))
+    S = NL * C  # distinct (layer, chunk) steps
+    xs_host = np.empty((S, T, H))
+    for l in range(NL):
+        if wl.routing in ("zipf", "uniform"):
+            rq, rs = pools[l][2], pools[l][3]
+            W = rq.astype(np.float64) * rs.view(np.float16).astype(np.float64)[:, None]
+            zr = synth.ZipfRealiser(W, wl.zipf_s, wl.seed, l)
+            for c in range(C):
+                xs_host[c * NL + l] = np.concatenate([zr.activations(c * T + t) for t in range(T)])
+        else:
+            for c in range(C):
+                xs_host[c * NL + l] = synth.activations(wl.seed, l, c, H, T)
+    xs_q = synth.quantize_act(xs_host, wl.act)
+    xs = (torch.from_numpy(xs_q.view(np.int16)).to(dev).view(torch.bfloat16) if wl.act == "bf16"
+          else torch.from_numpy(xs_q).to(dev))
+    ws = layers[0].workspace(T)
+    ids = torch.empty(S, T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(S, T, k, dtype=torch.float32, device=dev)
+    y = torch.empty(S, T, H, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f} s: {NL} layers x {E} experts of {rb} B, "
+        f"{S} distinct chunks of {T} tokens")
+
+    def run_step(s):
+        j = s % S
+        layers[j % NL].forward(xs[j], ws, out=(ids[j], w[j], y[j]))
+
+    for s in range(S):
+        run_step(s)
+    torch.cuda.synchronize()
+    K, W = args.steps, args.warmup
+    G = 1 if args.no_graph else math.gcd(args.graph_chunk, math.gcd(K, S))
+    units = []
+    if args.no_graph:
+        units = [(lambda s=s: run_step(s)) for s in range(S)]
+    else:
+        for c0 in range(0, S, G):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(c0, c0 + G):
+                    run_step(s)
+            units.append(g.replay)
+    n_units = len(units)
+    for i in range((W + G - 1) // G):
+        units[i % n_units]()
+    torch.cuda.synchronize()
+    start = (W + G - 1) // G
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(K // G):
+        units[(start + i) % n_units]()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / K
+    log(f"timed {K} steps in {ms_per_step * K:.2f} ms (wall {wall * 1e3:.2f} ms), graphs of {G} steps")
+
+    # bytes and MFMA work of each distinct step, from the selections it made
+    ids_h = ids.cpu().numpy()
+    uniq = np.array([len(np.unique(ids_h[j])) for j in range(S)])
+    tiles = np.array([int(sum((c + 15) // 16 for c in np.bincount(ids_h[j].ravel(), minlength=E) if c))
+                      for j in range(S)])
+    steps_j = [(start * G + i) % S for i in range(K)]  # distinct step of each timed step
+    router_b, act_b = E * H + 2 * E, T * H * (2 if wl.act == "bf16" else 4) + T * H * 4
+    step_bytes = uniq * rb + rbs + router_b + act_b
+    mean_bytes = float(np.mean(step_bytes[steps_j]))
+    gbps = mean_bytes / (ms_per_step * 1e-3) / 1e9
+    useful_flops = 2.0 * T * 3 * H * (k * I + Is)
+    shared_tiles = (T + 15) // 16 if Is else 0
+    exec_flops = 2.0 * 16 * 3 * H * (tiles * I + shared_tiles * Is)
+    mfma_peak = 2.5e15  # dense fp16 MFMA, MI355X
+    mean_exec = float(np.mean(exec_flops[steps_j]))
+
+    # live per-kernel hipEvent pass, launched eagerly over the S distinct steps
+    with KernelTimer(capacity=S * 8 + 64) as kt:
+        for s in range(S):
+            run_step(s)
+    recs = kt.read()
+    torch.cuda.synchronize()
+    empty = []
+    for _ in range(64):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        torch.cuda._sleep(0)
+        b_.record()
+        b_.synchronize()
+        empty.append(a_.elapsed_time(b_))
+    ev_overhead_ms = float(np.median(empty))
+    per_step_bytes = {"grouped_gate_up": uniq * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0),
+                      "grouped_down": uniq * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0)}
+    kernels = {}
+    for name in sorted({r[0] for r in recs}):
+        ms = np.array([m for n_, m in recs if n_ == name])
+        net = np.maximum(ms - ev_overhead_ms, 1e-6)
+        ent = {"launches": int(ms.size), "avg_us": round(float(net.mean()) * 1e3, 3),
+               "avg_us_raw": round(float(ms.mean()) * 1e3, 3)}
+        if name in per_step_bytes and ms.size == S:
+            b = per_step_bytes[name]
+            ent["alg_bytes_mean"] = int(b.mean())
+            ent["gbps"] = round(float(b.sum()) / (float(net.sum()) * 1e-3) / 1e9, 1)
+        kernels[name] = ent
+    gu = kernels["grouped_gate_up"]
+    gu_flops = float(np.mean(2.0 * 16 * 2 * H * (tiles * I + shared_tiles * Is)))
+    roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "k_gu_grouped", "alg_bytes_per_launch": gu["alg_bytes_mean"],
+                "avg_launch_us": gu["avg_us"], "event_pair_overhead_us": round(ev_overhead_ms * 1e3, 3),
+                "mfma_util": round(gu_flops / (gu["avg_us"] * 1e-6) / mfma_peak, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = prefill_cpu_baseline(wl, pools[0], xs_q[0], args.cpu_seconds)
+
+    out = {
+        "metric": "prefill tokens/s per MoE layer + achieved HBM GB/s vs peak (128-token chunk, top-8)",
+        "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tok/s per layer",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u4 weights x f16 activations -> f32 (MFMA)", "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
+                   "shared_inter": Is, "chunk_tokens": T, "act": wl.act, "routing": wl.routing,
+                   "weight_sets": NL, "distinct_chunks": S, "graph_chunk": G},
+        "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
+        "alg_bytes_per_chunk": int(mean_bytes), "unique_experts_mean": round(float(uniq.mean()), 2),
+        "mfma_util_useful": round(useful_flops / (ms_per_step * 1e-3) / mfma_peak, 5),
+        "mfma_util_executed": round(mean_exec / (ms_per_step * 1e-3) / mfma_peak, 5),
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def prefill_cpu_baseline(wl, pool, x_chunk, seconds):
+    """The CPU oracle, token by token, on the first chunk of layer 0 (records read
+    from that layer's generated pool), until about `seconds` of oracle compute."""
+    import oracle
+    orc = oracle.default()
+    threads = orc.set_threads(len(os.sched_getaffinity(0)))
+    dpool, dshared, rq, rs = pool
+    H, I, Is, k = wl.hidden, wl.inter, wl.shared_inter, wl.top_k
+    host = dpool.cpu().numpy()
+    shared = dshared.cpu().numpy() if dshared is not None else None
+    rb = host.size // wl.n_experts
+    spent, n = 0.0, 0
+    for t in range(x_chunk.shape[0]):
+        xd = orc.act_to_f64(wl.act, x_chunk[t])
+        t0 = time.perf_counter()
+        ids, w, _ = orc.route(rq, rs, xd, k)
+        yr = np.stack([orc.expert_ffn(H, I, host[int(e) * rb:(int(e) + 1) * rb], xd) for e in ids])
+        ys = orc.expert_ffn(H, Is, shared, xd) if Is else None
+        orc.combine(w, yr, ys)
+        spent += time.perf_counter() - t0
+        n += 1
+        if spent >= seconds:
+            break
+    return {"value": round(n / spent, 3), "unit": "tok/s per layer", "cores": threads, "kind": "oracle",
+            "sample": f"{n} tokens of the first chunk (layer 0), one by one; fp64 plain-loop oracle, "
+                      f"OpenMP over rows; {spent:.1f} s of oracle compute"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +412,10 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-layers", type=int, default=8,
+                    help="prefill workloads: layers of distinct weights cycled over")
+    ap.add_argument("--prefill-chunks", type=int, default=4,
+                    help="prefill workloads: distinct input chunks per layer")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -253,8 +445,7 @@ def main():
     if wl.n_slots:
         return run_cached(args, wl)
     if wl.n_tokens != 1:
-        print(f"workload {wl.name} is not a decode stack", file=sys.stderr)
-        sys.exit(2)
+        return run_prefill(args, wl)
     H, E, I, k, Is, L, T = (wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter,
                             wl.n_layers, wl.n_tokens)
     torch.cuda.set_device(0)

@@ -12,6 +12,9 @@ SOURCES = ["moe_kernels.hip", "moe_prefill.hip", "moe_layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results straight into VGPRs (no AGPR round trip before the
+         # fp32 group epilogue of the grouped kernels)
+         "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function"]
 
 

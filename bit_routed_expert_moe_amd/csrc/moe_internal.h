@@ -87,9 +87,10 @@ struct PrefillArgs {
     const uint8_t* experts;
     const uint8_t* shared;
     size_t rec_bytes;
-    uint16_t* x16;           // [XP][T][H] fp16 parts of x * 2^e (per 64-group e), slot order
-    float* xsum;             // [T][H/64] sum of each group's inputs
-    float* xinv;             // [T][H/64] 2^-e
+    size_t rec_bytes_shared;
+    uint16_t* x16;           // [XP][T][H] fp16 parts of x * 2^e (one e per token), slot order
+    float* xsum;             // [T][H/64] sum of each group of x * 2^e
+    float* xinv;             // [T] 2^-e
     int32_t* pair_tok;       // [P] token of each expert-sorted (token, slot) pair
     int32_t* pair_slot;      // [P] slot j of each sorted pair
     int4* tiles;             // [tile_cap] {expert or -1 (shared), first row, rows, 0}

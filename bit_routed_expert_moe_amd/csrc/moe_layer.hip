@@ -21,7 +21,9 @@ hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
 hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s);
-hipError_t launch_prefill_ffn(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -69,7 +71,7 @@ thread_local std::string g_last_error;
 
 // ---- per-launch event timing (moe_profile_*) ----
 enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4, K_TOPK = 5,
-       K_PREFILL = 6 };
+       K_PF_PREP = 6, K_PF_GROUP = 7, K_PF_GATE_UP = 8, K_PF_DOWN = 9 };
 struct ProfRec {
     int kid;
     hipEvent_t a, b;
@@ -108,6 +110,17 @@ struct WsLayout {
     int tile_cap;
 };
 
+// Tokens per pass of the grouped path: bounded so that every byte offset into
+// the fp16 activation and h buffers fits the kernels' 32-bit buffer offsets.
+int grouped_chunk(const moe_layer* L) {
+    const int64_t lim = (int64_t)0x7FFFFFFF;
+    const int64_t Imax = std::max(L->d.inter, L->d.shared_inter);
+    int64_t c = 8192;
+    c = std::min(c, lim / ((int64_t)(L->d.top_k + 1) * Imax * 2));
+    c = std::min(c, lim / ((int64_t)L->xparts * L->d.hidden * 2));
+    return (int)std::max<int64_t>(c, kPrefillMinTokens);
+}
+
 WsLayout ws_layout(const moe_layer* L, int T) {
     WsLayout o{};
     const int H = L->d.hidden, k = L->d.top_k;
@@ -119,35 +132,37 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     };
     o.err = take(4);
     o.rctr = take((size_t)T * 4);
-    o.dctr = take((size_t)T * L->n_otiles * kCounterStride * 4);
-    o.xpairs = take((size_t)T * (H / 2) * L->xparts * 4);
-    o.xK = take((size_t)T * L->NG * 4);
-    o.xX = take((size_t)T * L->NG * 4);
-    o.xinv = take((size_t)T * L->NG * 4);
     o.logits = take((size_t)T * L->d.n_experts * 4);
-    const size_t nslot = (size_t)T * (k + 1) * L->blk_max;
-    o.hpairs = take(nslot * 16 * kHParts * 4);
-    o.hK = take(nslot * 4);
-    o.hHs = take(nslot * 4);
-    o.hinv = take(nslot * 4);
-    o.dpart = take((size_t)T * L->n_otiles * L->n_items * 64 * 4);
     o.slot_ids = take((size_t)T * k * 4);
-    if (T >= kPrefillMinTokens) {
-        const size_t P = (size_t)T * k;
+    if (T < kPrefillMinTokens) {  // per-token (decode) path
+        o.dctr = take((size_t)T * L->n_otiles * kCounterStride * 4);
+        o.xpairs = take((size_t)T * (H / 2) * L->xparts * 4);
+        o.xK = take((size_t)T * L->NG * 4);
+        o.xX = take((size_t)T * L->NG * 4);
+        o.xinv = take((size_t)T * L->NG * 4);
+        const size_t nslot = (size_t)T * (k + 1) * L->blk_max;
+        o.hpairs = take(nslot * 16 * kHParts * 4);
+        o.hK = take(nslot * 4);
+        o.hHs = take(nslot * 4);
+        o.hinv = take(nslot * 4);
+        o.dpart = take((size_t)T * L->n_otiles * L->n_items * 64 * 4);
+    } else {  // grouped path, one chunk of at most grouped_chunk(L) tokens at a time
+        const size_t Tg = (size_t)std::min(T, grouped_chunk(L));
+        const size_t P = Tg * k;
         const int Imax = std::max(L->d.inter, L->d.shared_inter);
         o.tile_cap = (int)(std::min<size_t>((size_t)L->d.n_experts, P) + (P + kTileRows - 1) / kTileRows +
-                           (T + kTileRows - 1) / kTileRows);
-        o.x16 = take((size_t)L->xparts * T * H * 2);
-        o.pxsum = take((size_t)T * (H / 64) * 4);
-        o.pxinv = take((size_t)T * (H / 64) * 4);
+                           (Tg + kTileRows - 1) / kTileRows);
+        o.x16 = take((size_t)L->xparts * Tg * H * 2);
+        o.pxsum = take(Tg * (H / 64) * 4);
+        o.pxinv = take(Tg * 4);
         o.pair_tok = take(P * 4);
         o.pair_slot = take(P * 4);
         o.tiles = take((size_t)o.tile_cap * 16);
         o.n_tiles = take(4);
-        o.h16 = take((P + T) * Imax * 2);
-        o.phsum = take((P + T) * (Imax / 64) * 4);
-        o.phinv = take((P + T) * (Imax / 64) * 4);
-        o.eo = take((size_t)T * (k + 1) * H * 4);
+        o.h16 = take((P + Tg) * Imax * 2);
+        o.phsum = take((P + Tg) * (Imax / 64) * 4);
+        o.phinv = take((P + Tg) * (Imax / 64) * 4);
+        o.eo = take(Tg * (k + 1) * H * 4);
     }
     o.total = off;
     return o;
@@ -243,6 +258,7 @@ PrefillArgs prefill_args(const moe_layer* L, const void* x, const int32_t* ids, 
     a.experts = L->w.experts;
     a.shared = L->w.shared;
     a.rec_bytes = L->rec_bytes;
+    a.rec_bytes_shared = L->shared_rec_bytes;
     a.x16 = (uint16_t*)(ws + o.x16);
     a.xsum = (float*)(ws + o.pxsum);
     a.xinv = (float*)(ws + o.pxinv);
@@ -266,6 +282,42 @@ PrefillArgs prefill_args(const moe_layer* L, const void* x, const int32_t* ids, 
     a.tile_cap = o.tile_cap;
     a.xparts = L->xparts;
     return a;
+}
+
+moe_status grouped_ffn_chunk(const moe_layer* L, const PrefillArgs& pa, hipStream_t s) {
+    hipError_t e;
+    if ((e = timed(K_PF_PREP, s, [&] { return launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s); })) != hipSuccess)
+        return hip_fail(e, "prefill prep launch");
+    if ((e = timed(K_PF_GROUP, s, [&] { return launch_prefill_group(pa, s); })) != hipSuccess)
+        return hip_fail(e, "grouping launch");
+    if ((e = timed(K_PF_GATE_UP, s, [&] { return launch_prefill_gate_up(pa, s); })) != hipSuccess)
+        return hip_fail(e, "grouped gate/up launch");
+    if ((e = timed(K_PF_DOWN, s, [&] { return launch_prefill_down(pa, s); })) != hipSuccess)
+        return hip_fail(e, "grouped down launch");
+    return MOE_OK;
+}
+
+// The grouped path over T tokens in chunks.  expert_out given: per-slot outputs
+// written there; else each chunk's outputs go to the workspace and are combined
+// into y with w.
+moe_status grouped_ffn(const moe_layer* L, const void* x, int T, const int32_t* ids, const float* w,
+                       float* y, float* expert_out, uint8_t* ws, const WsLayout& o, hipStream_t s) {
+    const int H = L->d.hidden, k = L->d.top_k, C = grouped_chunk(L);
+    const size_t esz = L->d.act_dtype == MOE_BF16 ? 2 : 4;
+    for (int c0 = 0; c0 < T; c0 += C) {
+        const int Tc = std::min(C, T - c0);
+        const void* xc = (const uint8_t*)x + (size_t)c0 * H * esz;
+        const int32_t* ic = ids + (size_t)c0 * k;
+        float* eo = expert_out ? expert_out + (size_t)c0 * (k + 1) * H : (float*)(ws + o.eo);
+        moe_status st = grouped_ffn_chunk(L, prefill_args(L, xc, ic, ws, o, Tc, eo), s);
+        if (st != MOE_OK) return st;
+        if (!expert_out) {
+            CombineArgs ca{eo, w + (size_t)c0 * k, y + (size_t)c0 * H, H, k, Tc, 0};
+            hipError_t e = timed(K_COMBINE, s, [&] { return launch_combine(ca, s); });
+            if (e != hipSuccess) return hip_fail(e, "combine launch");
+        }
+    }
+    return MOE_OK;
 }
 
 moe_status check_call(const moe_layer* L, const void* x, int32_t T, const void* ws) {
@@ -499,12 +551,7 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
     if (T >= kPrefillMinTokens) {
-        PrefillArgs pa = prefill_args(L, x, ids, ws, o, T, expert_out);
-        hipError_t e = timed(K_PREFILL, s, [&] {
-            hipError_t r = launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s);
-            return r != hipSuccess ? r : launch_prefill_ffn(pa, s);
-        });
-        return e == hipSuccess ? MOE_OK : hip_fail(e, "prefill launch");
+        return grouped_ffn(L, x, T, ids, nullptr, nullptr, expert_out, ws, o, s);
     }
     RouteArgs ra = route_args(L, x, nullptr, nullptr, ws, o, 1);
     hipError_t e = timed(K_PREP, s, [&] { return launch_prep(ra, T, L->d.act_dtype == MOE_BF16, s); });
@@ -543,16 +590,7 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     if (T >= kPrefillMinTokens) {
         if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
             return hip_fail(e, "top-k launch");
-        PrefillArgs pa = prefill_args(L, x, ids, ws, o, T, (float*)(ws + o.eo));
-        if ((e = timed(K_PREFILL, s, [&] {
-                 hipError_t r = launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s);
-                 return r != hipSuccess ? r : launch_prefill_ffn(pa, s);
-             })) != hipSuccess)
-            return hip_fail(e, "prefill launch");
-        CombineArgs ca{(const float*)(ws + o.eo), w, y, L->d.hidden, L->d.top_k, T, 0};
-        if ((e = timed(K_COMBINE, s, [&] { return launch_combine(ca, s); })) != hipSuccess)
-            return hip_fail(e, "combine launch");
-        return MOE_OK;
+        return grouped_ffn(L, x, T, ids, w, y, nullptr, ws, o, s);
     }
     if (L->cache.n_slots) {
         if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)

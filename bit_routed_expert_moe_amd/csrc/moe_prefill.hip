@@ -1,19 +1,20 @@
 // moe_prefill.hip -- multi-token (prefill) path: experts grouped by selection
 // and run as MFMA grouped dequant GEMMs, so that each selected expert's
-// weights are streamed once per chunk and applied to every token routed to it.
+// weights are streamed once per call and applied to every token routed to it.
 //
-//   k_prep_tokens   per (token, 64-input group): fp16 parts of x * 2^e, with
-//                   e chosen so the group's largest value is below 2^14; the
-//                   group's input sum and 2^-e.
+//   k_prep_tokens   per token: fp16 parts of x * 2^e, with one e per token
+//                   chosen so that its largest value is below 2^14; the exact
+//                   sum of each 64-input group of x * 2^e.
 //   k_group         one workgroup: (token, slot) pairs sorted by expert
 //                   (stable), and a tile list of at most 16 rows per tile;
 //                   the shared expert adds tiles of 16 consecutive tokens.
-//   k_gu_grouped    per (tile, 64 rows of I): each wave computes gate and up
-//                   for 16 rows of I over all of H with v_mfma_f32_16x16x32_f16;
-//                   h = silu(gate) * up, stored as fp16 with a per-(row,
+//   k_gu_grouped    per (tile, 128 rows of I): wave = one 64-row group of I
+//                   (gate and up: 8 MFMA N-tiles of 16) over one half of H;
+//                   the two halves are added in a fixed order, then
+//                   h = silu(gate) * up is stored as fp16 with a per-(row,
 //                   64-group) power-of-two scale, plus the group's sum of h.
-//   k_down_grouped  per (tile, 64 outputs): each wave computes 16 outputs over
-//                   all of I; writes each row's expert output (unweighted).
+//   k_down_grouped  per (tile, 256 outputs): wave = 64 outputs over all of I;
+//                   writes each row's expert output (unweighted).
 // The combine is the decode path's k_combine (fixed order, shared last).
 //
 // Numerics follow the affine group quantisation directly: the MFMA operand B
@@ -29,6 +30,11 @@
 // scaled by 16; activations are stored in that order ("slot order") with odd
 // inputs divided by 16, which is exact in fp16.
 //
+// Streams: weights, scale/bias pairs and activations are read with buffer
+// loads whose per-lane offsets are loop invariant (the loop advances a scalar
+// offset), weights with the nontemporal hint.  A workgroup's waves read the
+// same activation rows, which stay in the CU's L1.
+//
 // MFMA 16x16x32 f16 operand layout (lane l): A[l%16][8*(l/16)+i],
 // B[8*(l/16)+i][l%16], D[4*(l/16)+r][l%16].
 #include "moe_device.h"
@@ -40,33 +46,81 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-constexpr int kPfDepth = 4;  // 64-input groups in flight per wave
+constexpr int kNtGu = 8;  // MFMA N-tiles per wave in k_gu_grouped (64 rows of I, gate + up)
+constexpr int kNtDn = 4;  // MFMA N-tiles per wave in k_down_grouped (64 outputs)
+constexpr int kAuxNT = 2; // buffer-load cache policy: nontemporal
+constexpr int kGuDepth = 2;  // 64-input groups in flight per wave, k_gu_grouped
+constexpr int kDnDepth = 4;  // 64-input groups in flight per wave, k_down_grouped
 
 // slot of input p (0..7) within its 8: inverse of (0,4,1,5,2,6,3,7)
 __device__ __forceinline__ int slot_of(int p) { return p < 4 ? 2 * p : 2 * (p - 4) + 1; }
 
-// 8 nibbles of one dword -> the 8 exact codes as fp16, in slot order, odd
-// inputs times 16.
-__device__ __forceinline__ half8 codes8(uint32_t w) {
-    const uint32_t M = 0x64006400u;
-    const uint32_t w8 = w >> 8;
-    const half2v off = {(_Float16)1024.0f, (_Float16)1024.0f};
-    const half2v p0 = __builtin_bit_cast(half2v, (w & 0x000F000Fu) | M) - off;   // q0, q4
-    const half2v p1 = __builtin_bit_cast(half2v, (w & 0x00F000F0u) | M) - off;   // 16q1, 16q5
-    const half2v p2 = __builtin_bit_cast(half2v, (w8 & 0x000F000Fu) | M) - off;  // q2, q6
-    const half2v p3 = __builtin_bit_cast(half2v, (w8 & 0x00F000F0u) | M) - off;  // 16q3, 16q7
-    half8 o;
-    o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
-    o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
-    return o;
+// Unpack constants kept in VGPRs so that each nibble pair costs one
+// v_and_or_b32 (a VOP3 cannot take two literal constants).
+struct Unpack {
+    uint32_t lo, hi, magic;
+    __device__ __forceinline__ Unpack() {
+        asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(lo));
+        asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(hi));
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+    }
+    // 8 nibbles of one dword -> the exact codes as fp16, in slot order, odd
+    // inputs times 16
+    __device__ __forceinline__ half8 codes(uint32_t w) const {
+        const uint32_t w8 = w >> 8;
+        const half2v off = {(_Float16)1024.0f, (_Float16)1024.0f};
+        const half2v p0 = __builtin_bit_cast(half2v, (w & lo) | magic) - off;   // q0, q4
+        const half2v p1 = __builtin_bit_cast(half2v, (w & hi) | magic) - off;   // 16q1, 16q5
+        const half2v p2 = __builtin_bit_cast(half2v, (w8 & lo) | magic) - off;  // q2, q6
+        const half2v p3 = __builtin_bit_cast(half2v, (w8 & hi) | magic) - off;  // 16q3, 16q7
+        half8 o;
+        o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+        o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+        return o;
+    }
+};
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, half8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma(u32x4 a, uint32_t w, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), codes8(w), c, 0, 0, 0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)min(bytes, (size_t)0x7FFFFFFF),
+                                             0x00020000);
+}
+template <int AUX = 0>
+__device__ __forceinline__ uint32_t bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
 }
 
-// max / sum over the 16 lanes of a DPP row; lane 0 of each row gets a value
-// whose summation order is fixed.
+// Lane-group moves on the wave's four 16-lane row groups (gfx950
+// v_permlane16_swap / v_permlane32_swap; all 64 lanes must be active).
+// xpose4: row group g, register j holds M[g][j] -> row group g, register t
+// holds M[t][g].  A wave's 16-byte load of rows 16g + n (lane n of group g)
+// becomes, in lane n of group g, dword g of rows n, 16 + n, 32 + n, 48 + n:
+// the MFMA B operand of four N-tiles.
+__device__ __forceinline__ u32x4 xpose4(u32x4 d) {
+    const auto s01 = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
+    const auto s02 = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(s01[1], s23[1], false, false);
+    return u32x4{s02[0], s13[0], s02[1], s13[1]};
+}
+// bcast4: register t of every row group <- v of row group t (same lane n).
+__device__ __forceinline__ u32x4 bcast4(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+    return u32x4{b[0], c[0], b[1], c[1]};
+}
+
+// max / sum over the 16 lanes of a DPP row.  Every lane of the row gets the
+// max; the sum's rounding order differs between lanes, so only one lane's
+// sum is used.
 __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp<0xB1>(v));
     v = fmaxf(v, dpp<0x4E>(v));
@@ -81,30 +135,37 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// k_prep_tokens: grid (ceil(H/256), T), 256 threads; wave = one 64-input group.
+// k_prep_tokens: grid (T), 256 threads.
 // ---------------------------------------------------------------------------
 template <int XP, bool BF16>
 __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
-    const int t = blockIdx.y, H = a.H, NG = H / 64;
-    const int g = blockIdx.x * kWaves + wave_id(), lane = threadIdx.x & 63;
-    if (g >= NG) return;
-    const size_t gi = (size_t)t * H + 64 * g + lane;
-    const float v = BF16 ? bf16_to_f32(((const uint16_t*)a.x)[gi]) : ((const float*)a.x)[gi];
-    const int e = act_exponent(wave_max(fabsf(v)));
+    __shared__ float red4[kWaves];
+    const int t = blockIdx.x, H = a.H, NG = H / 64;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    auto load = [&](int i) {
+        const size_t gi = (size_t)t * H + i;
+        return BF16 ? bf16_to_f32(((const uint16_t*)a.x)[gi]) : ((const float*)a.x)[gi];
+    };
+    float mx = 0.0f;
+    for (int i = threadIdx.x; i < H; i += kBlock) mx = fmaxf(mx, fabsf(load(i)));
+    mx = wave_max(mx);
+    if (lane == 0) red4[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+    const int e = act_exponent(mx);
+    const float sc = ldexpf(1.0f, e);
     const int p = lane & 7;
-    const float vs = v * ldexpf(1.0f, e) * ((p & 1) ? 0.0625f : 1.0f);
-    const uint16_t hi = f16bits(vs);
-    const size_t dst = (size_t)t * H + 64 * g + (lane & ~7) + slot_of(p);
-    a.x16[dst] = hi;
-    if (XP == 2) {
-        const float r = vs - (float)__builtin_bit_cast(_Float16, hi);
-        a.x16[(size_t)a.T * H + dst] = f16bits(r);
+    for (int g = wave; g < NG; g += kWaves) {
+        const float vs = load(64 * g + lane) * sc;  // exact: a power-of-two scaling
+        const float vq = vs * ((p & 1) ? 0.0625f : 1.0f);
+        const uint16_t hi = f16bits(vq);
+        const size_t dst = (size_t)t * H + 64 * g + (lane & ~7) + slot_of(p);
+        a.x16[dst] = hi;
+        if (XP == 2) a.x16[(size_t)a.T * H + dst] = f16bits(vq - (float)__builtin_bit_cast(_Float16, hi));
+        const double gs = wave_sum_d((double)vs);
+        if (lane == 0) a.xsum[(size_t)t * NG + g] = (float)gs;
     }
-    const double xs = wave_sum_d((double)v);
-    if (lane == 0) {
-        a.xsum[(size_t)t * NG + g] = (float)xs;
-        a.xinv[(size_t)t * NG + g] = ldexpf(1.0f, -e);
-    }
+    if (threadIdx.x == 0) a.xinv[t] = ldexpf(1.0f, -e);
 }
 
 // ---------------------------------------------------------------------------
@@ -193,142 +254,172 @@ __global__ __launch_bounds__(kBlock) void k_group(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_gu_grouped: grid (tile capacity, max(I, Is)/64), 256 threads.
-// Workgroup (tile, g) covers rows [64g, 64g+64) of I: GU tiles 2g and 2g+1.
-// Wave w: GU tile 2g + (w >> 1), gate rows 16*(w & 1) + n and the matching up
-// rows 32 + 16*(w & 1) + n, over all 64-input groups of H.
+// k_gu_grouped: grid (tile capacity, ceil(max(I, Is)/128)), 256 threads.
+// Wave w: 64-row group gi = 2*blockIdx.y + (w & 1) of I (GU tiles 2gi and
+// 2gi+1: N-tiles 0-1 gate and 2-3 up of the first, 4-7 of the second) over
+// the half (w >> 1) of the 64-input groups of H.
+// Dynamic LDS: [H/64][16] group sums of the rows' activations, then the
+// partial sums of the upper-half waves, [2][8][64] float4.
 // ---------------------------------------------------------------------------
 template <int XP>
 __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
-    extern __shared__ float dsm[];  // [H/64][16] group sums, then [H/64][16] 2^-e
+    extern __shared__ float dsm[];
     __shared__ int s_tok[kTileRows];
-    __shared__ float s_mx[kWaves][kTileRows];
-    __shared__ float s_hs[kWaves][kTileRows];
+    __shared__ float s_xinv[kTileRows];
     const int tidx = blockIdx.x;
     if (tidx >= a.n_tiles[0]) return;
     const int4 tl = a.tiles[tidx];
     const bool shared = tl.x < 0;
     const int Ie = shared ? a.Is : a.I;
-    const int g = blockIdx.y;
-    if (g >= Ie / 64) return;
+    if (2 * (int)blockIdx.y * 64 >= Ie) return;
     const int H = a.H, NG = H / 64;
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int n = lane & 15, kq = lane >> 4;
-    const int tt = wave >> 1, hf = wave & 1;
+    const int gi = 2 * blockIdx.y + (wave & 1), kh = wave >> 1;
+    const bool active = gi * 64 < Ie;
     float* sX = dsm;
-    float* sXi = dsm + NG * kTileRows;
+    f32x4* red = (f32x4*)(dsm + NG * kTileRows);
 
-    // rows of the tile: token of each, then the tokens' group sums and scales
     for (int i = threadIdx.x; i < NG * kTileRows; i += kBlock) {
         const int m = i & (kTileRows - 1), jg = i >> 4;
         const int tok = m < tl.z ? (shared ? tl.y + m : a.pair_tok[tl.y + m]) : -1;
         sX[i] = tok < 0 ? 0.0f : a.xsum[(size_t)tok * NG + jg];
-        sXi[i] = tok < 0 ? 0.0f : a.xinv[(size_t)tok * NG + jg];
-        if (jg == 0) s_tok[m] = tok;
+        if (jg == 0) {
+            s_tok[m] = tok;
+            s_xinv[m] = tok < 0 ? 0.0f : a.xinv[tok];
+        }
     }
     __syncthreads();
 
-    const uint8_t* rec = shared ? a.shared : a.experts + (size_t)tl.x * a.rec_bytes;
-    const int b = 2 * g + tt, rg = 16 * hf + n, ru = 32 + rg;
-    const uint8_t* wg = rec + (size_t)48 * H * b + rg * 16 + kq * 4;
-    const uint8_t* wu = rec + (size_t)48 * H * b + ru * 16 + kq * 4;
-    const uint8_t* sbt = rec + (size_t)3 * H * Ie / 2 + (size_t)12 * H * g + (size_t)4 * H * tt;
-    const int tok_n = max(s_tok[n], 0);  // padded rows compute on token 0; discarded
-    const uint16_t* xr = a.x16 + (size_t)tok_n * H + 8 * kq;
-    const size_t xpart = (size_t)a.T * H;
-
-    // ring of kPfDepth groups: per group 2 chunks of A (per part), gate and up
-    // code dwords of both chunks, and the gate and up scale/bias pairs
-    u32x4 A[kPfDepth][2][XP];
-    uint32_t WG[kPfDepth][2], WU[kPfDepth][2], SG[kPfDepth], SU[kPfDepth];
-    auto load = [&](int q, int jg) {
+    f32x4 acc[kNtGu];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+    for (int nt = 0; nt < kNtGu; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+    const int j0 = kh * NG / 2, j1 = (kh + 1) * NG / 2;
+    if (active && j1 > j0) {
+        const uint8_t* rec = shared ? a.shared : a.experts + (size_t)tl.x * a.rec_bytes;
+        const __amdgpu_buffer_rsrc_t rw = rsrc(rec, shared ? a.rec_bytes_shared : a.rec_bytes);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x16, (size_t)XP * a.T * H * 2);
+        // per-lane offsets (bytes): row 16*kq + n of each GU tile (codes and
+        // scale/bias pair; one 16-byte load covers a 1 KB chunk of a tile per
+        // wave), and the lane's activations; the rest of each address is
+        // uniform and goes in the scalar offset
+        const int rl = 16 * kq + n;
+        const int wo[2] = {48 * H * (2 * gi) + rl * 16, 48 * H * (2 * gi + 1) + rl * 16};
+        const int so[2] = {3 * H * Ie / 2 + 12 * H * gi + rl * 4, 3 * H * Ie / 2 + 12 * H * gi + 4 * H + rl * 4};
+        const int xo = (max(s_tok[n], 0) * H + 8 * kq) * 2;
+        const int xpart = a.T * H * 2;
+        const Unpack up;
+        struct Regs {
+            u32x4 A[2][XP];
+            u32x4 W[2][2];  // [GU tile][chunk], rows 16*kq + n
+            uint32_t SB[2];
+        };
+        auto load = [&](Regs& R, int jg) {
 #pragma unroll
-            for (int p = 0; p < XP; ++p)
-                A[q][c][p] = *(const u32x4*)(xr + p * xpart + 64 * jg + 32 * c);
-            WG[q][c] = ldg_nt((const uint32_t*)(wg + (size_t)(2 * jg + c) * 1024));
-            WU[q][c] = ldg_nt((const uint32_t*)(wu + (size_t)(2 * jg + c) * 1024));
-        }
-        SG[q] = *(const uint32_t*)(sbt + (size_t)jg * 256 + rg * 4);
-        SU[q] = *(const uint32_t*)(sbt + (size_t)jg * 256 + ru * 4);
-    };
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int q = 0; q < kPfDepth; ++q) {
-        load(q, min(q, NG - 1));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    for (int j0 = 0; j0 < NG; j0 += kPfDepth) {
+                for (int p = 0; p < XP; ++p) R.A[c][p] = bload4(rx, xo, p * xpart + 128 * jg + 64 * c);
 #pragma unroll
-        for (int q = 0; q < kPfDepth; ++q) {
-            const int jg = j0 + q;
-            if (jg < NG) {
-                f32x4 pg = {0, 0, 0, 0}, pu = {0, 0, 0, 0};
+            for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c) R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], 2048 * jg + 1024 * c);
 #pragma unroll
-                    for (int p = 0; p < XP; ++p) {
-                        pg = mfma(A[q][c][p], WG[q][c], pg);
-                        pu = mfma(A[q][c][p], WU[q][c], pu);
-                    }
-                const f32x4 xi = *(const f32x4*)&sXi[jg * kTileRows + 4 * kq];
-                const f32x4 xs = *(const f32x4*)&sX[jg * kTileRows + 4 * kq];
-                const float sg = f16lo(SG[q]), bg = f16hi(SG[q]);
-                const float su = f16lo(SU[q]), bu = f16hi(SU[q]);
+            for (int t2 = 0; t2 < 2; ++t2) R.SB[t2] = bload(rw, so[t2], 256 * jg);
+        };
+        auto compute = [&](const Regs& R, int jg) {
+            const f32x4 xs = *(const f32x4*)&sX[jg * kTileRows + 4 * kq];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    accg[r] = fmaf(bg, xs[r], fmaf(sg, pg[r] * xi[r], accg[r]));
-                    accu[r] = fmaf(bu, xs[r], fmaf(su, pu[r] * xi[r], accu[r]));
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const u32x4 w0 = xpose4(R.W[t2][0]), w1 = xpose4(R.W[t2][1]);
+                const u32x4 sb = bcast4(R.SB[t2]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int nt = 4 * t2 + t;
+                    f32x4 pg = {0, 0, 0, 0};
+                    const half8 q0 = up.codes(w0[t]), q1 = up.codes(w1[t]);
+#pragma unroll
+                    for (int p = 0; p < XP; ++p) pg = mfma(R.A[0][p], q0, pg);
+#pragma unroll
+                    for (int p = 0; p < XP; ++p) pg = mfma(R.A[1][p], q1, pg);
+                    const float sc = f16lo(sb[t]), bi = f16hi(sb[t]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[nt][r] = fmaf(sc, pg[r], fmaf(bi, xs[r], acc[nt][r]));
                 }
             }
-            load(q, min(jg + kPfDepth, NG - 1));
+        };
+        // ring of kGuDepth groups in flight; refills are clamped to the last
+        // group (re-reads of it are cache hits)
+        Regs R[kGuDepth];
+#pragma unroll
+        for (int q = 0; q < kGuDepth; ++q) {
+            load(R[q], min(j0 + q, j1 - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
-
-    // h = silu(gate) * up for rows 4kq + r, column 32*tt + 16*hf + n of the group
-    float h[4], mx[4], hs[4];
+        for (int jb = j0; jb < j1; jb += kGuDepth) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float gv = accg[r];
-        h[r] = s_tok[4 * kq + r] < 0 ? 0.0f : gv / (1.0f + expf(-gv)) * accu[r];
-        mx[r] = row16_max(fabsf(h[r]));
-        hs[r] = row16_sum(h[r]);
-    }
-    if (n == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s_mx[wave][4 * kq + r] = mx[r];
-            s_hs[wave][4 * kq + r] = hs[r];
+            for (int q = 0; q < kGuDepth; ++q) {
+                if (jb + q < j1) compute(R[q], jb + q);
+                load(R[q], min(jb + q + kGuDepth, j1 - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
+    // upper half of H: to LDS; lower half adds it (fixed order: lower + upper)
+    if (kh == 1) {
+#pragma unroll
+        for (int nt = 0; nt < kNtGu; ++nt) red[((wave & 1) * kNtGu + nt) * 64 + lane] = acc[nt];
+    }
     __syncthreads();
+    if (kh == 1 || !active) return;
+#pragma unroll
+    for (int nt = 0; nt < kNtGu; ++nt) acc[nt] += red[((wave & 1) * kNtGu + nt) * 64 + lane];
+
+    // h = silu(gate) * up: rows 4kq + r, columns i = 64gi + 32*t2 + 16*hh + n
+    float h[4][4], mx[4], hs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float xi = s_xinv[4 * kq + r];
+        mx[r] = 0.0f;
+        hs[r] = 0.0f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {  // c4 = 2*t2 + hh
+            const int ntg = 4 * (c4 >> 1) + (c4 & 1);
+            const float gv = acc[ntg][r] * xi, uv = acc[ntg + 2][r] * xi;
+            const float v = s_tok[4 * kq + r] < 0 ? 0.0f : gv / (1.0f + expf(-gv)) * uv;
+            h[r][c4] = v;
+            mx[r] = fmaxf(mx[r], fabsf(v));
+            hs[r] += v;
+        }
+        mx[r] = row16_max(mx[r]);
+        hs[r] = row16_sum(hs[r]);
+    }
     const int NGi = a.Imax / 64;
-    const int col = 64 * g + 32 * tt + 16 * hf + n;
-    const int hcol = (col & ~7) + slot_of(n & 7);
     const float odd = (n & 1) ? 0.0625f : 1.0f;
+    const int pslot = (n & ~7) + slot_of(n & 7);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * kq + r;
         if (m >= tl.z) continue;
-        const float M = fmaxf(fmaxf(s_mx[0][m], s_mx[1][m]), fmaxf(s_mx[2][m], s_mx[3][m]));
-        const int e = act_exponent(M);
+        const int e = act_exponent(mx[r]);
+        const float sc = ldexpf(1.0f, e) * odd;
         const size_t hrow = shared ? (size_t)a.P + tl.y + m : (size_t)(tl.y + m);
-        a.h16[hrow * a.Imax + hcol] = f16bits(h[r] * ldexpf(1.0f, e) * odd);
-        if (wave == 0 && n == 0) {
-            a.hsum[hrow * NGi + g] = ((s_hs[0][m] + s_hs[1][m]) + s_hs[2][m]) + s_hs[3][m];
-            a.hinv[hrow * NGi + g] = ldexpf(1.0f, -e);
+        uint16_t* hp = a.h16 + hrow * a.Imax + 64 * gi + pslot;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) hp[16 * c4] = f16bits(h[r][c4] * sc);
+        if (n == 0) {
+            a.hsum[hrow * NGi + gi] = hs[r];
+            a.hinv[hrow * NGi + gi] = ldexpf(1.0f, -e);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_down_grouped: grid (tile capacity, H/64), 256 threads.  Wave w computes
-// outputs o0 + 16w + n over all 64-groups of I.
+// k_down_grouped: grid (tile capacity, ceil(H/256)), 256 threads.  Wave w:
+// outputs o0 = 256*blockIdx.y + 64w + [0, 64) (N-tiles of 16) over all of I.
+// Dynamic LDS: [Ie/64][16] group sums of h, then [Ie/64][16] 2^-e of h.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
-    extern __shared__ float dsm[];  // [Ie/64][16] group sums of h, then [Ie/64][16] 2^-e
+    extern __shared__ float dsm[];
     __shared__ int s_row[kTileRows];
     const int tidx = blockIdx.x;
     if (tidx >= a.n_tiles[0]) return;
@@ -349,43 +440,59 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
         if (jg == 0) s_row[m] = row;
     }
     __syncthreads();
+    const int o0 = 256 * blockIdx.y + 64 * wave;
+    if (o0 >= H) return;
     const uint8_t* rec = shared ? a.shared : a.experts + (size_t)tl.x * a.rec_bytes;
-    const int o = blockIdx.y * 64 + 16 * wave + n;
-    const uint8_t* wd = rec + (size_t)32 * H + (size_t)o * 16 + kq * 4;
-    const uint8_t* sbd = rec + (size_t)3 * H * Ie / 2 + (size_t)8 * H + (size_t)o * 4;
-    const uint16_t* hr = a.h16 + (size_t)max(s_row[n], 0) * a.Imax + 8 * kq;
-
-    u32x4 A[kPfDepth][2];
-    uint32_t W[kPfDepth][2], SB[kPfDepth];
-    auto load = [&](int q, int jg) {
+    const __amdgpu_buffer_rsrc_t rw = rsrc(rec, shared ? a.rec_bytes_shared : a.rec_bytes);
+    const __amdgpu_buffer_rsrc_t rh = rsrc(a.h16, (size_t)(a.P + a.T) * a.Imax * 2);
+    // lane row o0 + 16*kq + n: one 16-byte load covers the wave's 64 rows of a
+    // down chunk, one dword load their scale/bias pairs
+    const int rl = o0 + 16 * kq + n;
+    const int wo = 32 * H + rl * 16;
+    const int so = 3 * H * Ie / 2 + 8 * H + rl * 4;
+    const int ho = (max(s_row[n], 0) * a.Imax + 8 * kq) * 2;
+    const Unpack up;
+    f32x4 acc[kNtDn];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            A[q][c] = *(const u32x4*)(hr + 64 * jg + 32 * c);
-            W[q][c] = ldg_nt((const uint32_t*)(wd + (size_t)48 * H * (2 * jg + c)));
-        }
-        SB[q] = *(const uint32_t*)(sbd + (size_t)12 * H * jg);
+    for (int nt = 0; nt < kNtDn; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+    struct Regs {
+        u32x4 A[2];
+        u32x4 W[2];
+        uint32_t SB;
     };
+    auto load = [&](Regs& R, int jg) {
 #pragma unroll
-    for (int q = 0; q < kPfDepth; ++q) {
-        load(q, min(q, NGe - 1));
+        for (int c = 0; c < 2; ++c) R.A[c] = bload4(rh, ho, 128 * jg + 64 * c);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) R.W[c] = bload4<kAuxNT>(rw, wo, 48 * H * (2 * jg + c));
+        R.SB = bload(rw, so, 12 * H * jg);
+    };
+    auto compute = [&](const Regs& R, int jg) {
+        const f32x4 hi = *(const f32x4*)&sHi[jg * kTileRows + 4 * kq];
+        const f32x4 hsum = *(const f32x4*)&sH[jg * kTileRows + 4 * kq];
+        const u32x4 w0 = xpose4(R.W[0]), w1 = xpose4(R.W[1]);
+        const u32x4 sb = bcast4(R.SB);
+#pragma unroll
+        for (int nt = 0; nt < kNtDn; ++nt) {
+            f32x4 pd = {0, 0, 0, 0};
+            pd = mfma(R.A[0], up.codes(w0[nt]), pd);
+            pd = mfma(R.A[1], up.codes(w1[nt]), pd);
+            const float sd = f16lo(sb[nt]), bd = f16hi(sb[nt]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[nt][r] = fmaf(bd, hsum[r], fmaf(sd, pd[r] * hi[r], acc[nt][r]));
+        }
+    };
+    Regs R[kDnDepth];
+#pragma unroll
+    for (int q = 0; q < kDnDepth; ++q) {
+        load(R[q], min(q, NGe - 1));
         __builtin_amdgcn_sched_barrier(0);
     }
-    f32x4 acc = {0, 0, 0, 0};
-    for (int j0 = 0; j0 < NGe; j0 += kPfDepth) {
+    for (int jb = 0; jb < NGe; jb += kDnDepth) {
 #pragma unroll
-        for (int q = 0; q < kPfDepth; ++q) {
-            const int jg = j0 + q;
-            if (jg < NGe) {
-                f32x4 pd = {0, 0, 0, 0};
-                pd = mfma(A[q][0], W[q][0], pd);
-                pd = mfma(A[q][1], W[q][1], pd);
-                const f32x4 hi = *(const f32x4*)&sHi[jg * kTileRows + 4 * kq];
-                const f32x4 hsum = *(const f32x4*)&sH[jg * kTileRows + 4 * kq];
-                const float sd = f16lo(SB[q]), bd = f16hi(SB[q]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf(bd, hsum[r], fmaf(sd, pd[r] * hi[r], acc[r]));
-            }
-            load(q, min(jg + kPfDepth, NGe - 1));
+        for (int q = 0; q < kDnDepth; ++q) {
+            if (jb + q < NGe) compute(R[q], jb + q);
+            load(R[q], min(jb + q + kDnDepth, NGe - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -393,8 +500,8 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * kq + r;
         if (m >= tl.z) continue;
-        float v = acc[r];
         int t, j;
+        bool bad = false;
         if (shared) {
             t = tl.y + m;
             j = a.k;
@@ -402,9 +509,11 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
             t = a.pair_tok[tl.y + m];
             j = a.pair_slot[tl.y + m];
             const int e = a.ids[(size_t)t * a.k + j];
-            if (e < 0 || e >= a.E) v = __builtin_nanf("");
+            bad = e < 0 || e >= a.E;
         }
-        a.eo[((size_t)t * (a.k + 1) + j) * H + o] = v;
+        float* dst = a.eo + ((size_t)t * (a.k + 1) + j) * H + o0 + n;
+#pragma unroll
+        for (int nt = 0; nt < kNtDn; ++nt) dst[16 * nt] = bad ? __builtin_nanf("") : acc[nt][r];
     }
 }
 
@@ -414,7 +523,7 @@ __global__ void k_zero_shared_rows(PrefillArgs a) {  // no shared expert: eo[:, 
 }
 
 hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s) {
-    const dim3 grid((a.H / 64 + kWaves - 1) / kWaves, a.T);
+    const dim3 grid(a.T);
     if (a.xparts == 1 && act_bf16)
         hipLaunchKernelGGL((k_prep_tokens<1, true>), grid, dim3(kBlock), 0, s, a);
     else if (a.xparts == 1)
@@ -426,15 +535,24 @@ hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_ffn(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_group, dim3(1), dim3(kBlock), 0, s, a);
-    const dim3 gu(a.tile_cap, a.Imax / 64);
-    const size_t lds_gu = (size_t)(a.H / 64) * kTileRows * 8, lds_dn = (size_t)(a.Imax / 64) * kTileRows * 8;
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s) {
+    const dim3 grid(a.tile_cap, (a.Imax + 127) / 128);
+    const size_t lds = (size_t)(a.H / 64) * kTileRows * 4 + (size_t)2 * kNtGu * 64 * 16;
     if (a.xparts == 1)
-        hipLaunchKernelGGL((k_gu_grouped<1>), gu, dim3(kBlock), lds_gu, s, a);
+        hipLaunchKernelGGL((k_gu_grouped<1>), grid, dim3(kBlock), lds, s, a);
     else
-        hipLaunchKernelGGL((k_gu_grouped<2>), gu, dim3(kBlock), lds_gu, s, a);
-    hipLaunchKernelGGL(k_down_grouped, dim3(a.tile_cap, a.H / 64), dim3(kBlock), lds_dn, s, a);
+        hipLaunchKernelGGL((k_gu_grouped<2>), grid, dim3(kBlock), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s) {
+    const size_t lds = (size_t)(a.Imax / 64) * kTileRows * 8;
+    hipLaunchKernelGGL(k_down_grouped, dim3(a.tile_cap, (a.H + 255) / 256), dim3(kBlock), lds, s, a);
     if (!a.Is) hipLaunchKernelGGL(k_zero_shared_rows, dim3((a.H + kBlock - 1) / kBlock, a.T), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }

@@ -25,7 +25,8 @@ EXPORTS = ["moe_expert_record_bytes", "moe_layer_create", "moe_layer_destroy",
            "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_poll_device_error",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
            "moe_status_str", "moe_last_error"]
-KERNEL_NAMES = {0: "route", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine", 5: "topk"}
+KERNEL_NAMES = {0: "route", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine", 5: "topk",
+                6: "grouped_prep", 7: "grouping", 8: "grouped_gate_up", 9: "grouped_down"}
 
 
 class MoeError(RuntimeError):

@@ -132,6 +132,16 @@ size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens);
 moe_status moe_route_topk(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
                           float* w, void* workspace, void* stream);
 
+/* Calls of 4 or more tokens (prefill chunks; the pages run prompts in chunks of
+ * up to 128 tokens so that a fetched expert serves several rows: TurboFieldfare
+ * article, "Proses pembuatan token"; Colibri analysis report, section 2,
+ * "Union"; Colibri README, "What's implemented", batch-union MoE) take the
+ * grouped path: the (token, slot) pairs are sorted by expert and every selected
+ * expert's record is read once per call and applied to all of its tokens with
+ * MFMA.  Results agree with the per-token path within the stated tolerance, not
+ * bit for bit; within each path a token's result does not depend on the other
+ * tokens of its call. */
+
 /* Per-expert SwiGLU outputs for the given selection.
  *   ids        device [T][k] int32 (values outside [0, E) set the device error
  *              flag, see moe_poll_device_error, and make that slot's output NaN)
@@ -189,7 +199,9 @@ moe_status moe_poll_device_error(moe_layer_t layer, void* workspace, void* strea
  * launches is bracketed by two hipEvents recorded on its launch stream, up to
  * `capacity` launches.  moe_profile_read synchronises those events and writes,
  * per recorded launch, the kernel id (0 router, 1 activation prep, 2 gate/up,
- * 3 down with in-place combine, 4 combine, 5 top-k) and the elapsed milliseconds;
+ * 3 down with in-place combine, 4 combine, 5 top-k; for calls of 4 or more
+ * tokens: 6 activation prep, 7 grouping by expert, 8 grouped gate/up, 9 grouped
+ * down) and the elapsed milliseconds;
  * it returns the number of records (or a negative status) and clears them.
  * Profiling state is process-wide and not thread-safe; do not profile inside
  * stream capture.  Errors: ARG, HIP, NOMEM. */

@@ -244,7 +244,9 @@ class Workload:
     n_layers: int
     n_tokens: int       # tokens per step (1 = decode, 128 = prefill chunk)
     steps: int
-    routing: str        # "natural" or "zipf"
+    routing: str        # "natural" (x ~ N(0,1) through the router), "zipf" or
+                        # "uniform" (Gumbel-top-k targets realised through the
+                        # router; uniform = Zipf with s = 0)
     zipf_s: float = 0.0
     n_slots: int = 0    # HBM expert slots per layer (0 = fully resident)
     seed: int = 0
@@ -280,7 +282,8 @@ WORKLOADS = {
                  "zipf", zipf_s=1.1, seed=0xB17E0003,
                  note="GLM-scale 40-layer decode, Zipf(1.1) routing"),
         Workload("glm_prefill_h6144_e256_t128", 6144, 256, 2048, 8, 2048, "bf16", 1, 128, 1,
-                 "natural", seed=0xB17E0004, note="GLM-scale 128-token prefill chunk"),
+                 "uniform", zipf_s=0.0, seed=0xB17E0004,
+                 note="GLM-scale 128-token prefill chunk, uniform random routing"),
         Workload("offload_h2816_e256_l40_lfu16", 2816, 256, 704, 8, 2112, "bf16", 40, 1, 512,
                  "zipf", zipf_s=1.1, n_slots=16, seed=0xB17E0005,
                  note="out-of-core decode: 16-slot LFU per layer, pinned host pool"),

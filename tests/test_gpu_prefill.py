@@ -151,3 +151,20 @@ def test_bad_ids_raise_device_error_and_poison():
                 assert np.all(np.isnan(eo[t, j])), (t, j)
             else:
                 assert np.all(np.isfinite(eo[t, j])), (t, j)
+
+
+def test_long_call_runs_in_chunks(orc):
+    """A call longer than one grouped pass (here k = 16 and a 16384-wide shared
+    expert give 2^31 / (17 * 16384 * 2) = 3855 tokens per pass): tokens on both
+    sides of the pass boundary match the oracle and equal a short call on the
+    same tokens bit for bit."""
+    H, E, I, k, Is, T = 64, 16, 64, 16, 16384, 3900
+    per_pass = min(8192, (2 ** 31 - 1) // ((k + 1) * Is * 2), (2 ** 31 - 1) // (H * 2))
+    assert per_pass == 3855 < T
+    dl = DeviceLayer(0xB17E0660, 0, H, E, I, k, Is, "bf16")
+    xq, xd = tokens(dl, orc, T)
+    ids, w, y = dl.layer_obj.forward(to_dev(xq, "bf16"))
+    lo, hi = per_pass - 5, per_pass + 5
+    i2, w2, y2 = dl.layer_obj.forward(to_dev(xq[lo:hi], "bf16"))
+    assert torch.equal(i2, ids[lo:hi]) and torch.equal(w2, w[lo:hi]) and torch.equal(y2, y[lo:hi])
+    check(dl, orc, xd, ids, w, y, "chunked call", sample=[0, lo, per_pass - 1, per_pass, hi, T - 1])

@@ -73,13 +73,26 @@ def test_glm_layer_zipf_full_size(orc):
 
 
 def test_glm_prefill_chunk_full_size(orc):
-    """GLM-scale 128-token chunk through the grouped path: every token's ids and
+    """GLM-scale 128-token chunk (uniform random routing realised through the
+    router) through the grouped path: every token's ids and
     gate weights against the oracle router, outputs on 4 sampled tokens (the
     oracle regenerates each selected record on the CPU, about a second each),
     and the whole chunk's result permuted exactly with its tokens."""
     wl = synth.WORKLOADS["glm_prefill_h6144_e256_t128"]
     dl = DeviceLayer(wl.seed, 0, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
-    toks = [dl.natural_token(orc, s) for s in range(wl.n_tokens)]
+    Wd = dl.rq.astype(np.float64) * dl.rs.view(np.float16).astype(np.float64)[:, None]
+    zr = synth.ZipfRealiser(Wd, wl.zipf_s, wl.seed, 0)  # s = 0: uniform Gumbel-top-8 targets
+    toks = []
+    for t in range(wl.n_tokens):
+        for a in range(50):
+            xq = synth.quantize_act(zr.activations(t, a)[0], wl.act)
+            xd = orc.act_to_f64(wl.act, xq)
+            if gap_ok(orc.router_logits(dl.rq, dl.rs, xd), wl.top_k):
+                break
+        toks.append((xq, xd))
+    n_unique = len({int(e) for t in toks for e in orc.route(dl.rq, dl.rs, t[1], wl.top_k)[0]})
+    print(f"glm prefill chunk: {n_unique} distinct experts selected", flush=True)
+    assert n_unique > 230  # uniform: 256 * (1 - (1 - 8/256)^128) = 251.6 expected
     xq = np.stack([t[0] for t in toks])
     ws = dl.layer_obj.workspace(wl.n_tokens)
     ids, w, y = dl.layer_obj.forward(to_dev(xq, wl.act), ws)
