@@ -14,7 +14,15 @@ Printed (stdout, one JSON line): decode tokens/s per MoE layer (value), the
 whole-stack tokens/s, achieved HBM GB/s on algorithmic bytes (router + 8
 selected records + shared record per token-layer) against the 8 TB/s peak,
 a roofline entry for the dominant kernel (gate/up) from a live per-kernel
-hipEvent pass, and the CPU oracle timed on this host's cores.
+pass (dispatch-stamped hipEvents), and the CPU oracle timed on this host's
+cores.
+
+--workload glm_prefill_h6144_e256_t128 measures the grouped (prefill) path
+instead: a step is one 128-token chunk through one layer, cycling over
+--prefill-layers layers of distinct weights; the roofline entry is the grouped
+gate/up kernel's, with its MFMA utilisation.  --workload
+offload_h2816_e256_l40_lfu16 measures the out-of-core decode with the HBM
+slot cache.
 """
 from __future__ import annotations
 
@@ -75,6 +83,22 @@ def make_inputs(wl, layer, S):
         zr = synth.ZipfRealiser(W, wl.zipf_s, wl.seed, layer)
         return np.stack([zr.activations(s) for s in range(S)])
     return np.stack([synth.activations(wl.seed, layer, s, wl.hidden, wl.n_tokens) for s in range(S)])
+
+
+def kernel_timed_pass(run_steps, capacity):
+    """Per-launch timings of run_steps(): while the library's profiler is on it
+    dispatches each kernel with hipExtLaunchKernelGGL and a start/stop hipEvent
+    pair on the launch stream, stamped by that dispatch itself (its begin and
+    end, as a kernel trace reports them).  Returns [(name, ms)]."""
+    import torch
+    from bit_routed_expert_moe_amd import KernelTimer
+    run_steps()  # warm pass
+    torch.cuda.synchronize()
+    with KernelTimer(capacity=capacity) as kt:
+        run_steps()
+    recs = kt.read()
+    torch.cuda.synchronize()
+    return recs
 
 
 def cpu_baseline(wl, xs_host, seconds):
@@ -221,7 +245,7 @@ def run_prefill(args, wl):
     import torch
     import synth
     import synth.gpu
-    from bit_routed_expert_moe_amd import KernelTimer, Layer, record_bytes
+    from bit_routed_expert_moe_amd import Layer, record_bytes
 
     H, E, I, k, Is, T = wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.n_tokens
     NL, C = args.prefill_layers, args.prefill_chunks
@@ -315,40 +339,30 @@ def run_prefill(args, wl):
     mfma_peak = 2.5e15  # dense fp16 MFMA, MI355X
     mean_exec = float(np.mean(exec_flops[steps_j]))
 
-    # live per-kernel hipEvent pass, launched eagerly over the S distinct steps
-    with KernelTimer(capacity=S * 8 + 64) as kt:
+    # live per-kernel pass over the S distinct steps (dispatch-stamped hipEvents)
+    def profiled_steps():
         for s in range(S):
             run_step(s)
-    recs = kt.read()
-    torch.cuda.synchronize()
-    empty = []
-    for _ in range(64):
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        torch.cuda._sleep(0)
-        b_.record()
-        b_.synchronize()
-        empty.append(a_.elapsed_time(b_))
-    ev_overhead_ms = float(np.median(empty))
+
+    recs = kernel_timed_pass(profiled_steps, S * 8 + 64)
     per_step_bytes = {"grouped_gate_up": uniq * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0),
                       "grouped_down": uniq * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0)}
     kernels = {}
     for name in sorted({r[0] for r in recs}):
         ms = np.array([m for n_, m in recs if n_ == name])
-        net = np.maximum(ms - ev_overhead_ms, 1e-6)
-        ent = {"launches": int(ms.size), "avg_us": round(float(net.mean()) * 1e3, 3),
-               "avg_us_raw": round(float(ms.mean()) * 1e3, 3)}
+        ent = {"launches": int(ms.size), "avg_us": round(float(ms.mean()) * 1e3, 3),
+               "p50_us": round(float(np.median(ms)) * 1e3, 3)}
         if name in per_step_bytes and ms.size == S:
             b = per_step_bytes[name]
             ent["alg_bytes_mean"] = int(b.mean())
-            ent["gbps"] = round(float(b.sum()) / (float(net.sum()) * 1e-3) / 1e9, 1)
+            ent["gbps"] = round(float(b.sum()) / (float(ms.sum()) * 1e-3) / 1e9, 1)
         kernels[name] = ent
     gu = kernels["grouped_gate_up"]
     gu_flops = float(np.mean(2.0 * 16 * 2 * H * (tiles * I + shared_tiles * Is)))
     roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4), "traffic": None,
                 "kernel": "k_gu_grouped", "alg_bytes_per_launch": gu["alg_bytes_mean"],
-                "avg_launch_us": gu["avg_us"], "event_pair_overhead_us": round(ev_overhead_ms * 1e3, 3),
+                "avg_launch_us": gu["avg_us"], "timing": "hipExtLaunchKernelGGL start/stop events",
                 "mfma_util": round(gu_flops / (gu["avg_us"] * 1e-6) / mfma_peak, 4)}
 
     cpu = None
@@ -439,7 +453,7 @@ def main():
         return
     import synth
     import synth.gpu
-    from bit_routed_expert_moe_amd import KernelTimer, Layer, record_bytes, stack_forward
+    from bit_routed_expert_moe_amd import Layer, record_bytes, stack_forward
 
     wl = synth.WORKLOADS[args.workload]
     if wl.n_slots:
@@ -521,33 +535,23 @@ def main():
     layer_tok_s = L * T / (ms_per_step * 1e-3)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # live per-kernel hipEvent pass over the same steps, launched eagerly
+    # live per-kernel pass over the same steps (dispatch-stamped hipEvents)
     P = min(args.profile_steps, S)
-    with KernelTimer(capacity=P * L * 4 + 64) as kt:
+
+    def profiled_steps():
         for s in range(P):
             run_step(s)
-    recs = kt.read()
-    torch.cuda.synchronize()
-    # event-pair overhead: the same bracketing around an empty kernel on the same stream
-    empty = []
-    for _ in range(64):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        torch.cuda._sleep(0)
-        e1.record()
-        e1.synchronize()
-        empty.append(e0.elapsed_time(e1))
-    ev_overhead_ms = float(np.median(empty))
+
+    recs = kernel_timed_pass(profiled_steps, P * L * 4 + 64)
     kbytes = {"route": T * (E * H + 2 * E),
               "gate_up": T * (k * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0)),
               "down_combine": T * (k * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0))}
     kernels = {}
     for name in sorted({r[0] for r in recs}):
         ms = np.array([m for n_, m in recs if n_ == name])
-        net = max(float(ms.mean()) - ev_overhead_ms, 1e-6)
+        net = float(ms.mean())
         ent = {"launches": int(ms.size), "avg_us": round(net * 1e3, 3),
-               "avg_us_raw": round(float(ms.mean()) * 1e3, 3),
-               "p50_us_raw": round(float(np.median(ms)) * 1e3, 3)}
+               "p50_us": round(float(np.median(ms)) * 1e3, 3)}
         if name in kbytes:
             ent["alg_bytes"] = int(kbytes[name])
             ent["gbps"] = round(kbytes[name] / (net * 1e-3) / 1e9, 1)
@@ -557,7 +561,7 @@ def main():
                 "unit": "GB/s", "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for(wl.name, "k_gate_up"),
                 "kernel": "k_gate_up", "alg_bytes_per_launch": gu["alg_bytes"],
-                "avg_launch_us": gu["avg_us"], "event_pair_overhead_us": round(ev_overhead_ms * 1e3, 3)}
+                "avg_launch_us": gu["avg_us"], "timing": "hipExtLaunchKernelGGL start/stop events"}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -2,6 +2,7 @@
 // (moe_layer.hip) and its kernels (moe_kernels.hip).  Not part of the ABI.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -109,5 +110,26 @@ struct CombineArgs {
     void* y;          // [T][H]
     int H, k, T, y_bf16;
 };
+
+// Per-launch timing: when the host layer sets g_stamp around one launcher
+// call, the first kernel that launcher starts is dispatched with
+// hipExtLaunchKernelGGL so that the event pair holds that dispatch's own start
+// and end (no marker packets in between).  Null when profiling is off.
+struct LaunchStamp {
+    hipEvent_t start, stop;
+    bool used;
+};
+extern LaunchStamp* g_stamp;
+
+template <typename... P, typename... A>
+inline void launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A... args) {
+    if (g_stamp && !g_stamp->used) {
+        g_stamp->used = true;
+        hipExtLaunchKernelGGL(k, grid, block, (uint32_t)lds, s, g_stamp->start, g_stamp->stop, 0,
+                              static_cast<P>(args)...);
+    } else {
+        hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<P>(args)...);
+    }
+}
 
 }  // namespace moe

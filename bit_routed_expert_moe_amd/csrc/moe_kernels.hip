@@ -551,26 +551,26 @@ hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s) 
     if (a.prep) nb = max(nb, (a.H / 64 + kWaves - 1) / kWaves);
     const dim3 grid(nb, T);
     if (act_bf16)
-        hipLaunchKernelGGL((k_route<1, true>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_route<1, true>, grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_route<2, false>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_route<2, false>, grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const RouteArgs& a, int T, hipStream_t s) {
-    if (a.E <= 64) hipLaunchKernelGGL(k_topk<1>, dim3(T), dim3(64), 0, s, a);
-    else if (a.E <= 128) hipLaunchKernelGGL(k_topk<2>, dim3(T), dim3(64), 0, s, a);
-    else if (a.E <= 256) hipLaunchKernelGGL(k_topk<4>, dim3(T), dim3(64), 0, s, a);
-    else hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(64), 0, s, a);
+    if (a.E <= 64) launch_kernel(k_topk<1>, dim3(T), dim3(64), 0, s, a);
+    else if (a.E <= 128) launch_kernel(k_topk<2>, dim3(T), dim3(64), 0, s, a);
+    else if (a.E <= 256) launch_kernel(k_topk<4>, dim3(T), dim3(64), 0, s, a);
+    else launch_kernel(k_topk<16>, dim3(T), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
     const dim3 grid((a.H / 64 + kWaves - 1) / kWaves, T);
     if (act_bf16)
-        hipLaunchKernelGGL((k_prep<1, true>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep<1, true>, grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_prep<2, false>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep<2, false>, grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
@@ -580,7 +580,7 @@ static hipError_t launch_gu_xq(const FfnArgs& a, int T, int n_units, hipStream_t
     const int NG = a.H / 64;
     const size_t sh = ((size_t)(a.H / 2) * XP + 3 * NG + kWaves * 64) * 4;
     const int m = a.gpw_gu;
-#define MOE_GU(MG) hipLaunchKernelGGL((k_gate_up<XP, MG, Q>), grid, dim3(kBlock), sh, s, a)
+#define MOE_GU(MG) launch_kernel(k_gate_up<XP, MG, Q>, grid, dim3(kBlock), sh, s, a)
     if (m <= 4) MOE_GU(4);
     else if (m <= 8) MOE_GU(8);
     else if (m <= 12) MOE_GU(12);
@@ -611,7 +611,7 @@ hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {
     const int nb = 2 * max(a.gi, a.gis);  // blocks staged per item (upper bound)
     const size_t sh = ((size_t)nb * (16 * kHParts + 3) + kWaves * 64) * 4;
     const int m = a.gpw_dn;
-#define MOE_DN(MG) hipLaunchKernelGGL((k_down<MG>), grid, dim3(kBlock), sh, s, a)
+#define MOE_DN(MG) launch_kernel(k_down<MG>, grid, dim3(kBlock), sh, s, a)
     if (m <= 2) MOE_DN(2);
     else if (m <= 4) MOE_DN(4);
     else if (m <= 8) MOE_DN(8);
@@ -622,12 +622,12 @@ hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     const dim3 grid((a.H + kBlock - 1) / kBlock, a.T);
-    hipLaunchKernelGGL(k_combine, grid, dim3(kBlock), 0, s, a);
+    launch_kernel(k_combine, grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_clear_word(uint32_t* p, hipStream_t s) {
-    hipLaunchKernelGGL(k_clear_word, dim3(1), dim3(1), 0, s, p);
+    launch_kernel(k_clear_word, dim3(1), dim3(1), 0, s, p);
     return hipGetLastError();
 }
 

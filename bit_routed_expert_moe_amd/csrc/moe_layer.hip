@@ -65,6 +65,10 @@ struct moe_layer {
     int gpw_gu, gpw_dn;
 };
 
+namespace moe {
+LaunchStamp* g_stamp = nullptr;  // see launch_kernel
+}  // namespace moe
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -82,14 +86,17 @@ bool g_prof_on = false;
 
 template <typename F>
 hipError_t timed(int kid, hipStream_t s, F&& launch) {
-    ProfRec* r = nullptr;
-    if (g_prof_on && g_prof_n < g_prof.size()) {
-        r = &g_prof[g_prof_n++];
-        r->kid = kid;
-        (void)hipEventRecord(r->a, s);
-    }
+    if (!(g_prof_on && g_prof_n < g_prof.size())) return launch();
+    ProfRec* r = &g_prof[g_prof_n++];
+    r->kid = kid;
+    LaunchStamp st{r->a, r->b, false};
+    g_stamp = &st;
     hipError_t e = launch();
-    if (r) (void)hipEventRecord(r->b, s);
+    g_stamp = nullptr;
+    if (!st.used) {  // nothing launched: an empty interval
+        (void)hipEventRecord(r->a, s);
+        (void)hipEventRecord(r->b, s);
+    }
     return e;
 }
 

@@ -525,18 +525,18 @@ __global__ void k_zero_shared_rows(PrefillArgs a) {  // no shared expert: eo[:, 
 hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s) {
     const dim3 grid(a.T);
     if (a.xparts == 1 && act_bf16)
-        hipLaunchKernelGGL((k_prep_tokens<1, true>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<1, true>, grid, dim3(kBlock), 0, s, a);
     else if (a.xparts == 1)
-        hipLaunchKernelGGL((k_prep_tokens<1, false>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<1, false>, grid, dim3(kBlock), 0, s, a);
     else if (act_bf16)
-        hipLaunchKernelGGL((k_prep_tokens<2, true>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<2, true>, grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_prep_tokens<2, false>), grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<2, false>, grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(kBlock), 0, s, a);
+    launch_kernel(k_group, dim3(1), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
@@ -544,16 +544,16 @@ hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s) {
     const dim3 grid(a.tile_cap, (a.Imax + 127) / 128);
     const size_t lds = (size_t)(a.H / 64) * kTileRows * 4 + (size_t)2 * kNtGu * 64 * 16;
     if (a.xparts == 1)
-        hipLaunchKernelGGL((k_gu_grouped<1>), grid, dim3(kBlock), lds, s, a);
+        launch_kernel(k_gu_grouped<1>, grid, dim3(kBlock), lds, s, a);
     else
-        hipLaunchKernelGGL((k_gu_grouped<2>), grid, dim3(kBlock), lds, s, a);
+        launch_kernel(k_gu_grouped<2>, grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s) {
     const size_t lds = (size_t)(a.Imax / 64) * kTileRows * 8;
-    hipLaunchKernelGGL(k_down_grouped, dim3(a.tile_cap, (a.H + 255) / 256), dim3(kBlock), lds, s, a);
-    if (!a.Is) hipLaunchKernelGGL(k_zero_shared_rows, dim3((a.H + kBlock - 1) / kBlock, a.T), dim3(kBlock), 0, s, a);
+    launch_kernel(k_down_grouped, dim3(a.tile_cap, (a.H + 255) / 256), dim3(kBlock), lds, s, a);
+    if (!a.Is) launch_kernel(k_zero_shared_rows, dim3((a.H + kBlock - 1) / kBlock, a.T), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
