@@ -137,12 +137,14 @@ WsLayout ws_layout(const moe_layer* L, int T) {
         off = align256(off + bytes);
         return at;
     };
+    // counters first, at offsets that do not depend on T: every call leaves
+    // them at zero, so a workspace zero-filled once serves calls of any size
     o.err = take(4);
-    o.rctr = take((size_t)T * 4);
+    o.rctr = take((size_t)kCounterStride * 4);
+    o.dctr = take((size_t)(kPrefillMinTokens - 1) * L->n_otiles * kCounterStride * 4);
     o.logits = take((size_t)T * L->d.n_experts * 4);
     o.slot_ids = take((size_t)T * k * 4);
     if (T < kPrefillMinTokens) {  // per-token (decode) path
-        o.dctr = take((size_t)T * L->n_otiles * kCounterStride * 4);
         o.xpairs = take((size_t)T * (H / 2) * L->xparts * 4);
         o.xK = take((size_t)T * L->NG * 4);
         o.xX = take((size_t)T * L->NG * 4);

@@ -118,9 +118,10 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
 moe_status moe_layer_destroy(moe_layer_t layer);
 
 /* Device workspace bytes needed by the compute calls for n_tokens tokens.
- * The workspace must be zero-filled before its first use; every call returns
- * its internal counters to zero, so it can be reused without clearing.  Two
- * calls that overlap in time must not share a workspace. */
+ * The workspace must be zero-filled before its first use; its arrival
+ * counters sit at fixed offsets at its start and every call returns them to
+ * zero, so it can be reused without clearing, for any n_tokens it is large
+ * enough for.  Two calls that overlap in time must not share a workspace. */
 size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens);
 
 /* Router + exact top-k + gates for n_tokens tokens.
