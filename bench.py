@@ -41,23 +41,30 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs (profiles/k_gate_up_gemma_stack_counters.md), each scaled by
-# the same counter's reading for a 1 GiB device copy (FETCH x2.0, WRITE x1.0).
-# Valid only for the kernel source they were taken on; None once it changes.
-TRAFFIC_SOURCE_SHA256 = "43385aefecdbd8b3"  # first 16 hex digits of csrc/moe_kernels.hip when measured
+# WRITE_SIZE runs (profiles/*_counters.md), each scaled by the same counter's
+# reading for a 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Valid only for the
+# kernel source they were taken on (first 16 hex digits of its sha256); None
+# once that file changes.
 TRAFFIC = {
-    # FETCH_SIZE 12154.6 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): 24931430,
+    # FETCH_SIZE 12158.1 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24938598, "moe_kernels.hip", "6d740c8bcffa6c9f"),
+    # FETCH_SIZE 1866012.9 KiB x 2.0 + WRITE_SIZE 5754.7 KiB x 1.0 per launch (mean)
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3827487232, "moe_prefill.hip", "15dbfa7b810640d6"),
 }
 
 
 def traffic_for(workload, kernel):
     import hashlib
-    src = os.path.join(ROOT, "bit_routed_expert_moe_amd", "csrc", "moe_kernels.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_SOURCE_SHA256:
+    ent = TRAFFIC.get((workload, kernel))
+    if ent is None:
+        return None
+    nbytes, src, digest = ent
+    with open(os.path.join(ROOT, "bit_routed_expert_moe_amd", "csrc", src), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
             return None
-    return TRAFFIC.get((workload, kernel))
+    return nbytes
+
+
 METRIC = "decode tokens/s per MoE layer + achieved HBM GB/s vs peak (batch 1, top-8)"
 
 
@@ -360,7 +367,7 @@ def run_prefill(args, wl):
     gu = kernels["grouped_gate_up"]
     gu_flops = float(np.mean(2.0 * 16 * 2 * H * (tiles * I + shared_tiles * Is)))
     roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4), "traffic": traffic_for(wl.name, "k_gu_grouped"),
                 "kernel": "k_gu_grouped", "alg_bytes_per_launch": gu["alg_bytes_mean"],
                 "avg_launch_us": gu["avg_us"], "timing": "hipExtLaunchKernelGGL start/stop events",
                 "mfma_util": round(gu_flops / (gu["avg_us"] * 1e-6) / mfma_peak, 4)}
