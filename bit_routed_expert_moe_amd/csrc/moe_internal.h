@@ -39,7 +39,7 @@ struct RouteArgs {
     float* xK;               // [T][H/64]
     float* xX;               // [T][H/64]
     float* xinv;             // [T][H/64]
-    int H, E, k, prep;
+    int H, E, k, prep, T;
 };
 
 struct FfnArgs {
@@ -101,6 +101,9 @@ struct PrefillArgs {
     float* hinv;             // [P + T][Imax/64]
     float* eo;               // [T][k+1][H] per-slot expert outputs
     uint32_t* err;           // device error word
+    const int8_t* rq;        // router [E][H] (k_route_tiles)
+    const uint16_t* rs;      // router row scales [E] fp16
+    float* logits;           // [T][E] out (k_route_tiles)
     int H, E, I, Is, k, T, P, Imax, tile_cap, xparts;
 };
 

@@ -122,30 +122,21 @@ constexpr int kRouterChunksPerLane = kMaxHidden / 16 / 64;  // 16-byte chunks pe
 
 template <int XP, bool BF16>
 __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
-    const int t = blockIdx.y;
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kWaves + wave;
-    if (a.prep) {
-        for (int g = gw; g < a.H / 64; g += gridDim.x * kWaves)
-            prep_group<XP, BF16>(a.x, t, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+    const int rb = (a.E + kWaves * kRouterRowsPerWave - 1) / (kWaves * kRouterRowsPerWave);
+    if ((int)blockIdx.x >= rb) {  // activation preparation blocks (one token each)
+        const int g = ((int)blockIdx.x - rb) * kWaves + wave;
+        if (g < a.H / 64) prep_group<XP, BF16>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+        return;
     }
-    const int row0 = gw * kRouterRowsPerWave;
+    const int row0 = (blockIdx.x * kWaves + wave) * kRouterRowsPerWave;
     if (row0 >= a.E) return;
     const int nch = a.H / 16;
     constexpr int CPL = kRouterChunksPerLane;
     constexpr int XV = BF16 ? 2 : 4;  // 16-byte loads per 16 activations
     u32x4 xr[CPL][XV];
     u32x4 wr[kRouterRowsPerWave][CPL];
-    const u32x4* xb = (const u32x4*)((const uint8_t*)a.x + (size_t)t * a.H * (BF16 ? 2 : 4));
     const int ncl = (nch + 63) / 64;  // chunk rounds in use (uniform)
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        if (i < ncl) {
-            const int c = min(lane + 64 * i, nch - 1);
-#pragma unroll
-            for (int v = 0; v < XV; ++v) xr[i][v] = xb[c * XV + v];
-        }
-    }
 #pragma unroll
     for (int r = 0; r < kRouterRowsPerWave; ++r) {
         const int e = min(row0 + r, a.E - 1);
@@ -154,40 +145,52 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
         for (int i = 0; i < CPL; ++i)
             if (i < ncl) wr[r][i] = ldg_nt(row + min(lane + 64 * i, nch - 1));
     }
-#pragma unroll
-    for (int r = 0; r < kRouterRowsPerWave; ++r) {
-        const int e = row0 + r;
-        float acc = 0.0f;
+    {
+        const int t = blockIdx.y;
+        const u32x4* xb = (const u32x4*)((const uint8_t*)a.x + (size_t)t * a.H * (BF16 ? 2 : 4));
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
-            if (e < a.E && c < nch) {
-                float xf[16];
+            if (i < ncl) {
+                const int c = min(lane + 64 * i, nch - 1);
 #pragma unroll
-                for (int v = 0; v < XV; ++v) {
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const uint32_t word = xr[i][v][d];
-                        if (BF16) {
-                            xf[8 * v + 2 * d] = __builtin_bit_cast(float, word << 16);
-                            xf[8 * v + 2 * d + 1] = __builtin_bit_cast(float, word & 0xFFFF0000u);
-                        } else {
-                            xf[4 * v + d] = __builtin_bit_cast(float, word);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t q = wr[r][i][d];
-#pragma unroll
-                    for (int bsel = 0; bsel < 4; ++bsel)
-                        acc = fmaf((float)(int)(int8_t)(q >> (8 * bsel)), xf[4 * d + bsel], acc);
-                }
+                for (int v = 0; v < XV; ++v) xr[i][v] = xb[c * XV + v];
             }
         }
-        acc = wave_sum(acc);
-        if (lane == 0 && e < a.E)
-            a.logits[(size_t)t * a.E + e] = acc * (float)__builtin_bit_cast(_Float16, a.rs[e]);
+#pragma unroll
+        for (int r = 0; r < kRouterRowsPerWave; ++r) {
+            const int e = row0 + r;
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = lane + 64 * i;
+                if (e < a.E && c < nch) {
+                    float xf[16];
+#pragma unroll
+                    for (int v = 0; v < XV; ++v) {
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const uint32_t word = xr[i][v][d];
+                            if (BF16) {
+                                xf[8 * v + 2 * d] = __builtin_bit_cast(float, word << 16);
+                                xf[8 * v + 2 * d + 1] = __builtin_bit_cast(float, word & 0xFFFF0000u);
+                            } else {
+                                xf[4 * v + d] = __builtin_bit_cast(float, word);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t q = wr[r][i][d];
+#pragma unroll
+                        for (int bsel = 0; bsel < 4; ++bsel)
+                            acc = fmaf((float)(int)(int8_t)(q >> (8 * bsel)), xf[4 * d + bsel], acc);
+                    }
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0 && e < a.E)
+                a.logits[(size_t)t * a.E + e] = acc * (float)__builtin_bit_cast(_Float16, a.rs[e]);
+        }
     }
 }
 
@@ -545,10 +548,11 @@ __global__ void k_clear_word(uint32_t* p) { *p = 0u; }
 // ---------------------------------------------------------------------------
 // host-side launchers (called from moe_layer.hip)
 // ---------------------------------------------------------------------------
+// Router blocks, then (with a.prep) activation preparation blocks running
+// beside them, one token per block row.
 hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
     const int rpb = kWaves * kRouterRowsPerWave;
-    int nb = (a.E + rpb - 1) / rpb;
-    if (a.prep) nb = max(nb, (a.H / 64 + kWaves - 1) / kWaves);
+    const int nb = (a.E + rpb - 1) / rpb + (a.prep ? (a.H / 64 + kWaves - 1) / kWaves : 0);
     const dim3 grid(nb, T);
     if (act_bf16)
         launch_kernel(k_route<1, true>, grid, dim3(kBlock), 0, s, a);

@@ -22,6 +22,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
 hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s);
 hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_route_tiles(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
 }  // namespace moe
@@ -192,7 +193,7 @@ moe_status check_device_ptr(const void* p, const char* name) {
 }
 
 RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, uint8_t* ws,
-                     const WsLayout& o, int prep) {
+                     const WsLayout& o, int prep, int T) {
     RouteArgs a{};
     a.x = x;
     a.rq = L->w.router_q;
@@ -209,6 +210,7 @@ RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, 
     a.E = L->d.n_experts;
     a.k = L->d.top_k;
     a.prep = prep;
+    a.T = T;
     return a;
 }
 
@@ -290,40 +292,49 @@ PrefillArgs prefill_args(const moe_layer* L, const void* x, const int32_t* ids, 
     a.Imax = std::max(L->d.inter, L->d.shared_inter);
     a.tile_cap = o.tile_cap;
     a.xparts = L->xparts;
+    a.rq = L->w.router_q;
+    a.rs = L->w.router_scale;
+    a.logits = (float*)(ws + o.logits);
     return a;
 }
 
-moe_status grouped_ffn_chunk(const moe_layer* L, const PrefillArgs& pa, hipStream_t s) {
-    hipError_t e;
-    if ((e = timed(K_PF_PREP, s, [&] { return launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s); })) != hipSuccess)
-        return hip_fail(e, "prefill prep launch");
-    if ((e = timed(K_PF_GROUP, s, [&] { return launch_prefill_group(pa, s); })) != hipSuccess)
-        return hip_fail(e, "grouping launch");
-    if ((e = timed(K_PF_GATE_UP, s, [&] { return launch_prefill_gate_up(pa, s); })) != hipSuccess)
-        return hip_fail(e, "grouped gate/up launch");
-    if ((e = timed(K_PF_DOWN, s, [&] { return launch_prefill_down(pa, s); })) != hipSuccess)
-        return hip_fail(e, "grouped down launch");
-    return MOE_OK;
-}
-
-// The grouped path over T tokens in chunks.  expert_out given: per-slot outputs
-// written there; else each chunk's outputs go to the workspace and are combined
-// into y with w.
-moe_status grouped_ffn(const moe_layer* L, const void* x, int T, const int32_t* ids, const float* w,
-                       float* y, float* expert_out, uint8_t* ws, const WsLayout& o, hipStream_t s) {
+// The grouped path over T tokens in chunks.  With `route`, each chunk is
+// routed first (prepared activations -> router tiles -> top-k into ids, w);
+// with `ffn`, the experts run: expert_out given -> per-slot outputs written
+// there; else each chunk's outputs go to the workspace and are combined into
+// y with w.
+moe_status grouped_ffn(const moe_layer* L, const void* x, int T, int32_t* ids, float* w, float* y,
+                       float* expert_out, uint8_t* ws, const WsLayout& o, hipStream_t s, bool route,
+                       bool ffn) {
     const int H = L->d.hidden, k = L->d.top_k, C = grouped_chunk(L);
     const size_t esz = L->d.act_dtype == MOE_BF16 ? 2 : 4;
+    hipError_t e;
     for (int c0 = 0; c0 < T; c0 += C) {
         const int Tc = std::min(C, T - c0);
         const void* xc = (const uint8_t*)x + (size_t)c0 * H * esz;
-        const int32_t* ic = ids + (size_t)c0 * k;
+        int32_t* ic = ids + (size_t)c0 * k;
         float* eo = expert_out ? expert_out + (size_t)c0 * (k + 1) * H : (float*)(ws + o.eo);
-        moe_status st = grouped_ffn_chunk(L, prefill_args(L, xc, ic, ws, o, Tc, eo), s);
-        if (st != MOE_OK) return st;
+        const PrefillArgs pa = prefill_args(L, xc, ic, ws, o, Tc, eo);
+        if ((e = timed(K_PF_PREP, s, [&] { return launch_prefill_prep(pa, L->d.act_dtype == MOE_BF16, s); })) != hipSuccess)
+            return hip_fail(e, "prefill prep launch");
+        if (route) {
+            if ((e = timed(K_ROUTE, s, [&] { return launch_route_tiles(pa, s); })) != hipSuccess)
+                return hip_fail(e, "router launch");
+            RouteArgs ra = route_args(L, xc, ic, w + (size_t)c0 * k, ws, o, 0, Tc);
+            if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, Tc, s); })) != hipSuccess)
+                return hip_fail(e, "top-k launch");
+        }
+        if (!ffn) continue;
+        if ((e = timed(K_PF_GROUP, s, [&] { return launch_prefill_group(pa, s); })) != hipSuccess)
+            return hip_fail(e, "grouping launch");
+        if ((e = timed(K_PF_GATE_UP, s, [&] { return launch_prefill_gate_up(pa, s); })) != hipSuccess)
+            return hip_fail(e, "grouped gate/up launch");
+        if ((e = timed(K_PF_DOWN, s, [&] { return launch_prefill_down(pa, s); })) != hipSuccess)
+            return hip_fail(e, "grouped down launch");
         if (!expert_out) {
             CombineArgs ca{eo, w + (size_t)c0 * k, y + (size_t)c0 * H, H, k, Tc, 0};
-            hipError_t e = timed(K_COMBINE, s, [&] { return launch_combine(ca, s); });
-            if (e != hipSuccess) return hip_fail(e, "combine launch");
+            if ((e = timed(K_COMBINE, s, [&] { return launch_combine(ca, s); })) != hipSuccess)
+                return hip_fail(e, "combine launch");
         }
     }
     return MOE_OK;
@@ -542,8 +553,10 @@ moe_status moe_route_topk(moe_layer_t L, const void* x, int32_t T, int32_t* ids,
     if (st != MOE_OK) return st;
     if (!ids || !w) return fail(MOE_ERR_ARG, "null ids or w");
     const WsLayout o = ws_layout(L, T);
-    RouteArgs a = route_args(L, x, ids, w, (uint8_t*)workspace, o, 0);
     hipStream_t s = (hipStream_t)stream;
+    if (T >= kPrefillMinTokens)  // the grouped path's router (MFMA tiles), as the forward call
+        return grouped_ffn(L, x, T, ids, w, nullptr, nullptr, (uint8_t*)workspace, o, s, true, false);
+    RouteArgs a = route_args(L, x, ids, w, (uint8_t*)workspace, o, 0, T);
     hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(a, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "router launch");
     e = timed(K_TOPK, s, [&] { return launch_topk(a, T, s); });
@@ -560,9 +573,10 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
     if (T >= kPrefillMinTokens) {
-        return grouped_ffn(L, x, T, ids, nullptr, nullptr, expert_out, ws, o, s);
+        return grouped_ffn(L, x, T, const_cast<int32_t*>(ids), nullptr, nullptr, expert_out, ws, o, s,
+                           false, true);
     }
-    RouteArgs ra = route_args(L, x, nullptr, nullptr, ws, o, 1);
+    RouteArgs ra = route_args(L, x, nullptr, nullptr, ws, o, 1, T);
     hipError_t e = timed(K_PREP, s, [&] { return launch_prep(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "prep launch");
     FfnArgs fa = ffn_args(L, ids, nullptr, ws, o, nullptr, expert_out, false);
@@ -593,14 +607,10 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
-    RouteArgs ra = route_args(L, x, ids, w, ws, o, T >= kPrefillMinTokens ? 0 : 1);
+    if (T >= kPrefillMinTokens) return grouped_ffn(L, x, T, ids, w, y, nullptr, ws, o, s, true, true);
+    RouteArgs ra = route_args(L, x, ids, w, ws, o, 1, T);
     hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "router launch");
-    if (T >= kPrefillMinTokens) {
-        if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
-            return hip_fail(e, "top-k launch");
-        return grouped_ffn(L, x, T, ids, w, y, nullptr, ws, o, s);
-    }
     if (L->cache.n_slots) {
         if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
             return hip_fail(e, "top-k launch");

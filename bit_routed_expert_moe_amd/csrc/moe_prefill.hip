@@ -47,10 +47,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kNtGu = 8;  // MFMA N-tiles per wave in k_gu_grouped (64 rows of I, gate + up)
-constexpr int kNtDn = 4;  // MFMA N-tiles per wave in k_down_grouped (64 outputs)
+constexpr int kNtDn = 8;  // MFMA N-tiles per wave in k_down_grouped (128 outputs)
 constexpr int kAuxNT = 2; // buffer-load cache policy: nontemporal
 constexpr int kGuDepth = 2;  // 64-input groups in flight per wave, k_gu_grouped
-constexpr int kDnDepth = 4;  // 64-input groups in flight per wave, k_down_grouped
+constexpr int kDnDepth = 2;  // 64-input groups in flight per wave, k_down_grouped
+// Scalar offset for ring refills past a wave's last group: with any per-lane
+// offset (< 2^28 in a record) the sum lies beyond every record (records are
+// under 2^28 bytes) without wrapping 32 bits, so the buffer load is dropped
+// (returns 0, no memory traffic) instead of fetching a group again.
+constexpr int kPastEnd = 0x7FFFF000;
 
 // slot of input p (0..7) within its 8: inverse of (0,4,1,5,2,6,3,7)
 __device__ __forceinline__ int slot_of(int p) { return p < 4 ? 2 * p : 2 * (p - 4) + 1; }
@@ -139,15 +144,40 @@ __device__ __forceinline__ float row16_sum(float v) {
 // ---------------------------------------------------------------------------
 template <int XP, bool BF16>
 __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
+    __shared__ float row[kMaxHidden];
     __shared__ float red4[kWaves];
     const int t = blockIdx.x, H = a.H, NG = H / 64;
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    auto load = [&](int i) {
-        const size_t gi = (size_t)t * H + i;
-        return BF16 ? bf16_to_f32(((const uint16_t*)a.x)[gi]) : ((const float*)a.x)[gi];
-    };
+    // the token's row into LDS with 16-byte loads, and its largest magnitude
     float mx = 0.0f;
-    for (int i = threadIdx.x; i < H; i += kBlock) mx = fmaxf(mx, fabsf(load(i)));
+    constexpr int PER = BF16 ? 8 : 4;                 // values per 16-byte load
+    constexpr int NV = kMaxHidden / PER / kBlock;     // loads per thread at the largest hidden size
+    const u32x4* src = (const u32x4*)((const uint8_t*)a.x + (size_t)t * H * (BF16 ? 2 : 4));
+    u32x4 w[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {  // every load issued before the first wait
+        w[j] = src[min((int)threadIdx.x + j * kBlock, H / PER - 1)];  // past the row: a repeat, unused
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int v = threadIdx.x + j * kBlock;
+        if (v >= H / PER) break;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t u = w[j][d];  // bit-cast a scalar copy, never a vector element lvalue
+            if (BF16) {
+                const float f0 = __builtin_bit_cast(float, u << 16);
+                const float f1 = __builtin_bit_cast(float, u & 0xFFFF0000u);
+                row[v * 8 + 2 * d] = f0;
+                row[v * 8 + 2 * d + 1] = f1;
+                mx = fmaxf(mx, fmaxf(fabsf(f0), fabsf(f1)));
+            } else {
+                const float f = __builtin_bit_cast(float, u);
+                row[v * 4 + d] = f;
+                mx = fmaxf(mx, fabsf(f));
+            }
+        }
+    }
     mx = wave_max(mx);
     if (lane == 0) red4[wave] = mx;
     __syncthreads();
@@ -156,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
     const float sc = ldexpf(1.0f, e);
     const int p = lane & 7;
     for (int g = wave; g < NG; g += kWaves) {
-        const float vs = load(64 * g + lane) * sc;  // exact: a power-of-two scaling
+        const float vs = row[64 * g + lane] * sc;  // exact: a power-of-two scaling
         const float vq = vs * ((p & 1) ? 0.0625f : 1.0f);
         const uint16_t hi = f16bits(vq);
         const size_t dst = (size_t)t * H + 64 * g + (lane & ~7) + slot_of(p);
@@ -169,64 +199,193 @@ __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_route_tiles: router logits of many tokens.  Grid (ceil(E/16), ceil(T/16)),
+// 256 threads; the workgroup computes a 16-token x 16-expert tile, wave w over
+// the 32-input chunks [w*C/4, (w+1)*C/4), the four partial sums added in a
+// fixed order.  A = the prepared fp16 activations (slot order, odd inputs / 16,
+// token scale 2^e); B = the int8 router bytes turned into fp16 in the same slot
+// order with odd inputs x16: byte b + 128 in the mantissa of 1024.0 (or of
+// 16384.0, where one mantissa step is 16) minus 1152 (or 18432) is b (or 16 b)
+// exactly.  Products are exact in fp32; logit = sum * 2^-e * scale.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ half8 router_b(uint32_t lo4, uint32_t hi4) {
+    const uint32_t u0 = lo4 ^ 0x80808080u, u1 = hi4 ^ 0x80808080u;  // bytes b + 128
+    // inputs (0,4) (1,5) (2,6) (3,7) into the low bytes of two halves
+    const uint32_t d0 = __builtin_amdgcn_perm(u1, u0, 0x0C040C00u);
+    const uint32_t d1 = __builtin_amdgcn_perm(u1, u0, 0x0C050C01u);
+    const uint32_t d2 = __builtin_amdgcn_perm(u1, u0, 0x0C060C02u);
+    const uint32_t d3 = __builtin_amdgcn_perm(u1, u0, 0x0C070C03u);
+    const half2v o1 = {(_Float16)1152.0f, (_Float16)1152.0f}, o16 = {(_Float16)18432.0f, (_Float16)18432.0f};
+    const half2v p0 = __builtin_bit_cast(half2v, d0 | 0x64006400u) - o1;   // b0, b4
+    const half2v p1 = __builtin_bit_cast(half2v, d1 | 0x74007400u) - o16;  // 16 b1, 16 b5
+    const half2v p2 = __builtin_bit_cast(half2v, d2 | 0x64006400u) - o1;   // b2, b6
+    const half2v p3 = __builtin_bit_cast(half2v, d3 | 0x74007400u) - o16;  // 16 b3, 16 b7
+    half8 o;
+    o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+    o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+    return o;
+}
+
+template <int XP>
+__global__ __launch_bounds__(kBlock) void k_route_tiles(PrefillArgs a) {
+    __shared__ float red[kWaves][kTileRows][kTileRows + 1];
+    const int H = a.H, nch = H / 32;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int n = lane & 15, kq = lane >> 4;
+    const int e0 = blockIdx.x * kTileRows, t0 = blockIdx.y * kTileRows;
+    const int c0 = wave * nch / kWaves, c1 = (wave + 1) * nch / kWaves;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(a.x16, (size_t)XP * a.T * H * 2);
+    const __amdgpu_buffer_rsrc_t rr = rsrc(a.rq, (size_t)a.E * H);
+    const int xpart = a.T * H * 2;
+    const int xo = (min(t0 + n, a.T - 1) * H + 8 * kq) * 2;  // rows past T compute on token T-1; discarded
+    const int ro = min(e0 + n, a.E - 1) * H + 8 * kq;
+    constexpr int D = 8;  // chunks in flight per wave
+    u32x4 A[D][XP];
+    uint32_t B[D][2];
+    auto load = [&](int q, int c) {
+        const int cc = min(c, c1 - 1);
+#pragma unroll
+        for (int p = 0; p < XP; ++p) A[q][p] = bload4(rx, xo, p * xpart + 64 * cc);
+        B[q][0] = bload(rr, ro, 32 * cc);
+        B[q][1] = bload(rr, ro + 4, 32 * cc);
+    };
+    f32x4 acc = {0, 0, 0, 0};
+    if (c1 > c0) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            load(q, c0 + q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int cb = c0; cb < c1; cb += D) {
+#pragma unroll
+            for (int q = 0; q < D; ++q) {
+                if (cb + q < c1) {
+                    const half8 b = router_b(B[q][0], B[q][1]);
+#pragma unroll
+                    for (int p = 0; p < XP; ++p) acc = mfma(A[q][p], b, acc);
+                }
+                load(q, cb + q + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][n] = acc[r];
+    __syncthreads();
+    const int m = threadIdx.x >> 4, ei = threadIdx.x & 15;  // token m, expert ei of the tile
+    const int t = t0 + m, e = e0 + ei;
+    if (t < a.T && e < a.E) {
+        const float v = ((red[0][m][ei] + red[1][m][ei]) + red[2][m][ei]) + red[3][m][ei];
+        a.logits[(size_t)t * a.E + e] = v * a.xinv[t] * (float)__builtin_bit_cast(_Float16, a.rs[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_group: one workgroup of 256 threads.
 // tiles[i] = {expert (or -1 = shared), first row, rows, 0}; rows of a routed
 // tile are positions in the expert-sorted pair list, rows of a shared tile are
 // tokens.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_group(PrefillArgs a) {
+    constexpr int R = 16;  // pair ids loaded per thread per batch (kBlock * R pairs in one round trip)
     __shared__ int hist[kMaxExperts];
-    __shared__ int offs[kMaxExperts + 1];
+    __shared__ int offs[kMaxExperts + 1];       // exclusive prefix sums of hist
+    __shared__ int tile_base[kMaxExperts + 1];  // exclusive prefix sums of the tile counts
     __shared__ int running[kMaxExperts];
     __shared__ int chunk_e[kBlock];
-    __shared__ int tile_base[kMaxExperts + 1];
+    __shared__ int scan[2][kBlock];
     const int E = a.E, P = a.T * a.k, tid = threadIdx.x;
     for (int e = tid; e < E; e += kBlock) {
         hist[e] = 0;
         running[e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kBlock) {
-        int e = a.ids[p];
-        if (e < 0 || e >= E) {  // flagged; the slot's output is poisoned by k_down_grouped
-            atomicOr(a.err, 1u);
-            e = 0;
+    auto load_ids = [&](int base, int* v) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int p = base + tid + kBlock * i;
+            v[i] = p < P ? a.ids[p] : 0;
         }
-        atomicAdd(&hist[e], 1);
+    };
+    for (int base = 0; base < P; base += kBlock * R) {
+        int v[R];
+        load_ids(base, v);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            if (base + tid + kBlock * i >= P) continue;
+            int e = v[i];
+            if (e < 0 || e >= E) {  // flagged; the slot's output is poisoned by k_down_grouped
+                atomicOr(a.err, 1u);
+                e = 0;
+            }
+            atomicAdd(&hist[e], 1);
+        }
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0, tiles = 0;
-        for (int e = 0; e < E; ++e) {
-            offs[e] = run;
-            run += hist[e];
-            tile_base[e] = tiles;
-            tiles += (hist[e] + kTileRows - 1) / kTileRows;
+    // exclusive prefix sums of the pair and tile counts: thread tid owns
+    // experts [4 tid, 4 tid + 4), a Hillis-Steele scan over the threads
+    int pc[4], tc[4], ps = 0, ts = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        pc[j] = e < E ? hist[e] : 0;
+        tc[j] = (pc[j] + kTileRows - 1) / kTileRows;
+        ps += pc[j];
+        ts += tc[j];
+    }
+    scan[0][tid] = ps;
+    scan[1][tid] = ts;
+    __syncthreads();
+    for (int d = 1; d < kBlock; d <<= 1) {
+        const int p0 = tid >= d ? scan[0][tid - d] : 0, t0 = tid >= d ? scan[1][tid - d] : 0;
+        __syncthreads();
+        scan[0][tid] += p0;
+        scan[1][tid] += t0;
+        __syncthreads();
+    }
+    int po = scan[0][tid] - ps, to = scan[1][tid] - ts;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        if (e < E) {
+            offs[e] = po;
+            tile_base[e] = to;
         }
-        offs[E] = run;
-        tile_base[E] = tiles;
+        po += pc[j];
+        to += tc[j];
+    }
+    if (tid == kBlock - 1) {
+        offs[E] = scan[0][tid];
+        tile_base[E] = scan[1][tid];
     }
     __syncthreads();
-    // stable scatter, 256 pairs at a time
-    for (int p0 = 0; p0 < P; p0 += kBlock) {
-        const int p = p0 + tid;
-        int e = -1;
-        if (p < P) {
-            e = a.ids[p];
-            e = (e < 0 || e >= E) ? 0 : e;
+    // stable scatter, kBlock pairs at a time
+    for (int base = 0; base < P; base += kBlock * R) {
+        int v[R];
+        load_ids(base, v);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int p0 = base + kBlock * i;
+            if (p0 >= P) break;  // uniform
+            const int p = p0 + tid;
+            int e = -1;
+            if (p < P) {
+                e = v[i];
+                e = (e < 0 || e >= E) ? 0 : e;
+            }
+            chunk_e[tid] = e;
+            __syncthreads();
+            if (p < P) {
+                int rank = 0;
+                for (int q = 0; q < tid; ++q) rank += chunk_e[q] == e;
+                const int pos = offs[e] + running[e] + rank;
+                a.pair_tok[pos] = p / a.k;
+                a.pair_slot[pos] = p % a.k;
+            }
+            __syncthreads();
+            if (p < P) atomicAdd(&running[e], 1);
+            __syncthreads();
         }
-        chunk_e[tid] = e;
-        __syncthreads();
-        if (p < P) {
-            int rank = 0;
-            for (int q = 0; q < tid; ++q) rank += chunk_e[q] == e;
-            const int pos = offs[e] + running[e] + rank;
-            a.pair_tok[pos] = p / a.k;
-            a.pair_slot[pos] = p % a.k;
-        }
-        __syncthreads();
-        if (p < P) atomicAdd(&running[e], 1);
-        __syncthreads();
     }
     // tiles
     for (int e = tid; e < E; e += kBlock) {
@@ -314,17 +473,20 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
             u32x4 W[2][2];  // [GU tile][chunk], rows 16*kq + n
             uint32_t SB[2];
         };
-        auto load = [&](Regs& R, int jg) {
+        auto load = [&](Regs& R, int jg) {  // jg >= j1: a refill past the end
+            const bool live = jg < j1;
+            const int ja = min(jg, j1 - 1);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int p = 0; p < XP; ++p) R.A[c][p] = bload4(rx, xo, p * xpart + 128 * jg + 64 * c);
+                for (int p = 0; p < XP; ++p) R.A[c][p] = bload4(rx, xo, p * xpart + 128 * ja + 64 * c);
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], 2048 * jg + 1024 * c);
+                for (int c = 0; c < 2; ++c)
+                    R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], live ? 2048 * jg + 1024 * c : kPastEnd);
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) R.SB[t2] = bload(rw, so[t2], 256 * jg);
+            for (int t2 = 0; t2 < 2; ++t2) R.SB[t2] = bload(rw, so[t2], live ? 256 * jg : kPastEnd);
         };
         auto compute = [&](const Regs& R, int jg) {
             const f32x4 xs = *(const f32x4*)&sX[jg * kTileRows + 4 * kq];
@@ -347,19 +509,18 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
                 }
             }
         };
-        // ring of kGuDepth groups in flight; refills are clamped to the last
-        // group (re-reads of it are cache hits)
+        // ring of kGuDepth groups in flight
         Regs R[kGuDepth];
 #pragma unroll
         for (int q = 0; q < kGuDepth; ++q) {
-            load(R[q], min(j0 + q, j1 - 1));
+            load(R[q], j0 + q);
             __builtin_amdgcn_sched_barrier(0);
         }
         for (int jb = j0; jb < j1; jb += kGuDepth) {
 #pragma unroll
             for (int q = 0; q < kGuDepth; ++q) {
                 if (jb + q < j1) compute(R[q], jb + q);
-                load(R[q], min(jb + q + kGuDepth, j1 - 1));
+                load(R[q], jb + q + kGuDepth);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -414,8 +575,9 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_down_grouped: grid (tile capacity, ceil(H/256)), 256 threads.  Wave w:
-// outputs o0 = 256*blockIdx.y + 64w + [0, 64) (N-tiles of 16) over all of I.
+// k_down_grouped: grid (tile capacity, ceil(H/512)), 256 threads.  Wave w:
+// outputs o0 = 512*blockIdx.y + 128w + [0, 128) (two 64-row halves of N-tiles
+// of 16) over all of I; a wave visit reads 2 KB of contiguous record bytes.
 // Dynamic LDS: [Ie/64][16] group sums of h, then [Ie/64][16] 2^-e of h.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
@@ -440,12 +602,13 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
         if (jg == 0) s_row[m] = row;
     }
     __syncthreads();
-    const int o0 = 256 * blockIdx.y + 64 * wave;
+    const int o0 = 512 * blockIdx.y + 128 * wave;
     if (o0 >= H) return;
+    const bool hi_ok = o0 + 128 <= H;  // the second 64-row half exists (H is a multiple of 64)
     const uint8_t* rec = shared ? a.shared : a.experts + (size_t)tl.x * a.rec_bytes;
     const __amdgpu_buffer_rsrc_t rw = rsrc(rec, shared ? a.rec_bytes_shared : a.rec_bytes);
     const __amdgpu_buffer_rsrc_t rh = rsrc(a.h16, (size_t)(a.P + a.T) * a.Imax * 2);
-    // lane row o0 + 16*kq + n: one 16-byte load covers the wave's 64 rows of a
+    // lane row o0 + 64*hh + 16*kq + n: one 16-byte load covers 64 rows of a
     // down chunk, one dword load their scale/bias pairs
     const int rl = o0 + 16 * kq + n;
     const int wo = 32 * H + rl * 16;
@@ -457,42 +620,52 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     for (int nt = 0; nt < kNtDn; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
     struct Regs {
         u32x4 A[2];
-        u32x4 W[2];
-        uint32_t SB;
+        u32x4 W[2][2];  // [half][chunk]
+        uint32_t SB[2];
     };
-    auto load = [&](Regs& R, int jg) {
+    auto load = [&](Regs& R, int jg) {  // jg >= NGe: a refill past the end
+        const int ja = min(jg, NGe - 1);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) R.A[c] = bload4(rh, ho, 128 * jg + 64 * c);
+        for (int c = 0; c < 2; ++c) R.A[c] = bload4(rh, ho, 128 * ja + 64 * c);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) R.W[c] = bload4<kAuxNT>(rw, wo, 48 * H * (2 * jg + c));
-        R.SB = bload(rw, so, 12 * H * jg);
+        for (int hh = 0; hh < 2; ++hh) {
+            const bool live = jg < NGe && (hh == 0 || hi_ok);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                R.W[hh][c] = bload4<kAuxNT>(rw, wo, live ? 48 * H * (2 * jg + c) + 1024 * hh : kPastEnd);
+            R.SB[hh] = bload(rw, so, live ? 12 * H * jg + 256 * hh : kPastEnd);
+        }
     };
     auto compute = [&](const Regs& R, int jg) {
         const f32x4 hi = *(const f32x4*)&sHi[jg * kTileRows + 4 * kq];
         const f32x4 hsum = *(const f32x4*)&sH[jg * kTileRows + 4 * kq];
-        const u32x4 w0 = xpose4(R.W[0]), w1 = xpose4(R.W[1]);
-        const u32x4 sb = bcast4(R.SB);
 #pragma unroll
-        for (int nt = 0; nt < kNtDn; ++nt) {
-            f32x4 pd = {0, 0, 0, 0};
-            pd = mfma(R.A[0], up.codes(w0[nt]), pd);
-            pd = mfma(R.A[1], up.codes(w1[nt]), pd);
-            const float sd = f16lo(sb[nt]), bd = f16hi(sb[nt]);
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 w0 = xpose4(R.W[hh][0]), w1 = xpose4(R.W[hh][1]);
+            const u32x4 sb = bcast4(R.SB[hh]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[nt][r] = fmaf(bd, hsum[r], fmaf(sd, pd[r] * hi[r], acc[nt][r]));
+            for (int t = 0; t < 4; ++t) {
+                const int nt = 4 * hh + t;
+                f32x4 pd = {0, 0, 0, 0};
+                pd = mfma(R.A[0], up.codes(w0[t]), pd);
+                pd = mfma(R.A[1], up.codes(w1[t]), pd);
+                const float sd = f16lo(sb[t]), bd = f16hi(sb[t]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[nt][r] = fmaf(bd, hsum[r], fmaf(sd, pd[r] * hi[r], acc[nt][r]));
+            }
         }
     };
     Regs R[kDnDepth];
 #pragma unroll
     for (int q = 0; q < kDnDepth; ++q) {
-        load(R[q], min(q, NGe - 1));
+        load(R[q], q);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int jb = 0; jb < NGe; jb += kDnDepth) {
 #pragma unroll
         for (int q = 0; q < kDnDepth; ++q) {
             if (jb + q < NGe) compute(R[q], jb + q);
-            load(R[q], min(jb + q + kDnDepth, NGe - 1));
+            load(R[q], jb + q + kDnDepth);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -513,7 +686,8 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
         }
         float* dst = a.eo + ((size_t)t * (a.k + 1) + j) * H + o0 + n;
 #pragma unroll
-        for (int nt = 0; nt < kNtDn; ++nt) dst[16 * nt] = bad ? __builtin_nanf("") : acc[nt][r];
+        for (int nt = 0; nt < kNtDn; ++nt)
+            if (nt < 4 || hi_ok) dst[16 * nt] = bad ? __builtin_nanf("") : acc[nt][r];
     }
 }
 
@@ -535,6 +709,15 @@ hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s
     return hipGetLastError();
 }
 
+hipError_t launch_route_tiles(const PrefillArgs& a, hipStream_t s) {
+    const dim3 grid((a.E + kTileRows - 1) / kTileRows, (a.T + kTileRows - 1) / kTileRows);
+    if (a.xparts == 1)
+        launch_kernel(k_route_tiles<1>, grid, dim3(kBlock), 0, s, a);
+    else
+        launch_kernel(k_route_tiles<2>, grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s) {
     launch_kernel(k_group, dim3(1), dim3(kBlock), 0, s, a);
     return hipGetLastError();
@@ -552,7 +735,7 @@ hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s) {
     const size_t lds = (size_t)(a.Imax / 64) * kTileRows * 8;
-    launch_kernel(k_down_grouped, dim3(a.tile_cap, (a.H + 255) / 256), dim3(kBlock), lds, s, a);
+    launch_kernel(k_down_grouped, dim3(a.tile_cap, (a.H + 511) / 512), dim3(kBlock), lds, s, a);
     if (!a.Is) launch_kernel(k_zero_shared_rows, dim3((a.H + kBlock - 1) / kBlock, a.T), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
