@@ -550,9 +550,9 @@ def main():
             run_step(s)
 
     recs = kernel_timed_pass(profiled_steps, P * L * 4 + 64)
-    kbytes = {"route": T * (E * H + 2 * E),
-              "gate_up": T * (k * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0)),
-              "down_combine": T * (k * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0))}
+    kb_gu = T * (k * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0))
+    kb_dn = T * (k * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0))
+    kbytes = {"route": T * (E * H + 2 * E), "gate_up": kb_gu, "down_combine": kb_dn}
     kernels = {}
     for name in sorted({r[0] for r in recs}):
         ms = np.array([m for n_, m in recs if n_ == name])
@@ -563,11 +563,12 @@ def main():
             ent["alg_bytes"] = int(kbytes[name])
             ent["gbps"] = round(kbytes[name] / (net * 1e-3) / 1e9, 1)
         kernels[name] = ent
+    kfn = "k_gate_up"
     gu = kernels["gate_up"]
     roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(wl.name, "k_gate_up"),
-                "kernel": "k_gate_up", "alg_bytes_per_launch": gu["alg_bytes"],
+                "traffic": traffic_for(wl.name, kfn),
+                "kernel": kfn, "alg_bytes_per_launch": gu["alg_bytes"],
                 "avg_launch_us": gu["avg_us"], "timing": "hipExtLaunchKernelGGL start/stop events"}
 
     cpu = None

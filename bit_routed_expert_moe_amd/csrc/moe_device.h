@@ -131,45 +131,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
-// Max of 64-bit unsigned keys over all 64 lanes; every lane gets the result.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#define MOE_MAX_STEP(CTRL)                                                          \
-    {                                                                               \
-        const uint64_t o = (uint64_t)dpp_u32<CTRL>((uint32_t)v) |                   \
-                           ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32);    \
-        v = o > v ? o : v;                                                          \
-    }
-    MOE_MAX_STEP(0xB1)
-    MOE_MAX_STEP(0x4E)
-    MOE_MAX_STEP(0x124)
-    MOE_MAX_STEP(0x128)
-#undef MOE_MAX_STEP
-    uint64_t m = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint64_t o = (uint64_t)readlane_u32((uint32_t)v, 16 * r) |
-                           ((uint64_t)readlane_u32((uint32_t)(v >> 32), 16 * r) << 32);
-        m = o > m ? o : m;
-    }
-    return m;
-}
-
-// Sort key of (logit, id): larger logit first, then lower id.  -0 is folded
-// into +0 so equal logits compare equal.
-__device__ __forceinline__ uint64_t topk_key(float v, int id) {
-    uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
-}
-__device__ __forceinline__ float topk_key_value(uint64_t key) {
-    uint32_t u = (uint32_t)(key >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-    return __builtin_bit_cast(float, u);
-}
-__device__ __forceinline__ int topk_key_id(uint64_t key) {
-    return (int)(0xFFFFFFFFu - (uint32_t)key);
-}
-
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

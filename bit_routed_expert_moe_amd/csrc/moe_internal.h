@@ -63,6 +63,7 @@ struct FfnArgs {
     float* hHs;              // [T][k+1][blk_max]
     float* hinv;             // [T][k+1][blk_max]
     float* dpart;            // [T][n_otiles][n_items][64]
+    int n_units;             // k*blk_r + blk_s
     uint32_t* dctr;          // [T][n_otiles][kCounterStride]
     float* y;                // [T][H] fused output (or nullptr)
     float* eo;               // [T][k+1][H] per-expert outputs (or nullptr)

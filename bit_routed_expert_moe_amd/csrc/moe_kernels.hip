@@ -66,53 +66,103 @@ __device__ void prep_group(const void* x, int t, int H, int g, uint32_t* pairs, 
 }
 
 // ---------------------------------------------------------------------------
-// exact top-k over E <= 1024 logits by one wave, then the renormalised softmax
-// gates.  Order: logit descending, ties to the lower id.
+// exact top-k over E <= 64*Q logits, then the renormalised softmax gates.
+// Order: logit descending, ties to the lower id.  Every wave of the
+// workgroup computes the selection (no wave waits on another's arithmetic);
+// all threads must call it (it synchronises the workgroup).
+//   1. order-preserving 32-bit keys u (larger logit -> larger u);
+//   2. radix select, most significant bit first: T = the largest value with
+//      #{u >= T} >= k (32 steps of one compare per key slot, a ballot and a
+//      scalar popcount);
+//   3. the selection = every key above T plus the lowest ids among the keys
+//      equal to T, as many as are needed;
+//   4. its order: each selected key counts the selected keys ahead of it
+//      (k rounds, the round's key broadcast with readlane).
+// Wave 0 leaves ids and logits in rank order in LDS; returns the id of rank
+// `want` (if >= 0).  ids_out / w_out (workgroup-uniform) get the selection
+// and the gates.
 // ---------------------------------------------------------------------------
-template <int Q>  // key slots per lane: E <= 64 * Q
-__device__ void topk_softmax_wave(const float* lg, int E, int k, int32_t* ids_out, float* w_out,
-                                  int want = -1, int* want_id = nullptr) {
+struct TopkScratch {
+    int sel[kMaxTopK];
+    float val[kMaxTopK];
+};
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);  // -0 -> +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <int Q>
+__device__ int topk_select(const float* lg, int E, int k, int want, TopkScratch& sm, int32_t* ids_out,
+                           float* w_out) {
     const int lane = threadIdx.x & 63;
-    uint64_t key[Q];
-    const int nq = (E + 63) / 64;
-    // all loads first, unconditionally (clamped index), keys afterwards: one round trip
     float lv[Q];
+    uint32_t u[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) lv[q] = lg[min(lane + 64 * q, E - 1)];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        key[q] = (q < nq && e < E) ? topk_key(lv[q], e) : 0;  // 0 sorts below every real key
-    }
-    float sel_l = 0.0f;
-    int sel_id = 0;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
+    for (int q = 0; q < Q; ++q) u[q] = lane + 64 * q < E ? order_key(lv[q]) : 0u;  // 0: below every key
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int c = 0;
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-            if (q < nq) best = key[q] > best ? key[q] : best;
-        const uint64_t m = wave_max_u64(best);
-        const int id = topk_key_id(m);
-        if ((id & 63) == lane) {
+        for (int q = 0; q < Q; ++q) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(u[q] >= cand));
+        if (c >= k) T = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(u[q] > T));
+    const int need = k - gt;  // keys equal to T to take, lowest ids first
+    uint64_t selm[Q];
+    int before = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const uint64_t eqm = __builtin_amdgcn_ballot_w64(u[q] == T && lane + 64 * q < E);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
+        const bool take = u[q] > T || ((eqm >> lane) & 1 && before + below < need);
+        selm[q] = __builtin_amdgcn_ballot_w64(take);
+        before += __builtin_popcountll(eqm);
+    }
+    // rank of each selected key = selected keys ahead of it (larger u, or equal u and lower id)
+    int rank[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) rank[q] = 0;
+#pragma unroll
+    for (int q2 = 0; q2 < Q; ++q2) {
+        uint64_t m = selm[q2];
+        while (m) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t ul = (uint32_t)__builtin_amdgcn_readlane((int)u[q2], l);
+            const int idl = l + 64 * q2;
 #pragma unroll
             for (int q = 0; q < Q; ++q)
-                if (q == (id >> 6)) key[q] = 0;
-        }
-        if (lane == j) {
-            sel_l = topk_key_value(m);
-            sel_id = id;
+                rank[q] += (ul > u[q] || (ul == u[q] && idl < lane + 64 * q)) ? 1 : 0;
         }
     }
-    if (want_id && lane == want) *want_id = sel_id;
-    if (!ids_out) return;
-    const float m = __shfl(sel_l, 0, 64);  // the first pick is the largest
-    const float ex = lane < k ? expf(sel_l - m) : 0.0f;
-    float z = 0.0f;
-    for (int j = 0; j < k; ++j) z += __shfl(ex, j, 64);
-    if (lane < k) {
-        ids_out[lane] = sel_id;
-        w_out[lane] = ex / z;
+    if (threadIdx.x < 64) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if ((selm[q] >> lane) & 1) {
+                sm.sel[rank[q]] = lane + 64 * q;
+                sm.val[rank[q]] = lv[q];
+            }
+        }
     }
+    __syncthreads();
+    if (ids_out && threadIdx.x < 64) {
+        const float sel_l = lane < k ? sm.val[lane] : 0.0f;
+        const float mx = __shfl(sel_l, 0, 64);  // rank 0 is the largest
+        const float ex = lane < k ? expf(sel_l - mx) : 0.0f;
+        float z = 0.0f;
+        for (int j = 0; j < k; ++j) z += __shfl(ex, j, 64);
+        if (lane < k) {
+            ids_out[lane] = sm.sel[lane];
+            w_out[lane] = ex / z;
+        }
+    }
+    return want >= 0 ? sm.sel[want] : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -194,12 +244,12 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
     }
 }
 
-// k_topk: grid (T), one wave: ids/w from the logits written by k_route.
+// k_topk: grid (T), one wave per token: ids/w from the logits.
 template <int Q>
 __global__ __launch_bounds__(64) void k_topk(RouteArgs a) {
+    __shared__ TopkScratch sm;
     const int t = blockIdx.x;
-    topk_softmax_wave<Q>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k,
-                         a.w + (size_t)t * a.k);
+    topk_select<Q>(a.logits + (size_t)t * a.E, a.E, a.k, -1, sm, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k);
 }
 
 // k_prep: grid (ceil(H/256), T); one wave per 64-input group.
@@ -224,7 +274,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     float* sX = sK + NG;                                 // [NG]
     float* sI = sX + NG;                                 // [NG]
     float* red = sI + NG;                                // [4][64]
-    __shared__ int s_expert;
+    __shared__ TopkScratch s_topk;
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int t = blockIdx.y, u = blockIdx.x + a.unit_offset;
@@ -254,14 +304,10 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     if (routed) {
         int e;
         if (a.logits) {
-            if (wave == 0) {
-                const bool first = u == 0;
-                topk_softmax_wave<Q>(a.logits + (size_t)t * a.E, a.E, a.k,
-                                  first ? a.ids_out + (size_t)t * a.k : nullptr,
-                                  first ? a.w_out + (size_t)t * a.k : nullptr, j, &s_expert);
-            }
-            __syncthreads();
-            e = s_expert;
+            const bool first = u == 0;
+            e = topk_select<Q>(a.logits + (size_t)t * a.E, a.E, a.k, j, s_topk,
+                               first ? a.ids_out + (size_t)t * a.k : nullptr,
+                               first ? a.w_out + (size_t)t * a.k : nullptr);
         } else {
             e = a.ids[(size_t)t * a.k + j];
         }
@@ -597,8 +643,7 @@ static hipError_t launch_gu_xq(const FfnArgs& a, int T, int n_units, hipStream_t
 
 template <int XP>
 static hipError_t launch_gu_xp(const FfnArgs& a, int T, int n, hipStream_t s) {
-    if (!a.logits) return launch_gu_xq<XP, 1>(a, T, n, s);  // no selection in the kernel
-    if (a.E <= 64) return launch_gu_xq<XP, 1>(a, T, n, s);
+    if (!a.logits || a.E <= 64) return launch_gu_xq<XP, 1>(a, T, n, s);  // Q = 1: no selection
     if (a.E <= 128) return launch_gu_xq<XP, 2>(a, T, n, s);
     if (a.E <= 256) return launch_gu_xq<XP, 4>(a, T, n, s);
     return launch_gu_xq<XP, 16>(a, T, n, s);

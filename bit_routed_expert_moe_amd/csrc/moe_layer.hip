@@ -240,6 +240,7 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.hHs = (float*)(ws + o.hHs);
     a.hinv = (float*)(ws + o.hinv);
     a.dpart = (float*)(ws + o.dpart);
+    a.n_units = L->d.top_k * L->blk_r + L->blk_s;
     a.dctr = (uint32_t*)(ws + o.dctr);
     a.y = y;
     a.eo = eo;
@@ -340,6 +341,18 @@ moe_status grouped_ffn(const moe_layer* L, const void* x, int T, int32_t* ids, f
     return MOE_OK;
 }
 
+// The per-token FFN: gate/up units [first, first + n), then the down stage
+// that writes y and/or the per-slot outputs.
+hipError_t decode_units(const moe_layer* L, const FfnArgs& fa, int T, int first, int n, hipStream_t s) {
+    FfnArgs a = fa;
+    a.unit_offset = first;
+    return timed(K_GATE_UP, s, [&] { return launch_gate_up(a, T, L->xparts, n, s); });
+}
+
+hipError_t decode_finish(const FfnArgs& fa, int T, hipStream_t s) {
+    return timed(K_DOWN, s, [&] { return launch_down(fa, T, s); });
+}
+
 moe_status check_call(const moe_layer* L, const void* x, int32_t T, const void* ws) {
     if (!L) return fail(MOE_ERR_ARG, "null layer handle");
     if (!x) return fail(MOE_ERR_ARG, "null activations");
@@ -410,19 +423,17 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
     e = hipMemcpyAsync(ws + o.slot_ids, c.h_slots, sizeof(int32_t) * k, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "slot table copy");
     const int routed_units = k * L->blk_r;
-    fa.unit_offset = routed_units;  // shared expert first, overlapping the copies
-    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, 1, L->xparts, L->blk_s, s); })) != hipSuccess)
+    // shared expert first, overlapping the copies
+    if ((e = decode_units(L, fa, 1, routed_units, L->blk_s, s)) != hipSuccess)
         return hip_fail(e, "gate/up launch");
     if (copies) {
         if ((e = hipEventRecord(c.ev_copies, c.side)) != hipSuccess ||
             (e = hipStreamWaitEvent(s, c.ev_copies, 0)) != hipSuccess)
             return hip_fail(e, "copy ordering");
     }
-    fa.unit_offset = 0;
-    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, 1, L->xparts, routed_units, s); })) != hipSuccess)
+    if ((e = decode_units(L, fa, 1, 0, routed_units, s)) != hipSuccess)
         return hip_fail(e, "gate/up launch");
-    if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, 1, s); })) != hipSuccess)
-        return hip_fail(e, "down launch");
+    if ((e = decode_finish(fa, 1, s)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
 
@@ -581,9 +592,8 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     if (e != hipSuccess) return hip_fail(e, "prep launch");
     FfnArgs fa = ffn_args(L, ids, nullptr, ws, o, nullptr, expert_out, false);
     if (L->cache.n_slots) return cached_ffn(L, ids, fa, o, ws, s);
-    const int units = L->d.top_k * L->blk_r + L->blk_s;
-    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, units, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
-    if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
+    if ((e = decode_units(L, fa, T, 0, fa.n_units, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+    if ((e = decode_finish(fa, T, s)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
 
@@ -617,9 +627,8 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
         return cached_ffn(L, ids, ffn_args(L, ids, w, ws, o, y, nullptr, false), o, ws, s);
     }
     FfnArgs fa = ffn_args(L, ids, w, ws, o, y, nullptr, true);
-    const int units = L->d.top_k * L->blk_r + L->blk_s;
-    if ((e = timed(K_GATE_UP, s, [&] { return launch_gate_up(fa, T, L->xparts, units, s); })) != hipSuccess) return hip_fail(e, "gate/up launch");
-    if ((e = timed(K_DOWN, s, [&] { return launch_down(fa, T, s); })) != hipSuccess) return hip_fail(e, "down launch");
+    if ((e = decode_units(L, fa, T, 0, fa.n_units, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+    if ((e = decode_finish(fa, T, s)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
 
