@@ -93,7 +93,7 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 }
 
 template <int Q>
-__device__ int topk_select(const float* lg, int E, int k, int want, TopkScratch& sm, int32_t* ids_out,
+__device__ __forceinline__ int topk_select(const float* lg, int E, int k, int want, TopkScratch& sm, int32_t* ids_out,
                            float* w_out) {
     const int lane = threadIdx.x & 63;
     float lv[Q];
