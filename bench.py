@@ -46,10 +46,11 @@ PEAK_HBM_GBS = 8000.0
 # kernel source they were taken on (first 16 hex digits of its sha256); None
 # once that file changes.
 TRAFFIC = {
-    # FETCH_SIZE 12158.1 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24938598, "moe_kernels.hip", "6d740c8bcffa6c9f"),
-    # FETCH_SIZE 1866012.9 KiB x 2.0 + WRITE_SIZE 5754.7 KiB x 1.0 per launch (mean)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3827487232, "moe_prefill.hip", "15dbfa7b810640d6"),
+    # FETCH_SIZE 12168.1 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24959078, "moe_kernels.hip", "9c5855d79f2ff3f4"),
+    # FETCH_SIZE 1833701.5 KiB x 2.0 + WRITE_SIZE 5753.0 KiB x 1.0 per launch (mean over
+    # the bench's 32 distinct chunks)
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761311715, "moe_prefill.hip", "3d0e32043f6d886e"),
 }
 
 
