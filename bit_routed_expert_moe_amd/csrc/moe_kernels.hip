@@ -1,15 +1,17 @@
 // moe_kernels.hip -- gfx950 kernels of the routed-expert MoE layer.
 //
 //   k_route       router GEMV (int8 rows x activations), two rows per wave,
-//                 every load issued before any use; one extra workgroup per
-//                 token prepares the activations for the FFN kernels.
-//   k_topk        exact top-k and gate weights from the logits (API route).
+//                 every load issued before any use; extra workgroups beside
+//                 the router prepare the activations for the FFN kernels (one
+//                 wave per 64-input group).
+//   k_topk        exact top-k and gate weights from the logits (API route and
+//                 the grouped path).
 //   k_prep        activation preparation alone (API expert FFN).
 //   k_gate_up     one workgroup per (token, expert slot, block of 32 rows of
 //                 I).  For routed slots in the fused path it first selects its
-//                 expert itself (exact top-k over the logits); then it streams
-//                 the 64-row gate/up tile, h = silu(g) * u, and writes h
-//                 prepared as fp16 pairs for the down kernel.
+//                 expert itself (exact top-k over the logits, a radix select);
+//                 then it streams the 64-row gate/up tile, h = silu(g) * u, and
+//                 writes h prepared as fp16 pairs for the down kernel.
 //   k_down        one workgroup per (token, 64 output rows, work item), a work
 //                 item being one routed expert or a k-slice of the shared one;
 //                 the last item to finish for an output tile sums the items in

@@ -5,6 +5,9 @@
 //   k_prep_tokens   per token: fp16 parts of x * 2^e, with one e per token
 //                   chosen so that its largest value is below 2^14; the exact
 //                   sum of each 64-input group of x * 2^e.
+//   k_route_tiles   router logits as 16-token x 16-expert MFMA tiles over the
+//                   prepared activations and the int8 rows turned exactly into
+//                   fp16 (k_topk then selects).
 //   k_group         one workgroup: (token, slot) pairs sorted by expert
 //                   (stable), and a tile list of at most 16 rows per tile;
 //                   the shared expert adds tiles of 16 consecutive tokens.
@@ -13,8 +16,9 @@
 //                   the two halves are added in a fixed order, then
 //                   h = silu(gate) * up is stored as fp16 with a per-(row,
 //                   64-group) power-of-two scale, plus the group's sum of h.
-//   k_down_grouped  per (tile, 256 outputs): wave = 64 outputs over all of I;
-//                   writes each row's expert output (unweighted).
+//   k_down_grouped  per (tile, 512 outputs): wave = 128 outputs (8 MFMA
+//                   N-tiles) over all of I; writes each row's expert output
+//                   (unweighted).
 // The combine is the decode path's k_combine (fixed order, shared last).
 //
 // Numerics follow the affine group quantisation directly: the MFMA operand B

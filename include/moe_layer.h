@@ -196,9 +196,11 @@ moe_status moe_cache_stats(moe_layer_t layer, uint64_t* hits, uint64_t* misses);
  * MOE_ERR_DEVICE otherwise. */
 moe_status moe_poll_device_error(moe_layer_t layer, void* workspace, void* stream);
 
-/* Measurement support.  While profiling is on, every kernel the library
- * launches is bracketed by two hipEvents recorded on its launch stream, up to
- * `capacity` launches.  moe_profile_read synchronises those events and writes,
+/* Measurement support.  While profiling is on, the library dispatches the
+ * first kernel of each launch step with hipExtLaunchKernelGGL carrying a
+ * start/stop hipEvent pair, so the pair holds that dispatch's own start and
+ * end on its launch stream (up to `capacity` launches).  moe_profile_read
+ * synchronises those events and writes,
  * per recorded launch, the kernel id (0 router, 1 activation prep, 2 gate/up,
  * 3 down with in-place combine, 4 combine, 5 top-k; for calls of 4 or more
  * tokens: 6 activation prep, 7 grouping by expert, 8 grouped gate/up, 9 grouped
