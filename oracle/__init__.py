@@ -51,6 +51,7 @@ class Oracle:
         L.oracle_router_logits.argtypes = [C.c_int, C.c_int, _i8p, _u16p, _dp, _dp]
         L.oracle_select_topk.argtypes = [C.c_int, C.c_int, _dp, _i32p]
         L.oracle_softmax_gates.argtypes = [C.c_int, _dp, _dp]
+        L.oracle_sigmoid_route.argtypes = [C.c_int, C.c_int, _dp, _opt(_dp), C.c_double, _i32p, _dp]
         L.oracle_silu.argtypes = [C.c_double]
         L.oracle_silu.restype = C.c_double
         L.oracle_expert_ffn.argtypes = [C.c_int, C.c_int, _u8p, _dp, _dp,
@@ -150,9 +151,24 @@ class Oracle:
                                     np.ascontiguousarray(x, dtype=np.float64), ids, w, y, lg)
         return ids, w, y, lg
 
-    def route(self, rq, rs, x: np.ndarray, k: int):
-        """Router, exact top-k and renormalised gates for one token."""
+    def sigmoid_route(self, logits: np.ndarray, k: int, bias: np.ndarray | None = None,
+                      scale: float = 1.0):
+        """Sigmoid scores, top-k of score + bias, gates = scale * score / sum."""
+        lg = np.ascontiguousarray(logits, dtype=np.float64)
+        ids = np.empty(k, dtype=np.int32)
+        w = np.empty(k)
+        self.lib.oracle_sigmoid_route(lg.size, k, lg, None if bias is None else
+                                      np.ascontiguousarray(bias, dtype=np.float64), float(scale), ids, w)
+        return ids, w
+
+    def route(self, rq, rs, x: np.ndarray, k: int, gate: str = "softmax",
+              bias: np.ndarray | None = None, scale: float = 1.0):
+        """Router, exact top-k and gates for one token: softmax over the
+        selected logits, or the sigmoid router (selection bias, scale)."""
         lg = self.router_logits(rq, rs, x)
+        if gate == "sigmoid":
+            ids, w = self.sigmoid_route(lg, k, bias, scale)
+            return ids, w, lg
         ids = self.select_topk(lg, k)
         return ids, self.softmax_gates(lg[ids]), lg
 

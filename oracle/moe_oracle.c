@@ -239,6 +239,33 @@ void oracle_softmax_gates(int k, const double *sel_logits, double *w)
         w[j] /= z;
 }
 
+/* Sigmoid router with a selection bias and a routed scaling factor: the
+ * DeepSeek-V3-style router that the Colibri README ("What's implemented")
+ * names for GLM (noaux_tc, routed_scaling_factor); the pages give no formula,
+ * so this is the published scheme's plainest reading:
+ *   score s_e = 1 / (1 + exp(-l_e));
+ *   selection: the k largest keys s_e + b_e (b = per-expert correction bias,
+ *     zero when bias is NULL), in the order (key descending, id ascending);
+ *   gates from the unbiased scores of the selection,
+ *     w_j = scale * s_{S_j} / sum_{j'} s_{S_j'}.
+ * Group-limited selection is not modelled (a single group). */
+void oracle_sigmoid_route(int E, int k, const double *logits, const double *bias,
+                          double scale, int32_t *ids, double *w)
+{
+    double *key = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int e = 0; e < E; ++e)
+        key[e] = 1.0 / (1.0 + exp(-logits[e])) + (bias ? bias[e] : 0.0);
+    oracle_select_topk(E, k, key, ids);
+    double z = 0.0;
+    for (int j = 0; j < k; ++j) {
+        w[j] = 1.0 / (1.0 + exp(-logits[ids[j]]));
+        z += w[j];
+    }
+    for (int j = 0; j < k; ++j)
+        w[j] = scale * (w[j] / z);
+    free(key);
+}
+
 double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
 
 /* One expert's SwiGLU FFN on a dequantised-on-use record:

@@ -12,7 +12,7 @@ What they pin to:
   * a dense SwiGLU computed with library matmuls and scipy's logistic
   * exact integer arithmetic for the router
   * brute-force sorting for top-k, scipy's softmax for the gates
-  * a hand-worked gate example
+  * a hand-worked gate example (softmax and sigmoid routers)
   * sizes printed on the pages (tests/golden/page_sizes.json)
 """
 from __future__ import annotations
@@ -187,6 +187,36 @@ def pin_gates(orc):
         _close(orc.softmax_gates(lg[ids]), softmax(lg[ids]), 1e-14, what="k=E softmax")
         _close(orc.softmax_gates(lg[ids] + 123.25), softmax(lg[ids]), 1e-13, what="shift")
     assert orc.softmax_gates(np.array([-4.2])).tolist() == [1.0]
+
+
+def pin_sigmoid_router(orc):
+    """Sigmoid router.  Hand-worked: logits (ln 3, -ln 3, 5, 6) with bias
+    (10, 10, 0, 0), k = 2, scale 2.5 -> ids (0, 1) (the bias decides the
+    selection) and gates from the unbiased scores 3/4 and 1/4: 2.5 * (3/4, 1/4).
+    Zero bias selects as the softmax router (the logistic is increasing);
+    equal logits give scale / k each with the lowest ids; k = 1 gives scale;
+    with random bias the selection is a brute-force sort by (-(logistic + bias),
+    id) and the gates sum to the scale."""
+    lg = np.array([math.log(3.0), -math.log(3.0), 5.0, 6.0])
+    ids, w = orc.sigmoid_route(lg, 2, np.array([10.0, 10.0, 0.0, 0.0]), 2.5)
+    assert ids.tolist() == [0, 1]
+    _close(w, [1.875, 0.625], 0, 1e-15, what="worked example")
+    rng = np.random.default_rng(21)
+    for trial in range(100):
+        E = int(rng.integers(1, 300)); k = int(rng.integers(1, min(E, 16) + 1))
+        lg = rng.standard_normal(E) * 2
+        ids, w = orc.sigmoid_route(lg, k, None, 1.0)
+        assert ids.tolist() == orc.select_topk(lg, k).tolist(), f"zero bias, trial {trial}"
+        b = np.round(rng.standard_normal(E) * 0.3, 1)
+        key = expit(lg) + b
+        ids, w = orc.sigmoid_route(lg, k, b, 1.7)
+        assert ids.tolist() == sorted(range(E), key=lambda e: (-key[e], e))[:k], f"bias, trial {trial}"
+        _close(np.sum(w), 1.7, 1e-14, what="gates sum to the scale")
+        _close(w / w[0], expit(lg[ids]) / expit(lg[ids[0]]), 1e-13, what="gates from unbiased scores")
+    ids, w = orc.sigmoid_route(np.full(10, 0.3), 4, None, 3.0)
+    assert ids.tolist() == [0, 1, 2, 3]
+    _close(w, np.full(4, 0.75), 0, 1e-15, what="equal logits")
+    assert orc.sigmoid_route(np.array([-7.0, 2.0]), 1, None, 2.5)[1].tolist() == [2.5]
 
 
 def pin_silu(orc):

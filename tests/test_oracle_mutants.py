@@ -37,6 +37,11 @@ MUTANTS = {
                           "(size_t)48 * H * b + (size_t)16 * H + (size_t)o * 16"),
     "shared_dropped": ("acc += y_shared[o];", "acc += 0.0 * y_shared[o];"),
     "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "sigmoid_gates_use_bias": ("w[j] = 1.0 / (1.0 + exp(-logits[ids[j]]));",
+                               "w[j] = key[ids[j]];"),
+    "sigmoid_scale_dropped": ("w[j] = scale * (w[j] / z);", "w[j] = w[j] / z;"),
+    "sigmoid_bias_ignored": ("+ (bias ? bias[e] : 0.0);", "+ 0.0;"),
+    "sigmoid_sign": ("key[e] = 1.0 / (1.0 + exp(-logits[e]))", "key[e] = 1.0 / (1.0 + exp(logits[e]))"),
 }
 
 
