@@ -46,11 +46,11 @@ PEAK_HBM_GBS = 8000.0
 # kernel source they were taken on (first 16 hex digits of its sha256); None
 # once that file changes.
 TRAFFIC = {
-    # FETCH_SIZE 12168.1 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24959078, "moe_kernels.hip", "9c5855d79f2ff3f4"),
-    # FETCH_SIZE 1833701.5 KiB x 2.0 + WRITE_SIZE 5753.0 KiB x 1.0 per launch (mean over
+    # FETCH_SIZE 12168.9 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24960717, "moe_kernels.hip", "aed6c2436052778d"),
+    # FETCH_SIZE 1833719.2 KiB x 2.0 + WRITE_SIZE 5753.4 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761311715, "moe_prefill.hip", "3d0e32043f6d886e"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761348516, "moe_prefill.hip", "ac1ac64007a8eb40"),
 }
 
 
@@ -109,7 +109,32 @@ def kernel_timed_pass(run_steps, capacity):
     return recs
 
 
-def cpu_baseline(wl, xs_host, seconds):
+SIGMOID_SCALE = 2.5  # routed scaling factor of the sigmoid-router runs
+
+
+def gate_kwargs(args, wl, layer, dev):
+    """Layer keyword arguments for the chosen gate; the bias is seeded per layer."""
+    import synth
+    import torch
+    if args.gate == "softmax":
+        return {}
+    b = synth.selection_bias(wl.seed, layer, wl.n_experts)
+    return dict(gate="sigmoid", routed_scale=SIGMOID_SCALE, selection_bias=torch.from_numpy(b).to(dev))
+
+
+def gate_desc(args):
+    return "softmax" if args.gate == "softmax" else f"sigmoid (bias U(-0.05, 0.05), scale {SIGMOID_SCALE})"
+
+
+def oracle_route(orc, args, wl, layer, rq, rs, xd):
+    import synth
+    if args.gate == "softmax":
+        return orc.route(rq, rs, xd, wl.top_k)
+    b = synth.selection_bias(wl.seed, layer, wl.n_experts).astype(np.float64)
+    return orc.route(rq, rs, xd, wl.top_k, gate="sigmoid", bias=b, scale=SIGMOID_SCALE)
+
+
+def cpu_baseline(wl, xs_host, seconds, args):
     """The CPU oracle on the first token-layers of the same inputs, until about
     `seconds` of oracle compute have been spent (record generation excluded)."""
     import oracle
@@ -128,7 +153,7 @@ def cpu_baseline(wl, xs_host, seconds):
             for t in range(wl.n_tokens):
                 xd = orc.act_to_f64(wl.act, xs_host[s, l, t])
                 t0 = time.perf_counter()
-                ids, w, _ = orc.route(rq, rs, xd, k)
+                ids, w, _ = oracle_route(orc, args, wl, l, rq, rs, xd)
                 spent += time.perf_counter() - t0
                 recs = [synth.expert_record(wl.seed, l, int(e), H, I) for e in ids]
                 shared = synth.expert_record(wl.seed, l, synth.SHARED_INDEX, H, Is) if Is else None
@@ -174,7 +199,8 @@ def run_cached(args, wl):
         slots = torch.zeros(wl.n_slots * rb, dtype=torch.uint8, device=dev)
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
                             torch.from_numpy(rs.view(np.float16)).to(dev), None, shared,
-                            act=wl.act, n_slots=wl.n_slots, host_pool=host, slots=slots))
+                            act=wl.act, n_slots=wl.n_slots, host_pool=host, slots=slots,
+                            **gate_kwargs(args, wl, l, dev)))
     del staging
     S = wl.steps
     xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][1][H]
@@ -232,7 +258,7 @@ def run_cached(args, wl):
         "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
                    "shared_inter": Is, "layers": L, "batch": 1, "act": wl.act,
-                   "routing": wl.routing, "n_slots": wl.n_slots},
+                   "routing": wl.routing, "gate": gate_desc(args), "n_slots": wl.n_slots},
         "stack_tok_s": round(1e3 / ms_per_step, 2),
         "hit_rate_timed": round(hit_timed, 4), "hit_rate_all_steps": round(hit_all, 4),
         "miss_bytes_per_step": int(miss_bytes_step), "h2d_gbps": round(h2d_gbs, 1),
@@ -272,7 +298,8 @@ def run_prefill(args, wl):
             synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
         pools.append((pool, shared, rq, rs))
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
-                            torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act))
+                            torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act,
+                            **gate_kwargs(args, wl, l, dev)))
     S = NL * C  # distinct (layer, chunk) steps
     xs_host = np.empty((S, T, H))
     for l in range(NL):
@@ -375,7 +402,7 @@ def run_prefill(args, wl):
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = prefill_cpu_baseline(wl, pools[0], xs_q[0], args.cpu_seconds)
+        cpu = prefill_cpu_baseline(wl, pools[0], xs_q[0], args.cpu_seconds, args)
 
     out = {
         "metric": "prefill tokens/s per MoE layer + achieved HBM GB/s vs peak (128-token chunk, top-8)",
@@ -384,7 +411,7 @@ def run_prefill(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u4 weights x f16 activations -> f32 (MFMA)", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
-                   "shared_inter": Is, "chunk_tokens": T, "act": wl.act, "routing": wl.routing,
+                   "shared_inter": Is, "chunk_tokens": T, "act": wl.act, "routing": wl.routing, "gate": gate_desc(args),
                    "weight_sets": NL, "distinct_chunks": S, "graph_chunk": G},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
         "alg_bytes_per_chunk": int(mean_bytes), "unique_experts_mean": round(float(uniq.mean()), 2),
@@ -395,7 +422,7 @@ def run_prefill(args, wl):
     print(json.dumps(out), flush=True)
 
 
-def prefill_cpu_baseline(wl, pool, x_chunk, seconds):
+def prefill_cpu_baseline(wl, pool, x_chunk, seconds, args):
     """The CPU oracle, token by token, on the first chunk of layer 0 (records read
     from that layer's generated pool), until about `seconds` of oracle compute."""
     import oracle
@@ -410,7 +437,7 @@ def prefill_cpu_baseline(wl, pool, x_chunk, seconds):
     for t in range(x_chunk.shape[0]):
         xd = orc.act_to_f64(wl.act, x_chunk[t])
         t0 = time.perf_counter()
-        ids, w, _ = orc.route(rq, rs, xd, k)
+        ids, w, _ = oracle_route(orc, args, wl, 0, rq, rs, xd)
         yr = np.stack([orc.expert_ffn(H, I, host[int(e) * rb:(int(e) + 1) * rb], xd) for e in ids])
         ys = orc.expert_ffn(H, Is, shared, xd) if Is else None
         orc.combine(w, yr, ys)
@@ -438,6 +465,9 @@ def main():
                     help="prefill workloads: layers of distinct weights cycled over")
     ap.add_argument("--prefill-chunks", type=int, default=4,
                     help="prefill workloads: distinct input chunks per layer")
+    ap.add_argument("--gate", choices=("softmax", "sigmoid"), default="softmax",
+                    help="router gate: renormalised softmax (default) or the sigmoid router "
+                         "(selection bias U(-0.05, 0.05) per expert, routed scale 2.5)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -484,7 +514,8 @@ def main():
             shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
             synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
-                            torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act))
+                            torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act,
+                            **gate_kwargs(args, wl, l, dev)))
     S = wl.steps
     xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][T][H]
     xs_q = synth.quantize_act(xs_host, wl.act)
@@ -574,7 +605,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, xs_q, args.cpu_seconds)
+        cpu = cpu_baseline(wl, xs_q, args.cpu_seconds, args)
 
     out = {
         "metric": METRIC, "value": round(layer_tok_s, 1), "unit": "tok/s per layer",
@@ -583,7 +614,7 @@ def main():
         "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
                    "shared_inter": Is, "layers": L, "batch": T, "act": wl.act,
-                   "routing": wl.routing, "graph_chunk": G},
+                   "routing": wl.routing, "gate": gate_desc(args), "graph_chunk": G},
         "stack_tok_s": round(T / (ms_per_step * 1e-3), 2),
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
         "alg_bytes_per_token_layer": tl_bytes,

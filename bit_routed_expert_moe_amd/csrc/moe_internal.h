@@ -39,7 +39,10 @@ struct RouteArgs {
     float* xK;               // [T][H/64]
     float* xX;               // [T][H/64]
     float* xinv;             // [T][H/64]
+    const float* bias;       // [E] selection bias (sigmoid gate) or nullptr
+    float rscale;            // sigmoid gate: routed scaling factor
     int H, E, k, prep, T;
+    int gate;                // 0 softmax, 1 sigmoid
 };
 
 struct FfnArgs {
@@ -52,6 +55,9 @@ struct FfnArgs {
     const int32_t* ids;      // [T][k] selection (read by k_down; by k_gate_up unless logits)
     const float* w;          // [T][k] gate weights (fused combine only)
     const float* logits;     // [T][E]: if set, k_gate_up selects the experts itself
+    const float* bias;       // [E] selection bias (sigmoid gate) or nullptr
+    float rscale;            // sigmoid gate: routed scaling factor
+    int gate;                // 0 softmax, 1 sigmoid
     int32_t* ids_out;        // [T][k] written by k_gate_up's first workgroup when logits is set
     float* w_out;            // [T][k]
     const uint32_t* xpairs;  // prepared x, as in RouteArgs

@@ -94,16 +94,40 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Gate functions: 0 = softmax over the selected logits (selection by logit);
+// 1 = sigmoid router (selection by logistic score + bias, gates = rscale *
+// score / sum of the selection's scores).
+struct GateFn {
+    int kind;
+    const float* bias;  // [E] or nullptr
+    float rscale;
+};
+
 template <int Q>
 __device__ __forceinline__ int topk_select(const float* lg, int E, int k, int want, TopkScratch& sm, int32_t* ids_out,
-                           float* w_out) {
+                           float* w_out, GateFn gf) {
     const int lane = threadIdx.x & 63;
-    float lv[Q];
+    float lv[Q];  // logit (softmax) or score (sigmoid) of each key slot
     uint32_t u[Q];
+    // all loads first, unconditionally (clamped index), keys afterwards: one round trip
 #pragma unroll
     for (int q = 0; q < Q; ++q) lv[q] = lg[min(lane + 64 * q, E - 1)];
+    if (gf.kind == 1) {
+        float bv[Q];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) u[q] = lane + 64 * q < E ? order_key(lv[q]) : 0u;  // 0: below every key
+        for (int q = 0; q < Q; ++q) bv[q] = gf.bias ? gf.bias[min(lane + 64 * q, E - 1)] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            lv[q] = __builtin_amdgcn_rcpf(1.0f + expf(-lv[q]));  // score; 1-ulp reciprocal
+            u[q] = order_key(lv[q] + bv[q]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) u[q] = order_key(lv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (lane + 64 * q >= E) u[q] = 0u;  // 0: below every key
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
@@ -155,13 +179,18 @@ __device__ __forceinline__ int topk_select(const float* lg, int E, int k, int wa
     __syncthreads();
     if (ids_out && threadIdx.x < 64) {
         const float sel_l = lane < k ? sm.val[lane] : 0.0f;
-        const float mx = __shfl(sel_l, 0, 64);  // rank 0 is the largest
-        const float ex = lane < k ? expf(sel_l - mx) : 0.0f;
+        float ex;
+        if (gf.kind == 1) {
+            ex = lane < k ? sel_l : 0.0f;  // the unbiased score
+        } else {
+            const float mx = __shfl(sel_l, 0, 64);  // rank 0 is the largest
+            ex = lane < k ? expf(sel_l - mx) : 0.0f;
+        }
         float z = 0.0f;
         for (int j = 0; j < k; ++j) z += __shfl(ex, j, 64);
         if (lane < k) {
             ids_out[lane] = sm.sel[lane];
-            w_out[lane] = ex / z;
+            w_out[lane] = gf.kind == 1 ? gf.rscale * (ex / z) : ex / z;
         }
     }
     return want >= 0 ? sm.sel[want] : -1;
@@ -251,7 +280,8 @@ template <int Q>
 __global__ __launch_bounds__(64) void k_topk(RouteArgs a) {
     __shared__ TopkScratch sm;
     const int t = blockIdx.x;
-    topk_select<Q>(a.logits + (size_t)t * a.E, a.E, a.k, -1, sm, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k);
+    topk_select<Q>(a.logits + (size_t)t * a.E, a.E, a.k, -1, sm, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k,
+                   GateFn{a.gate, a.bias, a.rscale});
 }
 
 // k_prep: grid (ceil(H/256), T); one wave per 64-input group.
@@ -309,7 +339,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
             const bool first = u == 0;
             e = topk_select<Q>(a.logits + (size_t)t * a.E, a.E, a.k, j, s_topk,
                                first ? a.ids_out + (size_t)t * a.k : nullptr,
-                               first ? a.w_out + (size_t)t * a.k : nullptr);
+                               first ? a.w_out + (size_t)t * a.k : nullptr, GateFn{a.gate, a.bias, a.rscale});
         } else {
             e = a.ids[(size_t)t * a.k + j];
         }

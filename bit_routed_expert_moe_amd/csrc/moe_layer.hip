@@ -211,6 +211,9 @@ RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, 
     a.k = L->d.top_k;
     a.prep = prep;
     a.T = T;
+    a.gate = L->d.gate_fn == MOE_SIGMOID_TOPK ? 1 : 0;
+    a.bias = L->w.selection_bias;
+    a.rscale = L->d.routed_scale > 0.0f ? L->d.routed_scale : 1.0f;
     return a;
 }
 
@@ -222,6 +225,9 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
         a.ids_out = const_cast<int32_t*>(ids);
         a.w_out = const_cast<float*>(w);
     }
+    a.gate = L->d.gate_fn == MOE_SIGMOID_TOPK ? 1 : 0;
+    a.bias = L->w.selection_bias;
+    a.rscale = L->d.routed_scale > 0.0f ? L->d.routed_scale : 1.0f;
     a.experts = L->w.experts;
     a.shared = L->w.shared;
     a.rec_bytes = L->rec_bytes;
@@ -464,8 +470,16 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         return fail(MOE_ERR_SHAPE, "top_k must be in 1..min(16, n_experts)");
     if (d.act_dtype != MOE_F32 && d.act_dtype != MOE_BF16)
         return fail(MOE_ERR_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
-    if (d.gate_fn != MOE_SOFTMAX_TOPK)
-        return fail(MOE_ERR_STATE, "only MOE_SOFTMAX_TOPK is available");
+    if (d.gate_fn != MOE_SOFTMAX_TOPK && d.gate_fn != MOE_SIGMOID_TOPK)
+        return fail(MOE_ERR_ARG, "gate_fn must be MOE_SOFTMAX_TOPK or MOE_SIGMOID_TOPK");
+    if (!(d.routed_scale >= 0.0f) || !(d.routed_scale < 3.0e38f))
+        return fail(MOE_ERR_ARG, "routed_scale must be finite and >= 0");
+    if (d.gate_fn == MOE_SOFTMAX_TOPK && d.routed_scale != 0.0f && d.routed_scale != 1.0f)
+        return fail(MOE_ERR_ARG, "routed_scale applies to MOE_SIGMOID_TOPK only");
+    if (d.gate_fn == MOE_SOFTMAX_TOPK && w->selection_bias)
+        return fail(MOE_ERR_ARG, "selection_bias applies to MOE_SIGMOID_TOPK only");
+    if (w->selection_bias && !aligned(w->selection_bias, 4))
+        return fail(MOE_ERR_ALIGN, "selection_bias needs 4-byte alignment");
     if (d.n_slots < 0 || d.n_slots > (1 << 20)) return fail(MOE_ERR_SHAPE, "bad n_slots");
     if (d.n_slots > 0 && d.n_slots < d.top_k)
         return fail(MOE_ERR_SHAPE, "n_slots must be at least top_k");
@@ -488,6 +502,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     if (w->experts && (st = check_device_ptr(w->experts, "experts")) != MOE_OK) return st;
     if (w->shared && (st = check_device_ptr(w->shared, "shared")) != MOE_OK) return st;
     if (w->slots && (st = check_device_ptr(w->slots, "slots")) != MOE_OK) return st;
+    if (w->selection_bias && (st = check_device_ptr(w->selection_bias, "selection_bias")) != MOE_OK)
+        return st;
     if (w->host_pool) {
         hipPointerAttribute_t attr;
         if (hipPointerGetAttributes(&attr, w->host_pool) != hipSuccess ||

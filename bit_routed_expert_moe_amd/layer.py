@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_layer.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK = 0
+MOE_SIGMOID_TOPK = 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
           -4: "MOE_ERR_HIP", -5: "MOE_ERR_NOMEM", -6: "MOE_ERR_NOT_PINNED",
           -7: "MOE_ERR_STATE", -8: "MOE_ERR_DEVICE"}
@@ -39,13 +40,13 @@ class Desc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("inter", C.c_int32),
                 ("top_k", C.c_int32), ("shared_inter", C.c_int32), ("group", C.c_int32),
                 ("act_dtype", C.c_int32), ("gate_fn", C.c_int32), ("n_slots", C.c_int32),
-                ("reserved", C.c_int32 * 7)]
+                ("routed_scale", C.c_float), ("reserved", C.c_int32 * 6)]
 
 
 class Weights(C.Structure):
     _fields_ = [("router_q", C.c_void_p), ("router_scale", C.c_void_p),
                 ("experts", C.c_void_p), ("shared", C.c_void_p),
-                ("host_pool", C.c_void_p), ("slots", C.c_void_p)]
+                ("host_pool", C.c_void_p), ("slots", C.c_void_p), ("selection_bias", C.c_void_p)]
 
 
 _LIB: C.CDLL | None = None
@@ -121,19 +122,30 @@ class Layer:
     host_pool     pinned uint8 CPU tensor of all E records, into
     slots         uint8 CUDA tensor [n_slots * record_bytes(H, inter)]
                   (experts may then be None)
+    gate          "softmax" (renormalised softmax over the selected logits) or
+                  "sigmoid" (logistic scores, selection by score + selection_bias,
+                  gates = routed_scale * score / sum over the selection)
+    routed_scale  sigmoid gate: the routed scaling factor
+    selection_bias  sigmoid gate: float32 CUDA tensor [E] or None
     """
 
     def __init__(self, hidden: int, n_experts: int, inter: int, top_k: int, shared_inter: int,
                  router_q: torch.Tensor, router_scale: torch.Tensor,
                  experts: torch.Tensor | None, shared: torch.Tensor | None, act: str = "bf16",
                  n_slots: int = 0, host_pool: torch.Tensor | None = None,
-                 slots: torch.Tensor | None = None):
+                 slots: torch.Tensor | None = None, gate: str = "softmax",
+                 routed_scale: float = 1.0, selection_bias: torch.Tensor | None = None):
         self.hidden, self.n_experts, self.inter = hidden, n_experts, inter
         self.top_k, self.shared_inter, self.act = top_k, shared_inter, act
         self.n_slots = n_slots
-        self._keep = (router_q, router_scale, experts, shared, host_pool, slots)
+        if gate not in ("softmax", "sigmoid"):
+            raise ValueError("gate must be 'softmax' or 'sigmoid'")
+        self.gate = gate
+        self._keep = (router_q, router_scale, experts, shared, host_pool, slots, selection_bias)
         d = Desc(hidden, n_experts, inter, top_k, shared_inter, 64,
-                 MOE_BF16 if act == "bf16" else MOE_F32, MOE_SOFTMAX_TOPK, n_slots)
+                 MOE_BF16 if act == "bf16" else MOE_F32,
+                 MOE_SIGMOID_TOPK if gate == "sigmoid" else MOE_SOFTMAX_TOPK, n_slots,
+                 float(routed_scale))
         hp = None
         if host_pool is not None:
             if host_pool.is_cuda or not host_pool.is_pinned() or not host_pool.is_contiguous():
@@ -143,7 +155,8 @@ class Layer:
                     _dev(router_scale, "router_scale"),
                     None if experts is None else _dev(experts, "experts", torch.uint8),
                     None if shared is None else _dev(shared, "shared", torch.uint8), hp,
-                    None if slots is None else _dev(slots, "slots", torch.uint8))
+                    None if slots is None else _dev(slots, "slots", torch.uint8),
+                    None if selection_bias is None else _dev(selection_bias, "selection_bias", torch.float32))
         h = C.c_void_p()
         _check(lib().moe_layer_create(C.byref(d), C.byref(w), C.byref(h)))
         self.handle = h

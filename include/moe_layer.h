@@ -87,10 +87,19 @@ typedef struct moe_layer_desc {
     int32_t shared_inter;  /* intermediate size of the shared expert, 0 = none    */
     int32_t group;         /* quantisation group; must be 64                      */
     int32_t act_dtype;     /* MOE_F32 or MOE_BF16 activations x                   */
-    int32_t gate_fn;       /* MOE_SOFTMAX_TOPK (renormalised softmax over the top-k) */
+    int32_t gate_fn;       /* MOE_SOFTMAX_TOPK: w = softmax of the selected logits
+                              (selection by logit).  MOE_SIGMOID_TOPK: scores
+                              s_e = 1 / (1 + exp(-logit_e)); selection by s_e + b_e
+                              (b = weights.selection_bias, zero if NULL); w_j =
+                              routed_scale * s_j / sum over the selection of s.  The
+                              DeepSeek-V3-style router that the Colibri README ("What's
+                              implemented") names for GLM (noaux_tc,
+                              routed_scaling_factor); one expert group.            */
     int32_t n_slots;       /* 0 = every routed record resident in HBM; otherwise the
                               number of HBM expert slots of the slot cache (>= top_k) */
-    int32_t reserved[7];
+    float routed_scale;    /* MOE_SIGMOID_TOPK: the routed scaling factor (> 0; 0 reads
+                              as 1); must be 0 or 1 with MOE_SOFTMAX_TOPK           */
+    int32_t reserved[6];
 } moe_layer_desc;
 
 typedef struct moe_layer_weights {
@@ -102,6 +111,9 @@ typedef struct moe_layer_weights {
                                      holding all E records back to back; else NULL */
     uint8_t* slots;               /* n_slots > 0: device, n_slots records; else NULL.
                                      The library overwrites slots as experts enter. */
+    const float* selection_bias;  /* MOE_SIGMOID_TOPK only: device, [E] fp32 correction
+                                     bias added to the scores for selection (not to the
+                                     gates), or NULL; must be NULL with MOE_SOFTMAX_TOPK */
 } moe_layer_weights;
 
 typedef struct moe_layer* moe_layer_t;
@@ -129,6 +141,8 @@ size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens);
  *   ids device [T][k] int32 out: selected experts, by logit descending, ties to
  *       the lower id
  *   w   device [T][k] fp32 out: exp(l_j - l_max) / sum over the selection
+ *       (MOE_SIGMOID_TOPK: routed_scale * s_j / sum of s over the selection; ids
+ *       then in the order of s + bias descending, ties to the lower id)
  * Errors: ARG, ALIGN, HIP. */
 moe_status moe_route_topk(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
                           float* w, void* workspace, void* stream);

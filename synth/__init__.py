@@ -52,6 +52,7 @@ KIND_PERM = 8
 KIND_GUMBEL = 9
 KIND_Z1 = 10
 KIND_Z2 = 11
+KIND_SEL_BIAS = 12
 SHARED_INDEX = 0xFFFF  # expert index used for the shared expert's streams
 
 
@@ -147,6 +148,14 @@ def router(seed: int, layer: int, n_experts: int, hidden: int):
     rs = (0.5 + unit_uniform(stream(key(seed, layer, KIND_ROUTER_S, 0), n_experts))) / (
         73.6 * math.sqrt(hidden))
     return q.astype(np.int8).reshape(n_experts, hidden), to_f16_bits(rs)
+
+
+def selection_bias(seed: int, layer: int, n_experts: int, half_width: float = 0.05) -> np.ndarray:
+    """Per-expert selection bias of the sigmoid router, float32 uniform on
+    [-half_width, half_width) (the pages give no values; any fixed seeded draw
+    exercises the path)."""
+    u = unit_uniform(stream(key(seed, layer, KIND_SEL_BIAS, 0), n_experts))
+    return ((2.0 * u - 1.0) * half_width).astype(np.float32)
 
 
 def normal(k1: int, k2: int, n: int) -> np.ndarray:

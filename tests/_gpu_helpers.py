@@ -12,6 +12,7 @@ import synth.gpu
 Y_TOL = 2e-3   # max |y - y_ref| / max |y_ref| per token
 W_TOL = 1e-6   # max |w - w_ref|
 GAP = 1e-4     # required separation of the top-(k+1) oracle logits
+GAP_SIGMOID = 1e-5  # the same for the sigmoid router's selection keys (score + bias)
 
 
 def rel_err(y, y_ref) -> float:
@@ -20,9 +21,9 @@ def rel_err(y, y_ref) -> float:
     return float(np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-30))
 
 
-def gap_ok(logits: np.ndarray, k: int) -> bool:
+def gap_ok(logits: np.ndarray, k: int, gap: float = GAP) -> bool:
     s = np.sort(logits)[::-1][:k + 1]
-    return bool(np.all(-np.diff(s) > GAP))
+    return bool(np.all(-np.diff(s) > gap))
 
 
 class DeviceLayer:
@@ -30,10 +31,16 @@ class DeviceLayer:
     fill) plus the host copies the oracle needs (router only; records are
     regenerated on the CPU on demand)."""
 
-    def __init__(self, seed, layer, H, E, I, k, Is, act, dev="cuda"):
+    def __init__(self, seed, layer, H, E, I, k, Is, act, dev="cuda", gate="softmax",
+                 routed_scale=1.0, bias=None):
+        """gate / routed_scale / bias (float32 numpy [E] or None): the router's
+        gate function, as in bit_routed_expert_moe_amd.Layer."""
         from bit_routed_expert_moe_amd import Layer, record_bytes
         self.seed, self.layer, self.H, self.E, self.I, self.k, self.Is, self.act = \
             seed, layer, H, E, I, k, Is, act
+        self.gate, self.routed_scale = gate, routed_scale
+        self.bias = None if bias is None else np.asarray(bias, dtype=np.float32)
+        self.bias_dev = None if bias is None else torch.from_numpy(self.bias).to(dev)
         self.rq, self.rs = synth.router(seed, layer, E, H)
         self.pool = torch.empty(E * record_bytes(H, I), dtype=torch.uint8, device=dev)
         synth.gpu.fill_records(self.pool, H, I, seed, layer, 0, E)
@@ -43,7 +50,8 @@ class DeviceLayer:
             synth.gpu.fill_records(self.shared, H, Is, seed, layer, -1, 1)
         self.layer_obj = Layer(H, E, I, k, Is, torch.from_numpy(self.rq).to(dev),
                                torch.from_numpy(self.rs.view(np.float16)).to(dev), self.pool,
-                               self.shared, act=act)
+                               self.shared, act=act, gate=gate, routed_scale=routed_scale,
+                               selection_bias=self.bias_dev)
         self._rec_cache = {}
 
     def record(self, e: int) -> np.ndarray:
@@ -61,12 +69,22 @@ class DeviceLayer:
             x = synth.activations(self.seed, self.layer, step, self.H, attempt=a)[0]
             xq = synth.quantize_act(x, self.act)
             xd = orc.act_to_f64(self.act, xq)
-            if gap_ok(orc.router_logits(self.rq, self.rs, xd), self.k):
+            if gap_ok(self.selection_keys(orc, xd), self.k, GAP if self.gate == "softmax" else GAP_SIGMOID):
                 return xq, xd
         raise RuntimeError("no well-separated token found")
 
+    def selection_keys(self, orc, xd: np.ndarray) -> np.ndarray:
+        """The oracle's selection keys: logits, or logistic scores plus bias."""
+        lg = orc.router_logits(self.rq, self.rs, xd)
+        if self.gate == "softmax":
+            return lg
+        key = 1.0 / (1.0 + np.exp(-lg))
+        return key if self.bias is None else key + self.bias.astype(np.float64)
+
     def oracle(self, orc, xd: np.ndarray):
-        ids, w, lg = orc.route(self.rq, self.rs, xd, self.k)
+        ids, w, lg = orc.route(self.rq, self.rs, xd, self.k, gate=self.gate,
+                               bias=None if self.bias is None else self.bias.astype(np.float64),
+                               scale=self.routed_scale)
         yr = np.stack([orc.expert_ffn(self.H, self.I, self.record(int(e)), xd) for e in ids])
         ys = orc.expert_ffn(self.H, self.Is, self.record(synth.SHARED_INDEX), xd) if self.Is else None
         return ids, w, orc.combine(w, yr, ys), yr, ys

@@ -58,7 +58,9 @@ FAKE = dict(router_q=0x10000, router_scale=0x20000, experts=0x30000, shared=0x40
     (dict(group=32), -2), (dict(hidden=100), -2), (dict(hidden=0), -2), (dict(hidden=16384), -2),
     (dict(inter=96), -2), (dict(shared_inter=100), -2), (dict(n_experts=0), -2),
     (dict(n_experts=2048), -2), (dict(top_k=0), -2), (dict(top_k=33), -2),
-    (dict(n_experts=4, top_k=5), -2), (dict(act_dtype=7), -1), (dict(gate_fn=1), -7),
+    (dict(n_experts=4, top_k=5), -2), (dict(act_dtype=7), -1), (dict(gate_fn=2), -1),
+    (dict(routed_scale=2.5), -1), (dict(gate_fn=1, routed_scale=-1.0), -1),
+    (dict(gate_fn=1, routed_scale=float("nan")), -1), (dict(gate_fn=1, routed_scale=float("inf")), -1),
     (dict(n_slots=4), -2), (dict(n_slots=16), -1), (dict(n_slots=-1), -2),
 ])
 def test_create_rejects_bad_descriptor(change, status):
@@ -78,6 +80,10 @@ def test_create_rejects_missing_and_misaligned_pointers():
     assert _create(d, L.Weights(**{**FAKE, "experts": 0x30008}))[0] == -3
     assert _create(d, L.Weights(**{**FAKE, "router_q": 0x10004}))[0] == -3
     assert _create(d, L.Weights(**{**FAKE, "host_pool": 0x50000}))[0] == -1
+    # the selection bias belongs to the sigmoid gate and must be 4-byte aligned
+    assert _create(d, L.Weights(**{**FAKE, "selection_bias": 0x60000}))[0] == -1
+    ds = L.Desc(**{**GOOD, "gate_fn": 1, "routed_scale": 2.5})
+    assert _create(ds, L.Weights(**{**FAKE, "selection_bias": 0x60002}))[0] == -3
 
 
 def test_null_handles():

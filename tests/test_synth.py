@@ -93,3 +93,12 @@ def test_zipf_targets_realised_through_router(orc):
     assert hits >= 0.9 * n, hits
     top = int(np.argmin(synth.zipf_rank_of_expert(11, 0, E)))
     assert counts[top] == counts.max()
+
+
+def test_selection_bias_is_seeded_and_bounded():
+    a = synth.selection_bias(7, 0, 300)
+    assert a.dtype == np.float32 and a.shape == (300,)
+    assert np.all(a >= -0.05) and np.all(a < 0.05)
+    assert np.array_equal(a, synth.selection_bias(7, 0, 300))
+    assert not np.array_equal(a, synth.selection_bias(7, 1, 300))
+    assert abs(float(a.mean())) < 0.01 and float(a.std()) > 0.02
