@@ -175,8 +175,10 @@ def cpu_baseline(wl, xs_host, seconds, args):
 
 def run_cached(args, wl):
     """Out-of-core decode: each layer keeps wl.n_slots HBM slots filled from a
-    pinned host pool of all its experts (LFU).  Launched eagerly: every layer
-    synchronises the host on its expert ids."""
+    pinned host pool of all its experts (--cache-policy, default LFU; with
+    --pin N the N experts used most during the warm-up steps are pinned per
+    layer before the timed steps).  Launched eagerly: every layer synchronises
+    the host on its expert ids."""
     import torch
     import synth
     import synth.gpu
@@ -200,7 +202,7 @@ def run_cached(args, wl):
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
                             torch.from_numpy(rs.view(np.float16)).to(dev), None, shared,
                             act=wl.act, n_slots=wl.n_slots, host_pool=host, slots=slots,
-                            **gate_kwargs(args, wl, l, dev)))
+                            cache_policy=args.cache_policy, **gate_kwargs(args, wl, l, dev)))
     del staging
     S = wl.steps
     xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][1][H]
@@ -233,9 +235,18 @@ def run_cached(args, wl):
 
     W = min(args.warmup, S)
     K = min(args.steps, S - W)
+    counts = np.zeros((L, E), dtype=np.int64)  # expert selections per layer over the warm-up
     for s in range(W):
         run_step(s)
+        if args.pin:
+            for l, row in enumerate(ids.cpu().numpy()[:, 0]):
+                np.add.at(counts[l], row, 1)
     torch.cuda.synchronize()
+    if args.pin:
+        for l in range(L):
+            top = sorted(range(E), key=lambda e: (-counts[l, e], e))[:args.pin]
+            layers[l].cache_pin(top)
+        torch.cuda.synchronize()
     h0 = sum(l_.cache_stats()[0] for l_ in layers)
     m0 = sum(l_.cache_stats()[1] for l_ in layers)
     t0 = time.perf_counter()
@@ -258,7 +269,9 @@ def run_cached(args, wl):
         "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
                    "shared_inter": Is, "layers": L, "batch": 1, "act": wl.act,
-                   "routing": wl.routing, "gate": gate_desc(args), "n_slots": wl.n_slots},
+                   "routing": wl.routing, "gate": gate_desc(args), "n_slots": wl.n_slots,
+                   "cache_policy": args.cache_policy, "pinned_per_layer": args.pin,
+                   "pin_source": f"expert counts over the {W} warm-up steps" if args.pin else None},
         "stack_tok_s": round(1e3 / ms_per_step, 2),
         "hit_rate_timed": round(hit_timed, 4), "hit_rate_all_steps": round(hit_all, 4),
         "miss_bytes_per_step": int(miss_bytes_step), "h2d_gbps": round(h2d_gbs, 1),
@@ -468,6 +481,11 @@ def main():
     ap.add_argument("--gate", choices=("softmax", "sigmoid"), default="softmax",
                     help="router gate: renormalised softmax (default) or the sigmoid router "
                          "(selection bias U(-0.05, 0.05) per expert, routed scale 2.5)")
+    ap.add_argument("--cache-policy", choices=("lfu", "lru"), default="lfu",
+                    help="slot-cache workloads: replacement policy")
+    ap.add_argument("--pin", type=int, default=0,
+                    help="slot-cache workloads: pin this many experts per layer, the most used "
+                         "during the warm-up steps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")

@@ -41,6 +41,8 @@ struct SlotCache {
     std::vector<int32_t> expert_in;   // [n_slots], -1 when free
     std::vector<uint64_t> count;      // [E]
     std::vector<uint64_t> last_use;   // [n_slots]
+    std::vector<char> pinned;         // [n_slots]
+    int policy = MOE_CACHE_LFU;
     uint64_t tick = 0, hits = 0, misses = 0;
     hipStream_t side = nullptr;
     hipEvent_t ev_ids = nullptr, ev_copies = nullptr;
@@ -368,6 +370,31 @@ moe_status check_call(const moe_layer* L, const void* x, int32_t T, const void* 
     return MOE_OK;
 }
 
+// The slot to evict: a resident expert that is neither pinned nor among the
+// `n` ids in `keep`; LFU: smallest count, then least recently used, then
+// lowest slot; LRU: least recently used, then lowest slot.  -1 if none.
+int victim_slot(const SlotCache& c, const int32_t* keep, int n) {
+    int slot = -1;
+    for (int q = 0; q < c.n_slots; ++q) {
+        const int r = c.expert_in[q];
+        if (r < 0 || c.pinned[q]) continue;
+        bool kept = false;
+        for (int jj = 0; jj < n; ++jj) kept |= keep[jj] == r;
+        if (kept) continue;
+        if (slot < 0) {
+            slot = q;
+            continue;
+        }
+        const int rs = c.expert_in[slot];
+        const bool better = c.policy == MOE_CACHE_LRU
+                                ? c.last_use[q] < c.last_use[slot]
+                                : (c.count[r] < c.count[rs] ||
+                                   (c.count[r] == c.count[rs] && c.last_use[q] < c.last_use[slot]));
+        if (better) slot = q;
+    }
+    return slot;
+}
+
 // Routed + shared FFN of one decode token through the slot cache.  ids are on
 // the device (written earlier on `s`).  The host reads them, updates the LFU,
 // copies the missing records into their slots on the side stream, runs the
@@ -399,16 +426,7 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
             for (int q = 0; q < c.n_slots && slot < 0; ++q)
                 if (c.expert_in[q] < 0) slot = q;
             if (slot < 0) {
-                for (int q = 0; q < c.n_slots; ++q) {
-                    const int r = c.expert_in[q];
-                    bool selected = false;
-                    for (int jj = 0; jj < k; ++jj) selected |= c.h_ids[jj] == r;
-                    if (selected) continue;
-                    if (slot < 0 || c.count[r] < c.count[c.expert_in[slot]] ||
-                        (c.count[r] == c.count[c.expert_in[slot]] &&
-                         c.last_use[q] < c.last_use[slot]))
-                        slot = q;
-                }
+                slot = victim_slot(c, c.h_ids, k);
                 c.slot_of[c.expert_in[slot]] = -1;
             }
             c.expert_in[slot] = ex;
@@ -483,6 +501,10 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     if (d.n_slots < 0 || d.n_slots > (1 << 20)) return fail(MOE_ERR_SHAPE, "bad n_slots");
     if (d.n_slots > 0 && d.n_slots < d.top_k)
         return fail(MOE_ERR_SHAPE, "n_slots must be at least top_k");
+    if (d.cache_policy != MOE_CACHE_LFU && d.cache_policy != MOE_CACHE_LRU)
+        return fail(MOE_ERR_ARG, "cache_policy must be MOE_CACHE_LFU or MOE_CACHE_LRU");
+    if (d.n_slots == 0 && d.cache_policy != MOE_CACHE_LFU)
+        return fail(MOE_ERR_ARG, "cache_policy applies to a slot cache only");
     if (d.n_slots == 0 && (w->host_pool || w->slots))
         return fail(MOE_ERR_ARG, "host_pool/slots must be NULL when n_slots = 0");
     if (d.n_slots > 0 && (!w->host_pool || !w->slots))
@@ -542,6 +564,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         c.expert_in.assign(d.n_slots, -1);
         c.count.assign(d.n_experts, 0);
         c.last_use.assign(d.n_slots, 0);
+        c.pinned.assign(d.n_slots, 0);
+        c.policy = d.cache_policy;
         hipError_t e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_ids, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_copies, hipEventDisableTiming);
@@ -670,6 +694,43 @@ moe_status moe_cache_stats(moe_layer_t L, uint64_t* hits, uint64_t* misses) {
     if (!L->cache.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
     *hits = L->cache.hits;
     *misses = L->cache.misses;
+    return MOE_OK;
+}
+
+moe_status moe_cache_pin(moe_layer_t L, const int32_t* experts, int32_t n, void* stream) {
+    if (!L) return fail(MOE_ERR_ARG, "null layer handle");
+    SlotCache& c = L->cache;
+    if (!c.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    if (n < 0 || n > c.n_slots - L->d.top_k) return fail(MOE_ERR_ARG, "n must be in 0..n_slots - top_k");
+    if (n > 0 && !experts) return fail(MOE_ERR_ARG, "null experts");
+    for (int i = 0; i < n; ++i) {
+        if (experts[i] < 0 || experts[i] >= L->d.n_experts) return fail(MOE_ERR_ARG, "expert id out of range");
+        for (int j = 0; j < i; ++j)
+            if (experts[j] == experts[i]) return fail(MOE_ERR_ARG, "duplicate expert id");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    std::fill(c.pinned.begin(), c.pinned.end(), 0);
+    ++c.tick;
+    for (int i = 0; i < n; ++i) {
+        const int ex = experts[i];
+        int slot = c.slot_of[ex];
+        if (slot < 0) {
+            for (int q = 0; q < c.n_slots && slot < 0; ++q)
+                if (c.expert_in[q] < 0) slot = q;
+            if (slot < 0) {
+                slot = victim_slot(c, experts, n);  // never one of the set being pinned
+                c.slot_of[c.expert_in[slot]] = -1;
+            }
+            c.expert_in[slot] = ex;
+            c.slot_of[ex] = slot;
+            hipError_t e = hipMemcpyAsync(L->w.slots + (size_t)slot * L->rec_bytes,
+                                          L->w.host_pool + (size_t)ex * L->rec_bytes, L->rec_bytes,
+                                          hipMemcpyHostToDevice, s);
+            if (e != hipSuccess) return hip_fail(e, "pinned expert copy");
+        }
+        c.pinned[slot] = 1;
+        c.last_use[slot] = c.tick;
+    }
     return MOE_OK;
 }
 

@@ -17,13 +17,15 @@ LIB_PATH = os.path.join(HERE, "libmoe_layer.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK = 0
 MOE_SIGMOID_TOPK = 1
+MOE_CACHE_LFU, MOE_CACHE_LRU = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
           -4: "MOE_ERR_HIP", -5: "MOE_ERR_NOMEM", -6: "MOE_ERR_NOT_PINNED",
           -7: "MOE_ERR_STATE", -8: "MOE_ERR_DEVICE"}
 
 EXPORTS = ["moe_expert_record_bytes", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_poll_device_error",
+           "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
+           "moe_poll_device_error",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
            "moe_status_str", "moe_last_error"]
 KERNEL_NAMES = {0: "route", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine", 5: "topk",
@@ -40,7 +42,7 @@ class Desc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("inter", C.c_int32),
                 ("top_k", C.c_int32), ("shared_inter", C.c_int32), ("group", C.c_int32),
                 ("act_dtype", C.c_int32), ("gate_fn", C.c_int32), ("n_slots", C.c_int32),
-                ("routed_scale", C.c_float), ("reserved", C.c_int32 * 6)]
+                ("routed_scale", C.c_float), ("cache_policy", C.c_int32), ("reserved", C.c_int32 * 5)]
 
 
 class Weights(C.Structure):
@@ -72,6 +74,7 @@ def lib() -> C.CDLL:
         L.moe_stack_forward.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, i64, vp, vp]
         L.moe_poll_device_error.argtypes = [vp, vp, vp]
         L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
+        L.moe_cache_pin.argtypes = [vp, C.POINTER(C.c_int32), i32, vp]
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = C.c_char_p
         L.moe_last_error.restype = C.c_char_p
@@ -81,7 +84,7 @@ def lib() -> C.CDLL:
         for f in ["moe_layer_create", "moe_layer_destroy", "moe_route_topk", "moe_expert_ffn",
                   "moe_combine", "moe_layer_forward", "moe_stack_forward",
                   "moe_poll_device_error", "moe_profile_start", "moe_profile_stop",
-                  "moe_cache_stats"]:
+                  "moe_cache_stats", "moe_cache_pin"]:
             getattr(L, f).restype = i32
         _LIB = L
     return _LIB
@@ -127,6 +130,7 @@ class Layer:
                   gates = routed_scale * score / sum over the selection)
     routed_scale  sigmoid gate: the routed scaling factor
     selection_bias  sigmoid gate: float32 CUDA tensor [E] or None
+    cache_policy  slot cache replacement: "lfu" (default) or "lru"
     """
 
     def __init__(self, hidden: int, n_experts: int, inter: int, top_k: int, shared_inter: int,
@@ -134,7 +138,8 @@ class Layer:
                  experts: torch.Tensor | None, shared: torch.Tensor | None, act: str = "bf16",
                  n_slots: int = 0, host_pool: torch.Tensor | None = None,
                  slots: torch.Tensor | None = None, gate: str = "softmax",
-                 routed_scale: float = 1.0, selection_bias: torch.Tensor | None = None):
+                 routed_scale: float = 1.0, selection_bias: torch.Tensor | None = None,
+                 cache_policy: str = "lfu"):
         self.hidden, self.n_experts, self.inter = hidden, n_experts, inter
         self.top_k, self.shared_inter, self.act = top_k, shared_inter, act
         self.n_slots = n_slots
@@ -145,7 +150,7 @@ class Layer:
         d = Desc(hidden, n_experts, inter, top_k, shared_inter, 64,
                  MOE_BF16 if act == "bf16" else MOE_F32,
                  MOE_SIGMOID_TOPK if gate == "sigmoid" else MOE_SOFTMAX_TOPK, n_slots,
-                 float(routed_scale))
+                 float(routed_scale), {"lfu": MOE_CACHE_LFU, "lru": MOE_CACHE_LRU}[cache_policy])
         hp = None
         if host_pool is not None:
             if host_pool.is_cuda or not host_pool.is_pinned() or not host_pool.is_contiguous():
@@ -225,6 +230,11 @@ class Layer:
         h, m = C.c_uint64(), C.c_uint64()
         _check(lib().moe_cache_stats(self.handle, C.byref(h), C.byref(m)))
         return int(h.value), int(m.value)
+
+    def cache_pin(self, experts) -> None:
+        """Pin these expert ids into the slot cache (replacing any pinned set)."""
+        ids = (C.c_int32 * max(len(experts), 1))(*[int(e) for e in experts])
+        _check(lib().moe_cache_pin(self.handle, ids, len(experts), _stream()))
 
     def poll_error(self, ws: torch.Tensor):
         _check(lib().moe_poll_device_error(self.handle, _dev(ws, "workspace"), _stream()))

@@ -78,6 +78,7 @@ enum {
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };                 /* activation / output dtypes */
 enum { MOE_SOFTMAX_TOPK = 0, MOE_SIGMOID_TOPK = 1 }; /* gate functions            */
+enum { MOE_CACHE_LFU = 0, MOE_CACHE_LRU = 1 };       /* slot cache replacement    */
 
 typedef struct moe_layer_desc {
     int32_t hidden;        /* H, multiple of 64, <= 8192                          */
@@ -99,7 +100,9 @@ typedef struct moe_layer_desc {
                               number of HBM expert slots of the slot cache (>= top_k) */
     float routed_scale;    /* MOE_SIGMOID_TOPK: the routed scaling factor (> 0; 0 reads
                               as 1); must be 0 or 1 with MOE_SOFTMAX_TOPK           */
-    int32_t reserved[6];
+    int32_t cache_policy;  /* n_slots > 0: MOE_CACHE_LFU or MOE_CACHE_LRU (see
+                              moe_cache_stats); must be MOE_CACHE_LFU otherwise     */
+    int32_t reserved[5];
 } moe_layer_desc;
 
 typedef struct moe_layer_weights {
@@ -195,8 +198,11 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
  * call (else MOE_ERR_STATE) and synchronise the host on that token's expert
  * ids.  Policy: each selection adds one to its expert's count (never
  * decayed); a miss always enters, into the lowest free slot if any, else in
- * place of the resident expert not selected by the current token with the
- * smallest count, then the least recently used, then the lowest slot.
+ * place of a resident expert that is neither selected by the current token nor
+ * pinned (moe_cache_pin): MOE_CACHE_LFU takes the one with the smallest count,
+ * then the least recently used, then the lowest slot; MOE_CACHE_LRU (the
+ * per-layer LRU of the Colibri README) the least recently used, then the
+ * lowest slot.
  * Misses are copied with hipMemcpyAsync from host_pool on a side stream owned
  * by the handle while the shared expert's gate/up runs; the routed kernels
  * wait for the copies.  The handle owns the side stream, two events and two
@@ -204,6 +210,16 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
  * resident path for the same records.
  * moe_cache_stats returns the hits and misses so far.  Errors: ARG, STATE. */
 moe_status moe_cache_stats(moe_layer_t layer, uint64_t* hits, uint64_t* misses);
+
+/* Pins experts into the slot cache: a static hot set chosen by the caller
+ * (for instance the most used experts of a statistics pass), as the pinned
+ * hot-store of the Colibri README.  experts: host [n] distinct ids in [0, E);
+ * 0 <= n <= n_slots - top_k (a token's misses always find an unpinned slot).
+ * Replaces any previous pinned set.  Experts not resident are copied from
+ * host_pool into free or evicted unpinned slots on `stream` (ordered after
+ * the work already on it); pinned slots are never evicted.  Pinning counts as
+ * neither hit nor miss.  Errors: ARG, STATE (no slot cache), HIP. */
+moe_status moe_cache_pin(moe_layer_t layer, const int32_t* experts, int32_t n, void* stream);
 
 /* Reads and clears the device error flag kept in `workspace` (synchronises
  * `stream`).  MOE_OK if no kernel reported bad input since the last poll,

@@ -61,6 +61,7 @@ FAKE = dict(router_q=0x10000, router_scale=0x20000, experts=0x30000, shared=0x40
     (dict(n_experts=4, top_k=5), -2), (dict(act_dtype=7), -1), (dict(gate_fn=2), -1),
     (dict(routed_scale=2.5), -1), (dict(gate_fn=1, routed_scale=-1.0), -1),
     (dict(gate_fn=1, routed_scale=float("nan")), -1), (dict(gate_fn=1, routed_scale=float("inf")), -1),
+    (dict(cache_policy=2), -1), (dict(cache_policy=1), -1),  # LRU needs a slot cache
     (dict(n_slots=4), -2), (dict(n_slots=16), -1), (dict(n_slots=-1), -2),
 ])
 def test_create_rejects_bad_descriptor(change, status):
@@ -88,6 +89,7 @@ def test_create_rejects_missing_and_misaligned_pointers():
 
 def test_null_handles():
     lib = L.lib()
+    assert lib.moe_cache_pin(None, None, 0, None) == -1
     assert lib.moe_layer_destroy(None) == -1
     assert lib.moe_workspace_bytes(None, 1) == 0
     assert lib.moe_layer_forward(None, None, 1, None, None, None, None, None) == -1

@@ -1,9 +1,10 @@
 """The HBM expert-slot cache (out-of-core decode) through the C ABI (needs a GPU).
 
 * Outputs are bit-identical to the fully resident layer on the same records.
-* Hits and misses equal a CPU simulation of the LFU policy (written here,
-  independently of the library) on the oracle's expert-id stream.
-* An unpinned host pool and multi-token calls are rejected.
+* Hits and misses equal a CPU simulation of the replacement policy (LFU or
+  LRU, with or without a pinned set; written here, independently of the
+  library) on the oracle's expert-id stream.
+* An unpinned host pool, multi-token calls and bad pin requests are rejected.
 """
 import numpy as np
 import pytest
@@ -23,38 +24,58 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def lfu_simulation(id_stream, n_slots, n_experts):
+def cache_simulation(id_stream, n_slots, n_experts, policy="lfu", pin=(), pin_at=0):
     """Counts +1 per selection, never decayed; a miss enters the lowest free slot,
-    else replaces the resident expert not selected by this token with the fewest
-    selections, then least recently used, then lowest slot."""
-    where = {}                      # expert -> slot
-    holder = [None] * n_slots       # slot -> expert
-    uses = [0] * n_experts
-    stamp = [0] * n_slots
-    hits = misses = 0
-    for step, ids in enumerate(id_stream, start=1):
+    else replaces a resident expert that is neither pinned nor selected by this
+    token: LFU the fewest selections, then least recently used, then lowest
+    slot; LRU the least recently used, then lowest slot.  `pin` (applied before
+    token `pin_at`) places its experts into free or evicted slots, never to be
+    evicted.  Returns (hits, misses, hits on pinned experts after pinning)."""
+    where, holder = {}, [None] * n_slots
+    uses, stamp, pinned = [0] * n_experts, [0] * n_slots, [False] * n_slots
+    hits = misses = pinned_hits = 0
+    tick = 0
+
+    def victim(keep):
+        cands = [q for q in range(n_slots)
+                 if holder[q] is not None and not pinned[q] and holder[q] not in keep]
+        if policy == "lru":
+            return min(cands, key=lambda q: (stamp[q], q))
+        return min(cands, key=lambda q: (uses[holder[q]], stamp[q], q))
+
+    def place(e, keep):
+        free = [q for q, h in enumerate(holder) if h is None]
+        q = free[0] if free else victim(keep)
+        if holder[q] is not None:
+            del where[holder[q]]
+        holder[q] = e
+        where[e] = q
+        return q
+
+    for step, ids in enumerate(id_stream):
+        if pin and step == pin_at:
+            tick += 1
+            pinned = [False] * n_slots
+            for e in pin:
+                q = where[e] if e in where else place(e, set(pin))
+                pinned[q] = True
+                stamp[q] = tick
+        tick += 1
         chosen = set(int(e) for e in ids)
         for e in (int(v) for v in ids):
             uses[e] += 1
             if e in where:
                 hits += 1
-                s = where[e]
+                q = where[e]
+                pinned_hits += int(pinned[q])
             else:
                 misses += 1
-                free = [q for q, h in enumerate(holder) if h is None]
-                if free:
-                    s = free[0]
-                else:
-                    s = min((q for q in range(n_slots) if holder[q] not in chosen),
-                            key=lambda q: (uses[holder[q]], stamp[q], q))
-                    del where[holder[s]]
-                holder[s] = e
-                where[e] = s
-            stamp[s] = step
-    return hits, misses
+                q = place(e, chosen)
+            stamp[q] = tick
+    return hits, misses, pinned_hits
 
 
-def cached_twin(dl, n_slots):
+def cached_twin(dl, n_slots, policy="lfu"):
     """A slot-cached layer over the same record bytes as DeviceLayer dl."""
     from bit_routed_expert_moe_amd import Layer, record_bytes
     host = torch.empty(dl.pool.numel(), dtype=torch.uint8, pin_memory=True)
@@ -63,21 +84,30 @@ def cached_twin(dl, n_slots):
     rq = torch.from_numpy(dl.rq).cuda()
     rs = torch.from_numpy(dl.rs.view(np.float16)).cuda()
     return Layer(dl.H, dl.E, dl.I, dl.k, dl.Is, rq, rs, None, dl.shared, act=dl.act,
-                 n_slots=n_slots, host_pool=host, slots=slots), host, slots
+                 n_slots=n_slots, host_pool=host, slots=slots, cache_policy=policy), host, slots
 
 
-@pytest.mark.parametrize("zipf", [False, True])
-def test_cached_layer_matches_resident_and_lfu(orc, zipf):
+@pytest.mark.parametrize("policy,zipf,pin", [
+    ("lfu", False, False), ("lfu", True, False), ("lru", True, False),
+    ("lfu", True, True), ("lru", True, True),
+])
+def test_cached_layer_matches_resident_and_policy(orc, policy, zipf, pin):
+    """48 decode steps; with `pin`, the 4 most used experts of the first 16
+    steps (a statistics pass) are pinned before step 16."""
     H, E, I, k, Is, n_slots = 512, 48, 192, 8, 256, 12
     dl = DeviceLayer(0xB17E0500 + zipf, 0, H, E, I, k, Is, "bf16")
-    cached, _, _ = cached_twin(dl, n_slots)
+    cached, _, _ = cached_twin(dl, n_slots, policy)
     zr = None
     if zipf:
         Wd = dl.rq.astype(np.float64) * dl.rs.view(np.float16).astype(np.float64)[:, None]
         zr = synth.ZipfRealiser(Wd, 1.1, dl.seed, 0)
     ws_r, ws_c = dl.layer_obj.workspace(1), cached.workspace(1)
-    oracle_ids = []
+    oracle_ids, pinned = [], ()
     for step in range(48):
+        if pin and step == 16:
+            counts = np.bincount(np.concatenate(oracle_ids), minlength=E)
+            pinned = tuple(int(e) for e in sorted(range(E), key=lambda e: (-counts[e], e))[:n_slots - k])
+            cached.cache_pin(pinned)
         if zr is None:
             xq, xd = dl.natural_token(orc, step)
         else:
@@ -94,9 +124,14 @@ def test_cached_layer_matches_resident_and_lfu(orc, zipf):
             assert torch.equal(a_, b_), f"step {step}: cached result differs from resident"
         assert r[0].cpu().numpy()[0].tolist() == oracle_ids[-1].tolist()
     hits, misses = cached.cache_stats()
-    assert (hits, misses) == lfu_simulation(oracle_ids, n_slots, E)
+    sim = cache_simulation(oracle_ids, n_slots, E, policy, pinned, 16)
+    assert (hits, misses) == sim[:2]
     assert hits + misses == 48 * k
-    print(f"zipf={zipf}: hits {hits} misses {misses} hit rate {hits / (hits + misses):.3f}")
+    if pin:  # every later selection of a pinned expert was a hit
+        later = sum(int(e in pinned) for ids in oracle_ids[16:] for e in ids)
+        assert sim[2] == later > 0
+    print(f"{policy} zipf={zipf} pin={len(pinned)}: hits {hits} misses {misses} "
+          f"hit rate {hits / (hits + misses):.3f}")
 
 
 def test_cached_api_expert_outputs_match_resident(orc):
@@ -128,4 +163,11 @@ def test_cache_rejects_unpinned_pool_and_batches():
     x = to_dev(synth.quantize_act(synth.activations(3, 0, 0, 256, n_tokens=2), "bf16"), "bf16")
     with pytest.raises(MoeError) as ei:
         cached.forward(x)
+    assert ei.value.status == -7
+    for bad in ([0, 1, 2, 3, 4], [1, 1], [16], [-1]):  # more than n_slots - k, duplicate, out of range
+        with pytest.raises(MoeError) as ei:
+            cached.cache_pin(bad)
+        assert ei.value.status == -1, bad
+    with pytest.raises(MoeError) as ei:
+        dl.layer_obj.cache_pin([0])  # no slot cache
     assert ei.value.status == -7
