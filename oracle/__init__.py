@@ -47,7 +47,10 @@ class Oracle:
         L.oracle_act_to_f64.argtypes = [C.c_int, C.c_void_p, C.c_int64, _dp]
         L.oracle_record_bytes.argtypes = [C.c_int, C.c_int]
         L.oracle_record_bytes.restype = C.c_size_t
+        L.oracle_record_bytes_bits.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.oracle_record_bytes_bits.restype = C.c_size_t
         L.oracle_dequant_record.argtypes = [C.c_int, C.c_int, _u8p, _dp, _dp, _dp]
+        L.oracle_dequant_record_bits.argtypes = [C.c_int, C.c_int, C.c_int, _u8p, _dp, _dp, _dp]
         L.oracle_router_logits.argtypes = [C.c_int, C.c_int, _i8p, _u16p, _dp, _dp]
         L.oracle_select_topk.argtypes = [C.c_int, C.c_int, _dp, _i32p]
         L.oracle_softmax_gates.argtypes = [C.c_int, _dp, _dp]
@@ -56,6 +59,8 @@ class Oracle:
         L.oracle_silu.restype = C.c_double
         L.oracle_expert_ffn.argtypes = [C.c_int, C.c_int, _u8p, _dp, _dp,
                                         _opt(_dp), _opt(_dp), _opt(_dp)]
+        L.oracle_expert_ffn_bits.argtypes = [C.c_int, C.c_int, C.c_int, _u8p, _dp, _dp,
+                                             _opt(_dp), _opt(_dp), _opt(_dp)]
         L.oracle_combine.argtypes = [C.c_int, C.c_int, _dp, _dp, _opt(_dp), _dp]
         L.oracle_layer_token.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                          _i8p, _u16p, _u8p, _opt(_u8p), _dp, _i32p, _dp,
@@ -84,13 +89,19 @@ class Oracle:
         self.lib.oracle_act_to_f64(code, src.ctypes.data, src.size, out)
         return out
 
-    def record_bytes(self, H: int, I: int) -> int:
-        return int(self.lib.oracle_record_bytes(H, I))
+    def record_bytes(self, H: int, I: int, bits: int = 4) -> int:
+        if bits == 4:
+            return int(self.lib.oracle_record_bytes(H, I))
+        return int(self.lib.oracle_record_bytes_bits(bits, H, I))
 
     # -- the method --------------------------------------------------------
-    def dequant_record(self, H: int, I: int, rec: np.ndarray):
+    def dequant_record(self, H: int, I: int, rec: np.ndarray, bits: int = 4):
         G = np.empty((I, H)); U = np.empty((I, H)); D = np.empty((H, I))
-        self.lib.oracle_dequant_record(H, I, np.ascontiguousarray(rec, dtype=np.uint8), G, U, D)
+        r = np.ascontiguousarray(rec, dtype=np.uint8)
+        if bits == 4:
+            self.lib.oracle_dequant_record(H, I, r, G, U, D)
+        else:
+            self.lib.oracle_dequant_record_bits(bits, H, I, r, G, U, D)
         return G, U, D
 
     def router_logits(self, rq: np.ndarray, rs: np.ndarray, x: np.ndarray) -> np.ndarray:
@@ -117,13 +128,17 @@ class Oracle:
         return self.lib.oracle_silu(float(v))
 
     def expert_ffn(self, H: int, I: int, rec: np.ndarray, x: np.ndarray,
-                   intermediates: bool = False):
+                   intermediates: bool = False, bits: int = 4):
         y = np.empty(H)
         g = np.empty(I) if intermediates else None
         u = np.empty(I) if intermediates else None
         h = np.empty(I) if intermediates else None
-        self.lib.oracle_expert_ffn(H, I, np.ascontiguousarray(rec, dtype=np.uint8),
-                                   np.ascontiguousarray(x, dtype=np.float64), y, g, u, h)
+        r = np.ascontiguousarray(rec, dtype=np.uint8)
+        xx = np.ascontiguousarray(x, dtype=np.float64)
+        if bits == 4:
+            self.lib.oracle_expert_ffn(H, I, r, xx, y, g, u, h)
+        else:
+            self.lib.oracle_expert_ffn_bits(bits, H, I, r, xx, y, g, u, h)
         return (y, g, u, h) if intermediates else y
 
     def combine(self, w: np.ndarray, y_routed: np.ndarray, y_shared: np.ndarray | None):

@@ -49,6 +49,16 @@
  *     +4*H    (scale, bias) fp16 pairs of GU tile 2g+1: same order
  *     +8*H    (scale, bias) fp16 pairs of D[o][64g .. 64g+64) for o < H
  *   A weight is  W = scale * q + bias,  q the nibble in 0..15.
+ *
+ * The 2-bit variant (our own format: the pages name 2-bit models but define
+ * no 2-bit container) keeps the structure with 64 inputs per 16-byte run,
+ * input 4m+j in bits [2j, 2j+2) of byte m, q in 0..3:
+ *   code region, 3*H*I/4 bytes, I/32 blocks of 24*H bytes; block b holds
+ *   rows i in [32b, 32b+32):
+ *     +0      GU tile: for chunk c < H/64, for tile row r < 64: 16 bytes =
+ *             inputs [64c, 64c+64) of G row 32b+r (r < 32) or U row 32b+r-32
+ *     +16*H   D block: for output row o < H: 8 bytes = D[o][32b .. 32b+32)
+ *   scale/bias region at 3*H*I/4, laid out as for 4 bits.
  */
 #include <math.h>
 #include <stddef.h>
@@ -135,6 +145,37 @@ static int q_down(const uint8_t *rec, int H, int o, int i)
     return nibble_at(rec, off, e);
 }
 
+/* 2-bit codes: input e of a run sits in bits [2(e%4), 2(e%4)+2) of byte e/4 */
+static int crumb_at(const uint8_t *rec, size_t byte_off, int elem)
+{
+    return (rec[byte_off] >> (2 * (elem & 3))) & 3;
+}
+
+static int q_gate_up2(const uint8_t *rec, int H, int which, int i, int k)
+{
+    int b = i / 32, r = i % 32 + 32 * which, c = k / 64, e = k % 64;
+    size_t off = (size_t)24 * H * b + (size_t)c * 1024 + (size_t)r * 16 + e / 4;
+    return crumb_at(rec, off, e);
+}
+
+static int q_down2(const uint8_t *rec, int H, int o, int i)
+{
+    int b = i / 32, e = i % 32;
+    size_t off = (size_t)24 * H * b + (size_t)16 * H + (size_t)o * 8 + e / 4;
+    return crumb_at(rec, off, e);
+}
+
+/* the code width in use: 4 (nibbles) or 2 */
+static int q_gu(int bits, const uint8_t *rec, int H, int which, int i, int k)
+{
+    return bits == 2 ? q_gate_up2(rec, H, which, i, k) : q_gate_up(rec, H, which, i, k);
+}
+
+static int q_d(int bits, const uint8_t *rec, int H, int o, int i)
+{
+    return bits == 2 ? q_down2(rec, H, o, i) : q_down(rec, H, o, i);
+}
+
 static void sb_read(const uint8_t *rec, size_t off, double *s, double *bias)
 {
     uint16_t sv, bv;
@@ -145,44 +186,56 @@ static void sb_read(const uint8_t *rec, size_t off, double *s, double *bias)
 }
 
 /* scale/bias of gate (which = 0) or up (which = 1) row i, input group h */
-static void sb_gate_up(const uint8_t *rec, int H, int I, int which, int i, int h,
+static void sb_gate_up(const uint8_t *rec, size_t sb0, int H, int which, int i, int h,
                        double *s, double *bias)
 {
     int g = i / 64, tile = (i / 32) % 2, r = i % 32 + 32 * which;
-    size_t off = sb_region(H, I) + (size_t)12 * H * g + (size_t)4 * H * tile
+    size_t off = sb0 + (size_t)12 * H * g + (size_t)4 * H * tile
                + (size_t)h * 256 + (size_t)r * 4;
     sb_read(rec, off, s, bias);
 }
 
-static void sb_down(const uint8_t *rec, int H, int I, int o, int g, double *s, double *bias)
+static void sb_down(const uint8_t *rec, size_t sb0, int H, int o, int g, double *s, double *bias)
 {
-    size_t off = sb_region(H, I) + (size_t)12 * H * g + (size_t)8 * H + (size_t)o * 4;
+    size_t off = sb0 + (size_t)12 * H * g + (size_t)8 * H + (size_t)o * 4;
     sb_read(rec, off, s, bias);
 }
 
-size_t oracle_record_bytes(int H, int I)
+/* start of the scale/bias region: after 3*H*I*bits/8 code bytes */
+static size_t sb_start(int bits, int H, int I) { return bits == 2 ? sb_region(H, I) / 2 : sb_region(H, I); }
+
+size_t oracle_record_bytes_bits(int bits, int H, int I)
 {
-    return sb_region(H, I) + (size_t)(I / 64) * 12 * H;
+    return sb_start(bits, H, I) + (size_t)(I / 64) * 12 * H;
 }
+
+size_t oracle_record_bytes(int H, int I) { return oracle_record_bytes_bits(4, H, I); }
 
 /* Dense dequantisation of one record: W = scale * q + bias per 64-group of the
  * input dim.  G, U are [I][H] row-major, D is [H][I].  Pinned against an
  * independently written packer and its dense source matrices. */
-void oracle_dequant_record(int H, int I, const uint8_t *rec, double *G, double *U, double *D)
+void oracle_dequant_record_bits(int bits, int H, int I, const uint8_t *rec, double *G, double *U,
+                                double *D)
 {
     double s, bias;
+    const size_t sb0 = sb_start(bits, H, I);
     for (int i = 0; i < I; ++i)
         for (int k = 0; k < H; ++k) {
-            sb_gate_up(rec, H, I, 0, i, k / 64, &s, &bias);
-            G[(size_t)i * H + k] = s * q_gate_up(rec, H, 0, i, k) + bias;
-            sb_gate_up(rec, H, I, 1, i, k / 64, &s, &bias);
-            U[(size_t)i * H + k] = s * q_gate_up(rec, H, 1, i, k) + bias;
+            sb_gate_up(rec, sb0, H, 0, i, k / 64, &s, &bias);
+            G[(size_t)i * H + k] = s * q_gu(bits, rec, H, 0, i, k) + bias;
+            sb_gate_up(rec, sb0, H, 1, i, k / 64, &s, &bias);
+            U[(size_t)i * H + k] = s * q_gu(bits, rec, H, 1, i, k) + bias;
         }
     for (int o = 0; o < H; ++o)
         for (int i = 0; i < I; ++i) {
-            sb_down(rec, H, I, o, i / 64, &s, &bias);
-            D[(size_t)o * I + i] = s * q_down(rec, H, o, i) + bias;
+            sb_down(rec, sb0, H, o, i / 64, &s, &bias);
+            D[(size_t)o * I + i] = s * q_d(bits, rec, H, o, i) + bias;
         }
+}
+
+void oracle_dequant_record(int H, int I, const uint8_t *rec, double *G, double *U, double *D)
+{
+    oracle_dequant_record_bits(4, H, I, rec, G, U, D);
 }
 
 /* ---- the layer --------------------------------------------------------- */
@@ -274,19 +327,20 @@ double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
  * element of the group as W = scale * q + bias.  Rows are independent, so the
  * row loops may run on several threads (OpenMP) without changing any sum.
  * Optional outputs g, u, h (length I) for the pins; pass NULL to skip. */
-void oracle_expert_ffn(int H, int I, const uint8_t *rec, const double *x, double *y,
-                       double *g_out, double *u_out, double *h_out)
+void oracle_expert_ffn_bits(int bits, int H, int I, const uint8_t *rec, const double *x,
+                            double *y, double *g_out, double *u_out, double *h_out)
 {
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    const size_t sb0 = sb_start(bits, H, I);
     #pragma omp parallel for schedule(static)
     for (int i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0, sg, bg, su, bu;
         for (int grp = 0; grp < H / 64; ++grp) {
-            sb_gate_up(rec, H, I, 0, i, grp, &sg, &bg);
-            sb_gate_up(rec, H, I, 1, i, grp, &su, &bu);
+            sb_gate_up(rec, sb0, H, 0, i, grp, &sg, &bg);
+            sb_gate_up(rec, sb0, H, 1, i, grp, &su, &bu);
             for (int k = 64 * grp; k < 64 * grp + 64; ++k) {
-                g += (sg * q_gate_up(rec, H, 0, i, k) + bg) * x[k];
-                u += (su * q_gate_up(rec, H, 1, i, k) + bu) * x[k];
+                g += (sg * q_gu(bits, rec, H, 0, i, k) + bg) * x[k];
+                u += (su * q_gu(bits, rec, H, 1, i, k) + bu) * x[k];
             }
         }
         h[i] = oracle_silu(g) * u;
@@ -298,13 +352,19 @@ void oracle_expert_ffn(int H, int I, const uint8_t *rec, const double *x, double
     for (int o = 0; o < H; ++o) {
         double acc = 0.0, s, bias;
         for (int grp = 0; grp < I / 64; ++grp) {
-            sb_down(rec, H, I, o, grp, &s, &bias);
+            sb_down(rec, sb0, H, o, grp, &s, &bias);
             for (int i = 64 * grp; i < 64 * grp + 64; ++i)
-                acc += (s * q_down(rec, H, o, i) + bias) * h[i];
+                acc += (s * q_d(bits, rec, H, o, i) + bias) * h[i];
         }
         y[o] = acc;
     }
     free(h);
+}
+
+void oracle_expert_ffn(int H, int I, const uint8_t *rec, const double *x, double *y,
+                       double *g_out, double *u_out, double *h_out)
+{
+    oracle_expert_ffn_bits(4, H, I, rec, x, y, g_out, u_out, h_out);
 }
 
 /* y = sum_j w_j * y_routed[j] + y_shared, summed in the order j = 0..k-1 and

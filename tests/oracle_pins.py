@@ -71,6 +71,32 @@ def pin_dequant_matches_packer(orc):
             f"dequant mismatch at H={H} I={I}"
 
 
+def pin_two_bit_format(orc):
+    """The 2-bit variant: dequantisation of packed bytes equals scale*q+bias of
+    the source (q in 0..3), the record is 15HI/16 bytes, one expert equals the
+    dense SwiGLU with library matmuls, and constant codes give the closed form."""
+    rng = np.random.default_rng(22)
+    for H, I in [(64, 64), (128, 192), (256, 128), (320, 64)]:
+        ex = DenseExpert(H, I, rng, s_range=(-0.02, 0.02), b_range=(-0.01, 0.01), bits=2)
+        assert orc.record_bytes(H, I, bits=2) == ex.rec.size == 15 * H * I // 16
+        G, U, D = orc.dequant_record(H, I, ex.rec, bits=2)
+        assert np.array_equal(G, ex.G) and np.array_equal(U, ex.U) and np.array_equal(D, ex.D), \
+            f"2-bit dequant mismatch at H={H} I={I}"
+        x = rng.standard_normal(H)
+        _close(orc.expert_ffn(H, I, ex.rec, x, bits=2), ex.ffn(x), 1e-12, what=f"2-bit ffn H={H}")
+    H, I, c, s, b = 128, 64, 3, 2.0 ** -6, -(2.0 ** -9)
+    f16 = lambda v, shape: np.full(shape, np.float16(v)).view(np.uint16)
+    sb = (f16(s, (I, H // 64)), f16(b, (I, H // 64)), f16(s, (I, H // 64)), f16(b, (I, H // 64)),
+          f16(s, (H, I // 64)), f16(b, (H, I // 64)))
+    ex = DenseExpert(H, I, rng, qG=np.full((I, H), c), qU=np.full((I, H), c),
+                     qD=np.full((H, I), c), sb=sb, bits=2)
+    x = rng.standard_normal(H)
+    gamma = (s * c + b) * x.sum()
+    h = gamma / (1.0 + math.exp(-gamma)) * gamma
+    _close(orc.expert_ffn(H, I, ex.rec, x, bits=2), np.full(H, (s * c + b) * I * h), 1e-12,
+           what="2-bit closed form")
+
+
 def pin_one_hot_columns(orc):
     """x = e_k reads out column k of G and U exactly; y reads D times h."""
     rng = np.random.default_rng(3)

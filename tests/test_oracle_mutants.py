@@ -21,8 +21,8 @@ MUTANTS = {
     "gate_up_rows_swapped": ("int b = i / 32, r = i % 32 + 32 * which, c = k / 32, e = k % 32;",
                              "int b = i / 32, r = i % 32 + 32 * (1 - which), c = k / 32, e = k % 32;"),
     "chunk_stride": ("(size_t)c * 1024", "(size_t)c * 512"),
-    "down_bias_dropped": ("acc += (s * q_down(rec, H, o, i) + bias) * h[i];",
-                          "acc += (s * q_down(rec, H, o, i)) * h[i];"),
+    "down_bias_dropped": ("acc += (s * q_d(bits, rec, H, o, i) + bias) * h[i];",
+                          "acc += (s * q_d(bits, rec, H, o, i)) * h[i];"),
     "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
     "gate_up_roles_swapped": ("h[i] = oracle_silu(g) * u;", "h[i] = oracle_silu(u) * g;"),
     "topk_tie_breaks_high_id": ("logits[e] > logits[best]", "logits[e] >= logits[best]"),
@@ -37,6 +37,12 @@ MUTANTS = {
                           "(size_t)48 * H * b + (size_t)16 * H + (size_t)o * 16"),
     "shared_dropped": ("acc += y_shared[o];", "acc += 0.0 * y_shared[o];"),
     "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "crumb_order_reversed": ("return (rec[byte_off] >> (2 * (elem & 3))) & 3;",
+                             "return (rec[byte_off] >> (6 - 2 * (elem & 3))) & 3;"),
+    "two_bit_chunk_width": ("c = k / 64, e = k % 64;", "c = k / 32, e = k % 32;"),
+    "two_bit_down_stride": ("(size_t)16 * H + (size_t)o * 8 + e / 4", "(size_t)16 * H + (size_t)o * 16 + e / 4"),
+    "two_bit_down_block_offset": ("(size_t)24 * H * b + (size_t)16 * H + (size_t)o * 8",
+                                  "(size_t)24 * H * b + (size_t)8 * H + (size_t)o * 8"),
     "sigmoid_gates_use_bias": ("w[j] = 1.0 / (1.0 + exp(-logits[ids[j]]));",
                                "w[j] = key[ids[j]];"),
     "sigmoid_scale_dropped": ("w[j] = scale * (w[j] / z);", "w[j] = w[j] / z;"),
