@@ -24,6 +24,7 @@ namespace moe {
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
@@ -38,6 +39,20 @@ __device__ __forceinline__ void dot_nib8(uint32_t w, const uint32_t* x, float& a
     acc1 = dot2((w & 0x00F000F0u) | M, x[1], acc1);
     acc0 = dot2((w8 & 0x000F000Fu) | M, x[2], acc0);
     acc1 = dot2((w8 & 0x00F000F0u) | M, x[3], acc1);
+}
+
+// 2-bit codes: a dword w holds 16 codes, input i in bits [2i, 2i+2).  Shifting
+// field j to bit 0 and or-ing 0x6400 gives the fp16 pair (1024 + q_j,
+// 1024 + q_{8+j}) (low and high halves), j = 0..7, paired with the
+// activation dwords x[j] = (a_j, a_{8+j}); no scaling of the activations.
+// acc0 gathers the even j, acc1 the odd j.
+__device__ __forceinline__ void dot_crumb16(uint32_t w, const uint32_t* x, float& acc0, float& acc1) {
+    const uint32_t M = 0x64006400u;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        acc0 = dot2(((w >> (2 * j)) & 0x00030003u) | M, x[j], acc0);
+        acc1 = dot2(((w >> (2 * j + 2)) & 0x00030003u) | M, x[j + 1], acc1);
+    }
 }
 
 __device__ __forceinline__ float f16lo(uint32_t v) {

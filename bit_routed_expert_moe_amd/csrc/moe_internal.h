@@ -43,6 +43,7 @@ struct RouteArgs {
     float rscale;            // sigmoid gate: routed scaling factor
     int H, E, k, prep, T;
     int gate;                // 0 softmax, 1 sigmoid
+    int bits;                // weight code width: 4 or 2 (activation pair order)
 };
 
 struct FfnArgs {
@@ -84,6 +85,9 @@ struct FfnArgs {
     int gi;                  // input groups (of I) per routed down item (= I/64)
     int gis;                 // input groups per shared down item
     int gpw_dn;              // input groups per wave in the down kernel
+    int bits;                // weight code width: 4 or 2
+    size_t sb_off;           // start of a routed record's scale/bias region
+    size_t sb_off_shared;    // the same for the shared record
 };
 
 constexpr int kTileRows = 16;         // rows (tokens) per MFMA tile in the prefill path

@@ -34,30 +34,33 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // activation preparation of one 64-input group by one wave (lane = input).
 // Each group gets its own power-of-two scale 2^e so that its largest value
-// lands below 2^14 in fp16; odd positions of each 8-set are also divided by 16
-// to pair with the x16 nibble slots.  Writes the group's 16*XP pair dwords,
-// K = 1024 * sum of the fp16 values (in double), X = sum of the inputs and
-// inv = 2^-e.
+// lands below 2^14 in fp16.  4-bit weights: odd positions of each 8-set are
+// also divided by 16 to pair with the x16 nibble slots, pairs (a_p, a_{p+4})
+// per 8-set; 2-bit weights: pairs (a_j, a_{j+8}) per 16-set, unscaled.
+// Writes the group's 16*XP pair dwords, K = 1024 * sum of the fp16 values (in
+// double), X = sum of the inputs and inv = 2^-e.
 // ---------------------------------------------------------------------------
-template <int XP, bool BF16>
+template <int XP, bool BF16, int BITS>
 __device__ void prep_group(const void* x, int t, int H, int g, uint32_t* pairs, float* K,
                            float* X, float* inv) {
     const int lane = threadIdx.x & 63;
     const size_t i = (size_t)t * H + 64 * g + lane;
     const float v = BF16 ? bf16_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
     const int e = act_exponent(wave_max(fabsf(v)));
-    const int p = lane & 7, set = lane >> 3;
-    const float vs = v * ldexpf(1.0f, e) * ((p & 1) ? 0.0625f : 1.0f);
+    constexpr int SET = BITS == 4 ? 8 : 16;  // inputs per pairing set
+    constexpr int PD = SET / 2;              // pair dwords per set and part
+    const int p = lane % SET, set = lane / SET;
+    const float vs = v * ldexpf(1.0f, e) * ((BITS == 4 && (p & 1)) ? 0.0625f : 1.0f);
     const _Float16 hi = (_Float16)vs;
     const _Float16 lo = (_Float16)(vs - (float)hi);
     const double kd = wave_sum_d((double)(float)hi + (XP == 2 ? (double)(float)lo : 0.0));
     const float xs = wave_sum(v);
     const uint32_t bh = __builtin_bit_cast(uint16_t, hi), bl = __builtin_bit_cast(uint16_t, lo);
-    const uint32_t ph = __shfl_down(bh, 4, 64), pl = __shfl_down(bl, 4, 64);
+    const uint32_t ph = __shfl_down(bh, PD, 64), pl = __shfl_down(bl, PD, 64);
     uint32_t* gp = pairs + ((size_t)t * (H / 8) + 8 * g) * XP * 4;
-    if (p < 4) {
-        gp[(set * XP + 0) * 4 + p] = bh | (ph << 16);
-        if (XP == 2) gp[(set * XP + 1) * 4 + p] = bl | (pl << 16);
+    if (p < PD) {
+        gp[(set * XP + 0) * PD + p] = bh | (ph << 16);
+        if (XP == 2) gp[(set * XP + 1) * PD + p] = bl | (pl << 16);
     }
     if (lane == 0) {
         const size_t gi = (size_t)t * (H / 64) + g;
@@ -201,13 +204,13 @@ __device__ __forceinline__ int topk_select(const float* lg, int E, int k, int wa
 // ---------------------------------------------------------------------------
 constexpr int kRouterChunksPerLane = kMaxHidden / 16 / 64;  // 16-byte chunks per lane
 
-template <int XP, bool BF16>
+template <int XP, bool BF16, int BITS>
 __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int rb = (a.E + kWaves * kRouterRowsPerWave - 1) / (kWaves * kRouterRowsPerWave);
     if ((int)blockIdx.x >= rb) {  // activation preparation blocks (one token each)
         const int g = ((int)blockIdx.x - rb) * kWaves + wave;
-        if (g < a.H / 64) prep_group<XP, BF16>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+        if (g < a.H / 64) prep_group<XP, BF16, BITS>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
         return;
     }
     const int row0 = (blockIdx.x * kWaves + wave) * kRouterRowsPerWave;
@@ -285,10 +288,10 @@ __global__ __launch_bounds__(64) void k_topk(RouteArgs a) {
 }
 
 // k_prep: grid (ceil(H/256), T); one wave per 64-input group.
-template <int XP, bool BF16>
+template <int XP, bool BF16, int BITS>
 __global__ __launch_bounds__(kBlock) void k_prep(RouteArgs a) {
     const int g = blockIdx.x * kWaves + wave_id();
-    if (g < a.H / 64) prep_group<XP, BF16>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+    if (g < a.H / 64) prep_group<XP, BF16, BITS>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kBlock) void k_prep(RouteArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kXPrepVecsPerThread = kMaxHidden / 8 * 2 / kBlock;  // 16-byte vectors
 
-template <int XP, int MAXG, int Q>
+template <int XP, int MAXG, int Q, int BITS>
 __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     extern __shared__ uint32_t smem[];
     const int H = a.H, NG = H / 64;
@@ -354,8 +357,11 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
         rec = a.shared;
         Ie = a.Is;
     }
-    const uint8_t* tile = rec + (size_t)48 * H * b + (size_t)lane * 16;
-    const uint8_t* sbt = rec + (size_t)3 * H * Ie / 2 + (size_t)12 * H * (b >> 1) +
+    // a 32-row block is 48*H bytes of nibbles (a 64-input group = two 16-byte
+    // chunks per tile row) or 24*H bytes of 2-bit codes (one chunk per group)
+    constexpr int NW = BITS == 4 ? 2 : 1;
+    const uint8_t* tile = rec + (size_t)(BITS == 4 ? 48 : 24) * H * b + (size_t)lane * 16;
+    const uint8_t* sbt = rec + (routed ? a.sb_off : a.sb_off_shared) + (size_t)12 * H * (b >> 1) +
                          (size_t)4 * H * (b & 1) + (size_t)lane * 4;
     const int g0 = wave * a.gpw_gu;
     const int g1 = min(NG, g0 + a.gpw_gu);
@@ -364,13 +370,13 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     // unconditional (clamped to a valid group) and kept in program order, so
     // each group's compute waits only for that group's loads.
     constexpr int D = kDepth < MAXG ? kDepth : MAXG;
-    u32x4 W[D][2];
+    u32x4 W[D][NW];
     uint32_t SB[D];
 #pragma unroll
     for (int q = 0; q < D; ++q) {
         const int g = min(g0 + q, NG - 1);
-        W[q][0] = ldg_nt((const u32x4*)(tile + (size_t)(2 * g) * 1024));
-        W[q][1] = ldg_nt((const u32x4*)(tile + (size_t)(2 * g + 1) * 1024));
+#pragma unroll
+        for (int c = 0; c < NW; ++c) W[q][c] = ldg_nt((const u32x4*)(tile + (size_t)(NW * g + c) * 1024));
         SB[q] = ldg_nt((const uint32_t*)(sbt + (size_t)g * 256));
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -395,14 +401,24 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
         const int g = g0 + q;
         if (g < g1) {
             float a0 = 0.0f, a1 = 0.0f;
+            if constexpr (BITS == 4) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const u32x4 wv = W[slot][half];
-                const uint32_t* xc = xp + (size_t)(2 * g + half) * 16 * XP;
+                for (int half = 0; half < 2; ++half) {
+                    const u32x4 wv = W[slot][half];
+                    const uint32_t* xc = xp + (size_t)(2 * g + half) * 16 * XP;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                        for (int p = 0; p < XP; ++p) dot_nib8(wv[m], xc + (m * XP + p) * 4, a0, a1);
+                    }
+                }
+            } else {
+                const u32x4 wv = W[slot][0];
+                const uint32_t* xc = xp + (size_t)g * 32 * XP;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                    for (int p = 0; p < XP; ++p) dot_nib8(wv[m], xc + (m * XP + p) * 4, a0, a1);
+                    for (int p = 0; p < XP; ++p) dot_crumb16(wv[m], xc + (m * XP + p) * 8, a0, a1);
                 }
             }
             rs = fmaf(f16lo(SB[slot]) * sI[g], (a0 + a1) - sK[g], rs);
@@ -410,8 +426,8 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
         }
         if (q + D < MAXG) {  // refill the slot just consumed
             const int gn = min(g0 + q + D, NG - 1);
-            W[slot][0] = ldg_nt((const u32x4*)(tile + (size_t)(2 * gn) * 1024));
-            W[slot][1] = ldg_nt((const u32x4*)(tile + (size_t)(2 * gn + 1) * 1024));
+#pragma unroll
+            for (int c = 0; c < NW; ++c) W[slot][c] = ldg_nt((const u32x4*)(tile + (size_t)(NW * gn + c) * 1024));
             SB[slot] = ldg_nt((const uint32_t*)(sbt + (size_t)gn * 256));
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -434,20 +450,23 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     if (bad && lane == 0) atomicOr(a.err, 1u);
     const float mx = wave_max(lane < 32 ? fabsf(h) : 0.0f);
     const int e = act_exponent(mx);
-    const int p = lane & 7, set = lane >> 3;
-    const float v = h * ldexpf(1.0f, e) * ((p & 1) ? 0.0625f : 1.0f);
+    // h pairs as the activations: (h_p, h_{p+4}) per 8-set with odd p / 16 for
+    // nibbles; (h_p, h_{p+8}) per 16-set, unscaled, for 2-bit codes
+    constexpr int SET = BITS == 4 ? 8 : 16, PD = SET / 2;
+    const int p = lane % SET, set = lane / SET;
+    const float v = h * ldexpf(1.0f, e) * ((BITS == 4 && (p & 1)) ? 0.0625f : 1.0f);
     const _Float16 hh = (_Float16)v;
     const _Float16 hl = (_Float16)(v - (float)hh);
     double kd = lane < 32 ? (double)(float)hh + (kHParts == 2 ? (double)(float)hl : 0.0) : 0.0;
     kd = wave_sum_d(kd);
     const float hs = wave_sum(lane < 32 ? h : 0.0f);
     const uint32_t bh = __builtin_bit_cast(uint16_t, hh), bl = __builtin_bit_cast(uint16_t, hl);
-    const uint32_t ph = __shfl_down(bh, 4, 64), pl = __shfl_down(bl, 4, 64);
+    const uint32_t ph = __shfl_down(bh, PD, 64), pl = __shfl_down(bl, PD, 64);
     const size_t slot = ((size_t)t * (a.k + 1) + j) * a.blk_max + b;
     uint32_t* hp = a.hpairs + slot * (16 * kHParts);
-    if (lane < 32 && p < 4) {
-        hp[(set * kHParts + 0) * 4 + p] = bh | (ph << 16);
-        if (kHParts == 2) hp[(set * kHParts + 1) * 4 + p] = bl | (pl << 16);
+    if (lane < 32 && p < PD) {
+        hp[(set * kHParts + 0) * PD + p] = bh | (ph << 16);
+        if (kHParts == 2) hp[(set * kHParts + 1) * PD + p] = bl | (pl << 16);
     }
     if (lane == 0) {
         a.hK[slot] = bad ? __builtin_nanf("") : (float)(1024.0 * kd);
@@ -460,8 +479,12 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
 // k_down: grid (n_otiles * n_items, T).  Lane = output row of a 64-row tile;
 // waves split the item's input groups (64 inputs of I = two h blocks).
 // ---------------------------------------------------------------------------
-template <int MAXG>
+template <int BITS> struct DownRow { typedef u32x4 T; };  // 32 nibbles of one row
+template <> struct DownRow<2> { typedef u32x2 T; };        // 32 2-bit codes
+
+template <int MAXG, int BITS>
 __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
+    typedef typename DownRow<BITS>::T RowT;
     extern __shared__ uint32_t smem[];
     const int H = a.H;
     const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -488,8 +511,11 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     const int o = ot * 64 + lane;
     const int g0 = ga + wave * a.gpw_dn;
     const int g1 = min(gb, g0 + a.gpw_dn);
-    const uint8_t* dblk = rec + (size_t)32 * H + (size_t)o * 16;
-    const uint8_t* dsb = rec + (size_t)3 * H * Ie / 2 + (size_t)8 * H + (size_t)o * 4;
+    // D block of 32 inputs of I: 16 (nibbles) or 8 (2-bit) bytes per output row,
+    // after the 32-row block's gate/up tile; blocks 48*H or 24*H bytes apart
+    const size_t blk = (size_t)(BITS == 4 ? 48 : 24) * H;
+    const uint8_t* dblk = rec + (size_t)(BITS == 4 ? 32 : 16) * H + (size_t)o * sizeof(RowT);
+    const uint8_t* dsb = rec + (item < a.k ? a.sb_off : a.sb_off_shared) + (size_t)8 * H + (size_t)o * 4;
 
     // h of (t, j), blocks [2ga, 2gb): loaded before the weights
     const int nb = 2 * (gb - ga);
@@ -513,13 +539,13 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     const float hi = a.hinv[slot0 + bq];
     __builtin_amdgcn_sched_barrier(0);
 
-    u32x4 W[2 * MAXG];
+    RowT W[2 * MAXG];
     uint32_t SB[MAXG];
 #pragma unroll
     for (int q = 0; q < MAXG; ++q) {
         const int g = min(g0 + q, gb - 1);  // past this wave's range: re-read a valid group
-        W[2 * q] = ldg_nt((const u32x4*)(dblk + (size_t)48 * H * (2 * g)));
-        W[2 * q + 1] = ldg_nt((const u32x4*)(dblk + (size_t)48 * H * (2 * g + 1)));
+        W[2 * q] = ldg_nt((const RowT*)(dblk + blk * (2 * g)));
+        W[2 * q + 1] = ldg_nt((const RowT*)(dblk + blk * (2 * g + 1)));
         SB[q] = ldg_nt((const uint32_t*)(dsb + (size_t)12 * H * g));
         __builtin_amdgcn_sched_barrier(0);  // keep issue order = consumption order
     }
@@ -544,14 +570,23 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int lb = 2 * (g - ga) + half;  // local h block
-                const u32x4 wv = W[2 * q + half];
+                const RowT wv = W[2 * q + half];
                 const uint32_t* hc = sp + (size_t)lb * 16 * kHParts;
                 float a0 = 0.0f, a1 = 0.0f;
+                if constexpr (BITS == 4) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                    for (int p = 0; p < kHParts; ++p)
-                        dot_nib8(wv[m], hc + (m * kHParts + p) * 4, a0, a1);
+                        for (int p = 0; p < kHParts; ++p)
+                            dot_nib8(wv[m], hc + (m * kHParts + p) * 4, a0, a1);
+                    }
+                } else {
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                        for (int p = 0; p < kHParts; ++p)
+                            dot_crumb16(wv[m], hc + (m * kHParts + p) * 8, a0, a1);
+                    }
                 }
                 part = fmaf((a0 + a1) - sK[lb], sI[lb], part);
             }
@@ -632,10 +667,13 @@ hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s) 
     const int rpb = kWaves * kRouterRowsPerWave;
     const int nb = (a.E + rpb - 1) / rpb + (a.prep ? (a.H / 64 + kWaves - 1) / kWaves : 0);
     const dim3 grid(nb, T);
-    if (act_bf16)
-        launch_kernel(k_route<1, true>, grid, dim3(kBlock), 0, s, a);
-    else
-        launch_kernel(k_route<2, false>, grid, dim3(kBlock), 0, s, a);
+    if (a.bits == 2) {
+        if (act_bf16) launch_kernel(k_route<1, true, 2>, grid, dim3(kBlock), 0, s, a);
+        else launch_kernel(k_route<2, false, 2>, grid, dim3(kBlock), 0, s, a);
+    } else {
+        if (act_bf16) launch_kernel(k_route<1, true, 4>, grid, dim3(kBlock), 0, s, a);
+        else launch_kernel(k_route<2, false, 4>, grid, dim3(kBlock), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -649,20 +687,23 @@ hipError_t launch_topk(const RouteArgs& a, int T, hipStream_t s) {
 
 hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
     const dim3 grid((a.H / 64 + kWaves - 1) / kWaves, T);
-    if (act_bf16)
-        launch_kernel(k_prep<1, true>, grid, dim3(kBlock), 0, s, a);
-    else
-        launch_kernel(k_prep<2, false>, grid, dim3(kBlock), 0, s, a);
+    if (a.bits == 2) {
+        if (act_bf16) launch_kernel(k_prep<1, true, 2>, grid, dim3(kBlock), 0, s, a);
+        else launch_kernel(k_prep<2, false, 2>, grid, dim3(kBlock), 0, s, a);
+    } else {
+        if (act_bf16) launch_kernel(k_prep<1, true, 4>, grid, dim3(kBlock), 0, s, a);
+        else launch_kernel(k_prep<2, false, 4>, grid, dim3(kBlock), 0, s, a);
+    }
     return hipGetLastError();
 }
 
-template <int XP, int Q>
+template <int XP, int Q, int BITS>
 static hipError_t launch_gu_xq(const FfnArgs& a, int T, int n_units, hipStream_t s) {
     const dim3 grid(n_units, T);
     const int NG = a.H / 64;
     const size_t sh = ((size_t)(a.H / 2) * XP + 3 * NG + kWaves * 64) * 4;
     const int m = a.gpw_gu;
-#define MOE_GU(MG) launch_kernel(k_gate_up<XP, MG, Q>, grid, dim3(kBlock), sh, s, a)
+#define MOE_GU(MG) launch_kernel(k_gate_up<XP, MG, Q, BITS>, grid, dim3(kBlock), sh, s, a)
     if (m <= 4) MOE_GU(4);
     else if (m <= 8) MOE_GU(8);
     else if (m <= 12) MOE_GU(12);
@@ -673,12 +714,17 @@ static hipError_t launch_gu_xq(const FfnArgs& a, int T, int n_units, hipStream_t
     return hipGetLastError();
 }
 
+template <int XP, int BITS>
+static hipError_t launch_gu_xb(const FfnArgs& a, int T, int n, hipStream_t s) {
+    if (!a.logits || a.E <= 64) return launch_gu_xq<XP, 1, BITS>(a, T, n, s);  // Q = 1: no selection
+    if (a.E <= 128) return launch_gu_xq<XP, 2, BITS>(a, T, n, s);
+    if (a.E <= 256) return launch_gu_xq<XP, 4, BITS>(a, T, n, s);
+    return launch_gu_xq<XP, 16, BITS>(a, T, n, s);
+}
+
 template <int XP>
 static hipError_t launch_gu_xp(const FfnArgs& a, int T, int n, hipStream_t s) {
-    if (!a.logits || a.E <= 64) return launch_gu_xq<XP, 1>(a, T, n, s);  // Q = 1: no selection
-    if (a.E <= 128) return launch_gu_xq<XP, 2>(a, T, n, s);
-    if (a.E <= 256) return launch_gu_xq<XP, 4>(a, T, n, s);
-    return launch_gu_xq<XP, 16>(a, T, n, s);
+    return a.bits == 2 ? launch_gu_xb<XP, 2>(a, T, n, s) : launch_gu_xb<XP, 4>(a, T, n, s);
 }
 
 // units [a.unit_offset, a.unit_offset + n_units) of the k*blk_r routed + blk_s shared units
@@ -692,7 +738,9 @@ hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {
     const int nb = 2 * max(a.gi, a.gis);  // blocks staged per item (upper bound)
     const size_t sh = ((size_t)nb * (16 * kHParts + 3) + kWaves * 64) * 4;
     const int m = a.gpw_dn;
-#define MOE_DN(MG) launch_kernel(k_down<MG>, grid, dim3(kBlock), sh, s, a)
+#define MOE_DN(MG)                                                             \
+    (a.bits == 2 ? launch_kernel(k_down<MG, 2>, grid, dim3(kBlock), sh, s, a)  \
+                 : launch_kernel(k_down<MG, 4>, grid, dim3(kBlock), sh, s, a))
     if (m <= 2) MOE_DN(2);
     else if (m <= 4) MOE_DN(4);
     else if (m <= 8) MOE_DN(8);

@@ -56,6 +56,9 @@ struct moe_layer {
     SlotCache cache;
     size_t rec_bytes;
     size_t shared_rec_bytes;
+    int bits;             // code width of the expert records: 4 or 2
+    size_t sb_off;        // scale/bias region of a routed record
+    size_t sb_off_shared; // ... and of the shared record
     int NG;        // H / 64
     int blk_r;     // I / 32
     int blk_s;     // Is / 32
@@ -131,8 +134,27 @@ int grouped_chunk(const moe_layer* L) {
     return (int)std::max<int64_t>(c, kPrefillMinTokens);
 }
 
+// 2-bit layers run every call through the per-token kernels, in passes of
+// at most kPrefillMinTokens - 1 tokens that share one workspace (stream order
+// keeps the passes apart).
+template <typename F>
+moe_status token_passes(int T, F&& pass) {
+    constexpr int P = kPrefillMinTokens - 1;
+    for (int c0 = 0; c0 < T; c0 += P) {
+        const moe_status st = pass(c0, std::min(P, T - c0));
+        if (st != MOE_OK) return st;
+    }
+    return MOE_OK;
+}
+
+// activations of token c0
+const void* x_at(const moe_layer* L, const void* x, int c0) {
+    return (const uint8_t*)x + (size_t)c0 * L->d.hidden * (L->d.act_dtype == MOE_BF16 ? 2 : 4);
+}
+
 WsLayout ws_layout(const moe_layer* L, int T) {
     WsLayout o{};
+    if (L->bits == 2) T = std::min(T, kPrefillMinTokens - 1);  // token passes
     const int H = L->d.hidden, k = L->d.top_k;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -216,6 +238,7 @@ RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, 
     a.gate = L->d.gate_fn == MOE_SIGMOID_TOPK ? 1 : 0;
     a.bias = L->w.selection_bias;
     a.rscale = L->d.routed_scale > 0.0f ? L->d.routed_scale : 1.0f;
+    a.bits = L->bits;
     return a;
 }
 
@@ -233,6 +256,9 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.experts = L->w.experts;
     a.shared = L->w.shared;
     a.rec_bytes = L->rec_bytes;
+    a.bits = L->bits;
+    a.sb_off = L->sb_off;
+    a.sb_off_shared = L->sb_off_shared;
     if (L->cache.n_slots) {
         a.slots = L->w.slots;
         a.slot_ids = (const int32_t*)(ws + o.slot_ids);
@@ -466,8 +492,13 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
 extern "C" {
 
 size_t moe_expert_record_bytes(int32_t hidden, int32_t inter) {
-    if (hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64) return 0;
-    return (size_t)27 * hidden * inter / 16;
+    return moe_expert_record_bytes_bits(hidden, inter, 4);
+}
+
+size_t moe_expert_record_bytes_bits(int32_t hidden, int32_t inter, int32_t bits) {
+    if (hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64 || (bits != 4 && bits != 2)) return 0;
+    // codes (bits/8 bytes per weight) + one fp16 (scale, bias) pair per 64 weights
+    return (size_t)(bits == 4 ? 27 : 15) * hidden * inter / 16;
 }
 
 moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w,
@@ -505,6 +536,7 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         return fail(MOE_ERR_ARG, "cache_policy must be MOE_CACHE_LFU or MOE_CACHE_LRU");
     if (d.n_slots == 0 && d.cache_policy != MOE_CACHE_LFU)
         return fail(MOE_ERR_ARG, "cache_policy applies to a slot cache only");
+    if (d.bits != 0 && d.bits != 4 && d.bits != 2) return fail(MOE_ERR_ARG, "bits must be 4 or 2 (0 reads as 4)");
     if (d.n_slots == 0 && (w->host_pool || w->slots))
         return fail(MOE_ERR_ARG, "host_pool/slots must be NULL when n_slots = 0");
     if (d.n_slots > 0 && (!w->host_pool || !w->slots))
@@ -539,8 +571,11 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     if (!L) return fail(MOE_ERR_NOMEM, "host allocation failed");
     L->d = d;
     L->w = *w;
-    L->rec_bytes = moe_expert_record_bytes(d.hidden, d.inter);
-    L->shared_rec_bytes = d.shared_inter ? moe_expert_record_bytes(d.hidden, d.shared_inter) : 0;
+    L->bits = d.bits == 2 ? 2 : 4;
+    L->rec_bytes = moe_expert_record_bytes_bits(d.hidden, d.inter, L->bits);
+    L->shared_rec_bytes = d.shared_inter ? moe_expert_record_bytes_bits(d.hidden, d.shared_inter, L->bits) : 0;
+    L->sb_off = (size_t)d.hidden * d.inter * L->bits * 3 / 8;  // G, U and D codes first
+    L->sb_off_shared = (size_t)d.hidden * d.shared_inter * L->bits * 3 / 8;
     L->NG = d.hidden / 64;
     L->blk_r = d.inter / 32;
     L->blk_s = d.shared_inter / 32;
@@ -603,6 +638,11 @@ moe_status moe_route_topk(moe_layer_t L, const void* x, int32_t T, int32_t* ids,
     moe_status st = check_call(L, x, T, workspace);
     if (st != MOE_OK) return st;
     if (!ids || !w) return fail(MOE_ERR_ARG, "null ids or w");
+    const size_t k = L->d.top_k;
+    if (L->bits == 2 && T >= kPrefillMinTokens)
+        return token_passes(T, [&](int c0, int Tc) {
+            return moe_route_topk(L, x_at(L, x, c0), Tc, ids + c0 * k, w + c0 * k, workspace, stream);
+        });
     const WsLayout o = ws_layout(L, T);
     hipStream_t s = (hipStream_t)stream;
     if (T >= kPrefillMinTokens)  // the grouped path's router (MFMA tiles), as the forward call
@@ -620,6 +660,13 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     if (st != MOE_OK) return st;
     if (L->cache.n_slots && T != 1) return fail(MOE_ERR_STATE, "the slot cache runs one token per call");
     if (!ids || !expert_out) return fail(MOE_ERR_ARG, "null ids or expert_out");
+    if (L->bits == 2 && T >= kPrefillMinTokens) {
+        const size_t k = L->d.top_k, H = L->d.hidden;
+        return token_passes(T, [&](int c0, int Tc) {
+            return moe_expert_ffn(L, x_at(L, x, c0), Tc, ids + c0 * k, workspace,
+                                  expert_out + c0 * (k + 1) * H, stream);
+        });
+    }
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
@@ -654,6 +701,13 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     if (st != MOE_OK) return st;
     if (L->cache.n_slots && T != 1) return fail(MOE_ERR_STATE, "the slot cache runs one token per call");
     if (!ids || !w || !y) return fail(MOE_ERR_ARG, "null ids, w or y");
+    if (L->bits == 2 && T >= kPrefillMinTokens) {
+        const size_t k = L->d.top_k, H = L->d.hidden;
+        return token_passes(T, [&](int c0, int Tc) {
+            return moe_layer_forward(L, x_at(L, x, c0), Tc, ids + c0 * k, w + c0 * k, y + c0 * H,
+                                     workspace, stream);
+        });
+    }
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;

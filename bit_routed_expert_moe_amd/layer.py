@@ -22,7 +22,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIG
           -4: "MOE_ERR_HIP", -5: "MOE_ERR_NOMEM", -6: "MOE_ERR_NOT_PINNED",
           -7: "MOE_ERR_STATE", -8: "MOE_ERR_DEVICE"}
 
-EXPORTS = ["moe_expert_record_bytes", "moe_layer_create", "moe_layer_destroy",
+EXPORTS = ["moe_expert_record_bytes", "moe_expert_record_bytes_bits", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
            "moe_poll_device_error",
@@ -42,7 +42,8 @@ class Desc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("inter", C.c_int32),
                 ("top_k", C.c_int32), ("shared_inter", C.c_int32), ("group", C.c_int32),
                 ("act_dtype", C.c_int32), ("gate_fn", C.c_int32), ("n_slots", C.c_int32),
-                ("routed_scale", C.c_float), ("cache_policy", C.c_int32), ("reserved", C.c_int32 * 5)]
+                ("routed_scale", C.c_float), ("cache_policy", C.c_int32), ("bits", C.c_int32),
+                ("reserved", C.c_int32 * 4)]
 
 
 class Weights(C.Structure):
@@ -63,6 +64,8 @@ def lib() -> C.CDLL:
         vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.moe_expert_record_bytes.argtypes = [i32, i32]
         L.moe_expert_record_bytes.restype = C.c_size_t
+        L.moe_expert_record_bytes_bits.argtypes = [i32, i32, i32]
+        L.moe_expert_record_bytes_bits.restype = C.c_size_t
         L.moe_layer_create.argtypes = [C.POINTER(Desc), C.POINTER(Weights), C.POINTER(vp)]
         L.moe_layer_destroy.argtypes = [vp]
         L.moe_workspace_bytes.argtypes = [vp, i32]
@@ -95,8 +98,8 @@ def _check(status: int):
         raise MoeError(status, lib().moe_last_error().decode())
 
 
-def record_bytes(hidden: int, inter: int) -> int:
-    return int(lib().moe_expert_record_bytes(hidden, inter))
+def record_bytes(hidden: int, inter: int, bits: int = 4) -> int:
+    return int(lib().moe_expert_record_bytes_bits(hidden, inter, bits))
 
 
 def _stream() -> int:
@@ -118,8 +121,8 @@ class Layer:
 
     router_q      int8 [E][H]
     router_scale  float16 [E] (or int16 holding fp16 bits)
-    experts       uint8 [E * record_bytes(H, inter)]
-    shared        uint8 [record_bytes(H, shared_inter)] or None
+    experts       uint8 [E * record_bytes(H, inter, bits)]
+    shared        uint8 [record_bytes(H, shared_inter, bits)] or None
     act           "bf16" or "f32" activations
     n_slots       > 0: HBM slot cache of that many records, filled from
     host_pool     pinned uint8 CPU tensor of all E records, into
@@ -131,6 +134,7 @@ class Layer:
     routed_scale  sigmoid gate: the routed scaling factor
     selection_bias  sigmoid gate: float32 CUDA tensor [E] or None
     cache_policy  slot cache replacement: "lfu" (default) or "lru"
+    bits          width of the expert weight codes: 4 (default) or 2
     """
 
     def __init__(self, hidden: int, n_experts: int, inter: int, top_k: int, shared_inter: int,
@@ -139,8 +143,9 @@ class Layer:
                  n_slots: int = 0, host_pool: torch.Tensor | None = None,
                  slots: torch.Tensor | None = None, gate: str = "softmax",
                  routed_scale: float = 1.0, selection_bias: torch.Tensor | None = None,
-                 cache_policy: str = "lfu"):
+                 cache_policy: str = "lfu", bits: int = 4):
         self.hidden, self.n_experts, self.inter = hidden, n_experts, inter
+        self.bits = bits
         self.top_k, self.shared_inter, self.act = top_k, shared_inter, act
         self.n_slots = n_slots
         if gate not in ("softmax", "sigmoid"):
@@ -150,7 +155,7 @@ class Layer:
         d = Desc(hidden, n_experts, inter, top_k, shared_inter, 64,
                  MOE_BF16 if act == "bf16" else MOE_F32,
                  MOE_SIGMOID_TOPK if gate == "sigmoid" else MOE_SOFTMAX_TOPK, n_slots,
-                 float(routed_scale), {"lfu": MOE_CACHE_LFU, "lru": MOE_CACHE_LRU}[cache_policy])
+                 float(routed_scale), {"lfu": MOE_CACHE_LFU, "lru": MOE_CACHE_LRU}[cache_policy], bits)
         hp = None
         if host_pool is not None:
             if host_pool.is_cuda or not host_pool.is_pinned() or not host_pool.is_contiguous():

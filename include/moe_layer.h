@@ -50,6 +50,18 @@
  *     +8*H   (scale, bias) of D[o][64g .. 64g+64) for o < H
  *   Record size: 27*H*I/16 bytes (0.5625 bytes per weight).  A layer's routed
  *   records lie back to back: record e at experts + e * moe_expert_record_bytes.
+ * 2-bit records (desc.bits = 2): W = scale * q + bias, q in 0..3, the same
+ * groups and the same scale/bias slabs; a 16-byte run holds 64 inputs, input
+ * 4m+j in bits [2j, 2j+2) of byte m.  The 4-bit format with half the code
+ * bytes (Colibri README, "What's implemented", names packed int2 among its CPU
+ * quantisation kernels; the layout here is our own).
+ *   code region (3*H*I/4 bytes): I/32 blocks of 24*H bytes:
+ *     +0     GU tile: for chunk c < H/64, for tile row r < 64: 16 bytes holding
+ *            inputs [64c, 64c+64) of G row 32b+r (r < 32) or U row 32b+r-32
+ *     +16*H  D block: for output row o < H: 8 bytes = D[o][32b .. 32b+32)
+ *   scale/bias region at 3*H*I/4, laid out as above.
+ *   Record size: 15*H*I/16 bytes (0.3125 bytes per weight);
+ *   moe_expert_record_bytes_bits gives either size.
  * Router: rows q[E][H] int8, row-major, and one fp16 scale per row;
  *   logit_e = scale_e * sum_h q[e][h] * x_h.
  */
@@ -102,7 +114,11 @@ typedef struct moe_layer_desc {
                               as 1); must be 0 or 1 with MOE_SOFTMAX_TOPK           */
     int32_t cache_policy;  /* n_slots > 0: MOE_CACHE_LFU or MOE_CACHE_LRU (see
                               moe_cache_stats); must be MOE_CACHE_LFU otherwise     */
-    int32_t reserved[5];
+    int32_t bits;          /* width of the expert weight codes: 4 (0 reads as 4) or 2;
+                              router rows stay int8.  Layers of 2-bit records run
+                              every call through the per-token kernels, at most 3
+                              tokens per pass (the grouped prefill path is 4-bit only) */
+    int32_t reserved[4];
 } moe_layer_desc;
 
 typedef struct moe_layer_weights {
@@ -121,9 +137,13 @@ typedef struct moe_layer_weights {
 
 typedef struct moe_layer* moe_layer_t;
 
-/* Bytes of one packed record of (hidden, inter): 27*hidden*inter/16, or 0 if
- * either is not a positive multiple of 64. */
+/* Bytes of one packed 4-bit record of (hidden, inter): 27*hidden*inter/16, or 0
+ * if either is not a positive multiple of 64. */
 size_t moe_expert_record_bytes(int32_t hidden, int32_t inter);
+
+/* Bytes of one packed record of (hidden, inter) with `bits`-wide codes (4 or 2):
+ * 27*hidden*inter/16 or 15*hidden*inter/16; 0 for a bad shape or width. */
+size_t moe_expert_record_bytes_bits(int32_t hidden, int32_t inter, int32_t bits);
 
 /* Validates desc and weights and builds a handle.  The handle borrows the
  * weight pointers (they must outlive it) and owns only host metadata.

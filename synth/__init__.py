@@ -114,21 +114,23 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # belongs to is the layout's business, not the generator's.
 # ---------------------------------------------------------------------------
 
-def nibble_region_bytes(hidden: int, inter: int) -> int:
-    return 3 * hidden * inter // 2
+def nibble_region_bytes(hidden: int, inter: int, bits: int = 4) -> int:
+    """Bytes of the code region (4-bit nibbles, or 2-bit codes)."""
+    return 3 * hidden * inter * bits // 8
 
 
 def sb_pairs(hidden: int, inter: int) -> int:
     return 3 * hidden * inter // 64
 
 
-def record_bytes(hidden: int, inter: int) -> int:
-    return nibble_region_bytes(hidden, inter) + 4 * sb_pairs(hidden, inter)
+def record_bytes(hidden: int, inter: int, bits: int = 4) -> int:
+    return nibble_region_bytes(hidden, inter, bits) + 4 * sb_pairs(hidden, inter)
 
 
-def expert_record(seed: int, layer: int, expert: int, hidden: int, inter: int) -> np.ndarray:
+def expert_record(seed: int, layer: int, expert: int, hidden: int, inter: int,
+                  bits: int = 4) -> np.ndarray:
     """One packed expert record (uint8), generated on the CPU."""
-    nb = nibble_region_bytes(hidden, inter)
+    nb = nibble_region_bytes(hidden, inter, bits)
     npairs = sb_pairs(hidden, inter)
     out = np.empty(nb + 4 * npairs, dtype=np.uint8)
     out[:nb] = stream(key(seed, layer, KIND_NIBBLE, expert), nb // 8).view(np.uint8)

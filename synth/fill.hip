@@ -61,11 +61,11 @@ __global__ void k_fill_records(uint8_t* dst, int64_t stride, int64_t nib_bytes, 
 }  // namespace
 
 extern "C" int synth_fill_records(void* dst, int64_t stride, int hidden, int inter, uint64_t seed,
-                                  int layer, int first_index, int n_records, void* stream) {
+                                  int layer, int first_index, int n_records, void* stream, int bits) {
     if (!dst || hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64 || n_records <= 0 ||
-        n_records > 65535)
+        n_records > 65535 || (bits != 4 && bits != 2))
         return -1;
-    const int64_t nib = (int64_t)3 * hidden * inter / 2;
+    const int64_t nib = (int64_t)3 * hidden * inter * bits / 8;  // code region bytes
     const int64_t npairs = (int64_t)3 * hidden * inter / 64;
     if (stride < nib + 4 * npairs) return -1;
     int64_t want = (nib / 8 + 255) / 256;

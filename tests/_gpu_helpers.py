@@ -32,34 +32,37 @@ class DeviceLayer:
     regenerated on the CPU on demand)."""
 
     def __init__(self, seed, layer, H, E, I, k, Is, act, dev="cuda", gate="softmax",
-                 routed_scale=1.0, bias=None):
+                 routed_scale=1.0, bias=None, bits=4):
         """gate / routed_scale / bias (float32 numpy [E] or None): the router's
-        gate function, as in bit_routed_expert_moe_amd.Layer."""
+        gate function, as in bit_routed_expert_moe_amd.Layer; bits: code width
+        of the expert records (4 or 2)."""
         from bit_routed_expert_moe_amd import Layer, record_bytes
         self.seed, self.layer, self.H, self.E, self.I, self.k, self.Is, self.act = \
             seed, layer, H, E, I, k, Is, act
-        self.gate, self.routed_scale = gate, routed_scale
+        self.gate, self.routed_scale, self.bits = gate, routed_scale, bits
         self.bias = None if bias is None else np.asarray(bias, dtype=np.float32)
         self.bias_dev = None if bias is None else torch.from_numpy(self.bias).to(dev)
         self.rq, self.rs = synth.router(seed, layer, E, H)
-        self.pool = torch.empty(E * record_bytes(H, I), dtype=torch.uint8, device=dev)
-        synth.gpu.fill_records(self.pool, H, I, seed, layer, 0, E)
+        self.pool = torch.empty(E * record_bytes(H, I, bits), dtype=torch.uint8, device=dev)
+        synth.gpu.fill_records(self.pool, H, I, seed, layer, 0, E, bits=bits)
         self.shared = None
         if Is:
-            self.shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
-            synth.gpu.fill_records(self.shared, H, Is, seed, layer, -1, 1)
+            self.shared = torch.empty(record_bytes(H, Is, bits), dtype=torch.uint8, device=dev)
+            synth.gpu.fill_records(self.shared, H, Is, seed, layer, -1, 1, bits=bits)
         self.layer_obj = Layer(H, E, I, k, Is, torch.from_numpy(self.rq).to(dev),
                                torch.from_numpy(self.rs.view(np.float16)).to(dev), self.pool,
                                self.shared, act=act, gate=gate, routed_scale=routed_scale,
-                               selection_bias=self.bias_dev)
+                               selection_bias=self.bias_dev, bits=bits)
         self._rec_cache = {}
 
     def record(self, e: int) -> np.ndarray:
         if e not in self._rec_cache:
             if e == synth.SHARED_INDEX:
-                self._rec_cache[e] = synth.expert_record(self.seed, self.layer, e, self.H, self.Is)
+                self._rec_cache[e] = synth.expert_record(self.seed, self.layer, e, self.H, self.Is,
+                                                         bits=self.bits)
             else:
-                self._rec_cache[e] = synth.expert_record(self.seed, self.layer, e, self.H, self.I)
+                self._rec_cache[e] = synth.expert_record(self.seed, self.layer, e, self.H, self.I,
+                                                         bits=self.bits)
         return self._rec_cache[e]
 
     def natural_token(self, orc, step: int, max_attempts: int = 200):
@@ -85,8 +88,10 @@ class DeviceLayer:
         ids, w, lg = orc.route(self.rq, self.rs, xd, self.k, gate=self.gate,
                                bias=None if self.bias is None else self.bias.astype(np.float64),
                                scale=self.routed_scale)
-        yr = np.stack([orc.expert_ffn(self.H, self.I, self.record(int(e)), xd) for e in ids])
-        ys = orc.expert_ffn(self.H, self.Is, self.record(synth.SHARED_INDEX), xd) if self.Is else None
+        yr = np.stack([orc.expert_ffn(self.H, self.I, self.record(int(e)), xd, bits=self.bits)
+                       for e in ids])
+        ys = (orc.expert_ffn(self.H, self.Is, self.record(synth.SHARED_INDEX), xd, bits=self.bits)
+              if self.Is else None)
         return ids, w, orc.combine(w, yr, ys), yr, ys
 
 

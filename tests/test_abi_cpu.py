@@ -37,6 +37,18 @@ def test_record_bytes_formula():
         assert lib.moe_expert_record_bytes(H, I) == 0
 
 
+def test_record_bytes_by_bit_width():
+    # codes at bits/8 bytes per weight, plus 4 bytes of (scale, bias) per 64 weights
+    lib = L.lib()
+    for H, I in [(64, 64), (256, 128), (2816, 704), (6144, 2048)]:
+        assert lib.moe_expert_record_bytes_bits(H, I, 4) == 3 * H * I // 2 + 3 * H * I // 16
+        assert lib.moe_expert_record_bytes_bits(H, I, 2) == 3 * H * I // 4 + 3 * H * I // 16
+        assert L.record_bytes(H, I, 2) == 15 * H * I // 16
+    for bits in (0, 1, 3, 8):
+        assert lib.moe_expert_record_bytes_bits(256, 128, bits) == 0
+    assert lib.moe_expert_record_bytes_bits(100, 64, 2) == 0
+
+
 def test_status_strings():
     lib = L.lib()
     for code, name in L.STATUS.items():
@@ -63,6 +75,7 @@ FAKE = dict(router_q=0x10000, router_scale=0x20000, experts=0x30000, shared=0x40
     (dict(gate_fn=1, routed_scale=float("nan")), -1), (dict(gate_fn=1, routed_scale=float("inf")), -1),
     (dict(cache_policy=2), -1), (dict(cache_policy=1), -1),  # LRU needs a slot cache
     (dict(n_slots=4), -2), (dict(n_slots=16), -1), (dict(n_slots=-1), -2),
+    (dict(bits=3), -1), (dict(bits=8), -1), (dict(bits=-2), -1),
 ])
 def test_create_rejects_bad_descriptor(change, status):
     d = L.Desc(**{**GOOD, **change})

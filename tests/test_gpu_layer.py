@@ -41,15 +41,16 @@ def check_tokens(dl, orc, xs_q, xs_d, ids, w, y, tag):
     assert worst_w <= W_TOL and worst_y <= Y_TOL
 
 
-def test_gpu_fill_matches_cpu_generator():
+@pytest.mark.parametrize("bits", [4, 2])
+def test_gpu_fill_matches_cpu_generator(bits):
     for H, I, first, n in [(256, 128, 0, 3), (2816, 704, 5, 2), (64, 64, -1, 1)]:
-        rb = synth.record_bytes(H, I)
+        rb = synth.record_bytes(H, I, bits)
         buf = torch.empty(rb * n, dtype=torch.uint8, device="cuda")
-        synth.gpu.fill_records(buf, H, I, 77, 3, first, n)
+        synth.gpu.fill_records(buf, H, I, 77, 3, first, n, bits=bits)
         got = buf.cpu().numpy()
         for r in range(n):
             e = synth.SHARED_INDEX if first < 0 else first + r
-            assert np.array_equal(got[r * rb:(r + 1) * rb], synth.expert_record(77, 3, e, H, I))
+            assert np.array_equal(got[r * rb:(r + 1) * rb], synth.expert_record(77, 3, e, H, I, bits))
 
 
 def test_tiny_layer_many_tokens(orc):
