@@ -22,7 +22,8 @@ instead: a step is one 128-token chunk through one layer, cycling over
 --prefill-layers layers of distinct weights; the roofline entry is the grouped
 gate/up kernel's, with its MFMA utilisation.  --workload
 offload_h2816_e256_l40_lfu16 measures the out-of-core decode with the HBM
-slot cache.
+slot cache.  --bits 2 runs the decode workloads on 2-bit records of the same
+affine group-64 format.
 """
 from __future__ import annotations
 
@@ -43,27 +44,36 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE runs (profiles/*_counters.md), each scaled by the same counter's
 # reading for a 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Valid only for the
-# kernel source they were taken on (first 16 hex digits of its sha256); None
-# once that file changes.
+# kernel sources they were taken on (first 16 hex digits of the sha256 of the
+# kernel file followed by the two device headers it includes); None once any
+# of them changes.
+KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12168.9 KiB x 2.0 + WRITE_SIZE 37.9 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24960717, "moe_kernels.hip", "aed6c2436052778d"),
-    # FETCH_SIZE 1833719.2 KiB x 2.0 + WRITE_SIZE 5753.4 KiB x 1.0 per launch (mean over
+    # FETCH_SIZE 12150.45 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24922897, "moe_kernels.hip", "8e1bcc923c7a6283"),
+    # 2-bit records: FETCH_SIZE 6813.03 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13991873, "moe_kernels.hip", "8e1bcc923c7a6283"),
+    # FETCH_SIZE 1833665.77 KiB x 2.0 + WRITE_SIZE 5753.88 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761348516, "moe_prefill.hip", "ac1ac64007a8eb40"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761239471, "moe_prefill.hip", "5e0050176b420ab5"),
 }
 
 
-def traffic_for(workload, kernel):
+def source_digest(src):
     import hashlib
-    ent = TRAFFIC.get((workload, kernel))
+    h = hashlib.sha256()
+    for name in (src, *KERNEL_HEADERS):
+        with open(os.path.join(ROOT, "bit_routed_expert_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload, kernel, bits=4):
+    ent = TRAFFIC.get((workload if bits == 4 else f"{workload}/bits{bits}", kernel))
     if ent is None:
         return None
     nbytes, src, digest = ent
-    with open(os.path.join(ROOT, "bit_routed_expert_moe_amd", "csrc", src), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
-            return None
-    return nbytes
+    return nbytes if source_digest(src) == digest else None
 
 
 METRIC = "decode tokens/s per MoE layer + achieved HBM GB/s vs peak (batch 1, top-8)"
@@ -73,13 +83,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gu_bytes(H, I):
-    """gate+up half of a record: nibbles I*H bytes + scale/bias I*H/8 bytes."""
-    return 9 * H * I // 8
+def gu_bytes(H, I, bits=4):
+    """gate+up part of a record: codes 2*I*H*bits/8 bytes + scale/bias I*H/8 bytes."""
+    return H * I * bits // 4 + H * I // 8
 
 
-def down_bytes(H, I):
-    return 9 * H * I // 16
+def down_bytes(H, I, bits=4):
+    """down part: codes H*I*bits/8 bytes + scale/bias H*I/16 bytes."""
+    return H * I * bits // 8 + H * I // 16
+
+
+def token_layer_bytes(wl, bits):
+    """Algorithmic HBM bytes of one decode token through one layer: the router,
+    the top_k selected records and the shared record."""
+    from bit_routed_expert_moe_amd import record_bytes
+    rbs = record_bytes(wl.hidden, wl.shared_inter, bits) if wl.shared_inter else 0
+    return wl.router_bytes + wl.top_k * record_bytes(wl.hidden, wl.inter, bits) + rbs
+
+
+def dtype_desc(bits):
+    return f"u{bits} weights x f16 activations -> f32"
 
 
 def make_inputs(wl, layer, S):
@@ -155,11 +178,12 @@ def cpu_baseline(wl, xs_host, seconds, args):
                 t0 = time.perf_counter()
                 ids, w, _ = oracle_route(orc, args, wl, l, rq, rs, xd)
                 spent += time.perf_counter() - t0
-                recs = [synth.expert_record(wl.seed, l, int(e), H, I) for e in ids]
-                shared = synth.expert_record(wl.seed, l, synth.SHARED_INDEX, H, Is) if Is else None
+                recs = [synth.expert_record(wl.seed, l, int(e), H, I, args.bits) for e in ids]
+                shared = (synth.expert_record(wl.seed, l, synth.SHARED_INDEX, H, Is, args.bits)
+                          if Is else None)
                 t0 = time.perf_counter()
-                yr = np.stack([orc.expert_ffn(H, I, r, xd) for r in recs])
-                ys = orc.expert_ffn(H, Is, shared, xd) if Is else None
+                yr = np.stack([orc.expert_ffn(H, I, r, xd, bits=args.bits) for r in recs])
+                ys = orc.expert_ffn(H, Is, shared, xd, bits=args.bits) if Is else None
                 orc.combine(w, yr, ys)
                 spent += time.perf_counter() - t0
                 n += 1
@@ -187,22 +211,24 @@ def run_cached(args, wl):
     H, E, I, k, Is, L = wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.n_layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(0)
-    rb = record_bytes(H, I)
+    bits = args.bits
+    rb = record_bytes(H, I, bits)
     t_setup = time.time()
     layers, keep = [], []
     staging = torch.empty(E * rb, dtype=torch.uint8, device=dev)
     for l in range(L):
         rq, rs = synth.router(wl.seed, l, E, H)
-        synth.gpu.fill_records(staging, H, I, wl.seed, l, 0, E)
+        synth.gpu.fill_records(staging, H, I, wl.seed, l, 0, E, bits=bits)
         host = torch.empty(E * rb, dtype=torch.uint8, pin_memory=True)
         host.copy_(staging)
-        shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
-        synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
+        shared = torch.empty(record_bytes(H, Is, bits), dtype=torch.uint8, device=dev)
+        synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1, bits=bits)
         slots = torch.zeros(wl.n_slots * rb, dtype=torch.uint8, device=dev)
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
                             torch.from_numpy(rs.view(np.float16)).to(dev), None, shared,
                             act=wl.act, n_slots=wl.n_slots, host_pool=host, slots=slots,
-                            cache_policy=args.cache_policy, **gate_kwargs(args, wl, l, dev)))
+                            cache_policy=args.cache_policy, bits=bits,
+                            **gate_kwargs(args, wl, l, dev)))
     del staging
     S = wl.steps
     xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][1][H]
@@ -260,15 +286,15 @@ def run_cached(args, wl):
     hit_timed = (h1 - h0) / max(1, (h1 - h0) + (m1 - m0))
     hit_all = h1 / max(1, h1 + m1)
     miss_bytes_step = (m1 - m0) / K * rb
-    hbm_bytes_step = L * wl.token_layer_bytes + miss_bytes_step  # reads + slot writes
+    hbm_bytes_step = L * token_layer_bytes(wl, bits) + miss_bytes_step  # reads + slot writes
     bound_ms = max(hbm_bytes_step / (PEAK_HBM_GBS * 1e9), miss_bytes_step / (h2d_gbs * 1e9)) * 1e3
     out = {
         "metric": METRIC, "value": round(L / (ms_per_step * 1e-3), 1), "unit": "tok/s per layer",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
+        "dtype": dtype_desc(bits), "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
-                   "shared_inter": Is, "layers": L, "batch": 1, "act": wl.act,
+                   "shared_inter": Is, "layers": L, "batch": 1, "act": wl.act, "bits": bits,
                    "routing": wl.routing, "gate": gate_desc(args), "n_slots": wl.n_slots,
                    "cache_policy": args.cache_policy, "pinned_per_layer": args.pin,
                    "pin_source": f"expert counts over the {W} warm-up steps" if args.pin else None},
@@ -486,6 +512,8 @@ def main():
     ap.add_argument("--pin", type=int, default=0,
                     help="slot-cache workloads: pin this many experts per layer, the most used "
                          "during the warm-up steps")
+    ap.add_argument("--bits", type=int, choices=(4, 2), default=4,
+                    help="decode workloads: width of the expert weight codes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -515,25 +543,30 @@ def main():
     if wl.n_slots:
         return run_cached(args, wl)
     if wl.n_tokens != 1:
+        if args.bits != 4:
+            print("--bits 2 applies to the decode workloads: the grouped prefill path reads "
+                  "4-bit records only", file=sys.stderr)
+            sys.exit(2)
         return run_prefill(args, wl)
     H, E, I, k, Is, L, T = (wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter,
                             wl.n_layers, wl.n_tokens)
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     t_setup = time.time()
-    rb = record_bytes(H, I)
+    bits = args.bits
+    rb = record_bytes(H, I, bits)
     layers, keep = [], []
     for l in range(L):
         rq, rs = synth.router(wl.seed, l, E, H)
         pool = torch.empty(E * rb, dtype=torch.uint8, device=dev)
-        synth.gpu.fill_records(pool, H, I, wl.seed, l, 0, E)
+        synth.gpu.fill_records(pool, H, I, wl.seed, l, 0, E, bits=bits)
         shared = None
         if Is:
-            shared = torch.empty(record_bytes(H, Is), dtype=torch.uint8, device=dev)
-            synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
+            shared = torch.empty(record_bytes(H, Is, bits), dtype=torch.uint8, device=dev)
+            synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1, bits=bits)
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
                             torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act,
-                            **gate_kwargs(args, wl, l, dev)))
+                            bits=bits, **gate_kwargs(args, wl, l, dev)))
     S = wl.steps
     xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][T][H]
     xs_q = synth.quantize_act(xs_host, wl.act)
@@ -587,7 +620,7 @@ def main():
     ms_per_step = total_ms / K
     log(f"timed {K} steps in {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), graphs of {G} steps")
 
-    tl_bytes = wl.token_layer_bytes
+    tl_bytes = token_layer_bytes(wl, bits)
     step_bytes = L * T * tl_bytes
     layer_tok_s = L * T / (ms_per_step * 1e-3)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -600,8 +633,8 @@ def main():
             run_step(s)
 
     recs = kernel_timed_pass(profiled_steps, P * L * 4 + 64)
-    kb_gu = T * (k * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0))
-    kb_dn = T * (k * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0))
+    kb_gu = T * (k * gu_bytes(H, I, bits) + (gu_bytes(H, Is, bits) if Is else 0))
+    kb_dn = T * (k * down_bytes(H, I, bits) + (down_bytes(H, Is, bits) if Is else 0))
     kbytes = {"route": T * (E * H + 2 * E), "gate_up": kb_gu, "down_combine": kb_dn}
     kernels = {}
     for name in sorted({r[0] for r in recs}):
@@ -617,7 +650,7 @@ def main():
     gu = kernels["gate_up"]
     roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(wl.name, kfn),
+                "traffic": traffic_for(wl.name, kfn, bits),
                 "kernel": kfn, "alg_bytes_per_launch": gu["alg_bytes"],
                 "avg_launch_us": gu["avg_us"], "timing": "hipExtLaunchKernelGGL start/stop events"}
 
@@ -629,9 +662,9 @@ def main():
         "metric": METRIC, "value": round(layer_tok_s, 1), "unit": "tok/s per layer",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "u4 weights x f16 activations -> f32", "data": "synthetic",
+        "dtype": dtype_desc(bits), "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
-                   "shared_inter": Is, "layers": L, "batch": T, "act": wl.act,
+                   "shared_inter": Is, "layers": L, "batch": T, "act": wl.act, "bits": bits,
                    "routing": wl.routing, "gate": gate_desc(args), "graph_chunk": G},
         "stack_tok_s": round(T / (ms_per_step * 1e-3), 2),
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),

@@ -31,9 +31,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                   c, false);
 }
 
+// The fp16 pair (1024, 1024) in a register the compiler cannot fold: with the
+// constant hidden, (w & mask) | M selects one v_and_or_b32 (mask in an SGPR)
+// instead of a v_and_b32 and a v_or_b32 with literal operands.
+__device__ __forceinline__ uint32_t magic_1024x2() {
+    uint32_t m = 0x64006400u;
+    asm("" : "+v"(m));
+    return m;
+}
+
 // acc0 gathers the q0/q4/q2/q6 pairs, acc1 the x16 pairs; x points at 4 dwords.
 __device__ __forceinline__ void dot_nib8(uint32_t w, const uint32_t* x, float& acc0, float& acc1) {
-    const uint32_t M = 0x64006400u;
+    const uint32_t M = magic_1024x2();
     const uint32_t w8 = w >> 8;
     acc0 = dot2((w & 0x000F000Fu) | M, x[0], acc0);
     acc1 = dot2((w & 0x00F000F0u) | M, x[1], acc1);
@@ -41,19 +50,28 @@ __device__ __forceinline__ void dot_nib8(uint32_t w, const uint32_t* x, float& a
     acc1 = dot2((w8 & 0x00F000F0u) | M, x[3], acc1);
 }
 
-// 2-bit codes: a dword w holds 16 codes, input i in bits [2i, 2i+2).  Shifting
-// field j to bit 0 and or-ing 0x6400 gives the fp16 pair (1024 + q_j,
-// 1024 + q_{8+j}) (low and high halves), j = 0..7, paired with the
-// activation dwords x[j] = (a_j, a_{8+j}); no scaling of the activations.
-// acc0 gathers the even j, acc1 the odd j.
+// 2-bit codes: a dword w holds 16 codes, input i in bits [2i, 2i+2); pair j
+// is (q_j, q_{8+j}), j = 0..7, the halves' fields at bits 2j and 16+2j.  Left
+// in place, field j or-ed with 0x6400 is the fp16 1024 + 4^j q for j < 5 (it
+// stays within the 10 mantissa bits); fields 5..7 are taken the same way from
+// w >> 10, as 1024 + 4^(j-5) q.  The activation dwords x[j] = (a_j, a_{8+j})
+// carry the inverse power (crumb_scale_log2).  acc0 gathers the even j, acc1
+// the odd j.  One and-or per pair plus one shift per dword.
 __device__ __forceinline__ void dot_crumb16(uint32_t w, const uint32_t* x, float& acc0, float& acc1) {
-    const uint32_t M = 0x64006400u;
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-        acc0 = dot2(((w >> (2 * j)) & 0x00030003u) | M, x[j], acc0);
-        acc1 = dot2(((w >> (2 * j + 2)) & 0x00030003u) | M, x[j + 1], acc1);
-    }
+    const uint32_t M = magic_1024x2();
+    const uint32_t v = w >> 10;
+    acc0 = dot2((w & 0x00030003u) | M, x[0], acc0);
+    acc1 = dot2((w & 0x000C000Cu) | M, x[1], acc1);
+    acc0 = dot2((w & 0x00300030u) | M, x[2], acc0);
+    acc1 = dot2((w & 0x00C000C0u) | M, x[3], acc1);
+    acc0 = dot2((w & 0x03000300u) | M, x[4], acc0);
+    acc1 = dot2((v & 0x00030003u) | M, x[5], acc1);
+    acc0 = dot2((v & 0x000C000Cu) | M, x[6], acc0);
+    acc1 = dot2((v & 0x00300030u) | M, x[7], acc1);
 }
+
+// log2 of the factor that pair j of dot_crumb16 needs on its activations
+__device__ __forceinline__ int crumb_scale_log2(int j) { return j < 5 ? -2 * j : -2 * (j - 5); }
 
 __device__ __forceinline__ float f16lo(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));

@@ -18,7 +18,11 @@ constexpr int kHParts = 1;         // fp16 parts used for the intermediate h
 constexpr int kMaxDownGroups = 64; // input groups (of I) per down work item
 constexpr int kMaxGateUpGroupsPerWave = 32;
 constexpr int kCounterStride = 64;  // arrival counters 256 bytes apart (own cache lines)
-constexpr int kDepth = 8;           // weight groups in flight per wave in k_gate_up
+// Weight groups in flight per wave in k_gate_up.  Shallow on purpose: with one
+// wave per SIMD and every wave's loads queued at once, deeper rings delay each
+// wave's first groups behind the others' later ones (measured: 3 beats 4, 6, 8
+// and 12 at hidden 2816 and 6144, for 4-bit and 2-bit records).
+constexpr int kDepth = 3;
 constexpr int kMaxSharedItems = 8;  // down work items of the shared expert
 constexpr int kMaxItems = kMaxTopK + kMaxSharedItems;
 

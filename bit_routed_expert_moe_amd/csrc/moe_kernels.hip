@@ -50,7 +50,9 @@ __device__ void prep_group(const void* x, int t, int H, int g, uint32_t* pairs, 
     constexpr int SET = BITS == 4 ? 8 : 16;  // inputs per pairing set
     constexpr int PD = SET / 2;              // pair dwords per set and part
     const int p = lane % SET, set = lane / SET;
-    const float vs = v * ldexpf(1.0f, e) * ((BITS == 4 && (p & 1)) ? 0.0625f : 1.0f);
+    // nibbles: odd p / 16; 2-bit codes: the in-place factor of pair p % 8
+    const int sh = BITS == 4 ? ((p & 1) ? -4 : 0) : crumb_scale_log2(p & 7);
+    const float vs = v * ldexpf(1.0f, e + sh);
     const _Float16 hi = (_Float16)vs;
     const _Float16 lo = (_Float16)(vs - (float)hi);
     const double kd = wave_sum_d((double)(float)hi + (XP == 2 ? (double)(float)lo : 0.0));
@@ -451,10 +453,11 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     const float mx = wave_max(lane < 32 ? fabsf(h) : 0.0f);
     const int e = act_exponent(mx);
     // h pairs as the activations: (h_p, h_{p+4}) per 8-set with odd p / 16 for
-    // nibbles; (h_p, h_{p+8}) per 16-set, unscaled, for 2-bit codes
+    // nibbles; (h_p, h_{p+8}) per 16-set with pair p % 8's factor for 2-bit codes
     constexpr int SET = BITS == 4 ? 8 : 16, PD = SET / 2;
     const int p = lane % SET, set = lane / SET;
-    const float v = h * ldexpf(1.0f, e) * ((BITS == 4 && (p & 1)) ? 0.0625f : 1.0f);
+    const int sh = BITS == 4 ? ((p & 1) ? -4 : 0) : crumb_scale_log2(p & 7);
+    const float v = h * ldexpf(1.0f, e + sh);
     const _Float16 hh = (_Float16)v;
     const _Float16 hl = (_Float16)(v - (float)hh);
     double kd = lane < 32 ? (double)(float)hh + (kHParts == 2 ? (double)(float)hl : 0.0) : 0.0;
