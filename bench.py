@@ -49,10 +49,10 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12150.45 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24922897, "moe_kernels.hip", "8e1bcc923c7a6283"),
+    # FETCH_SIZE 12150.40 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24922807, "moe_kernels.hip", "8e6a87112a2ceea9"),
     # 2-bit records: FETCH_SIZE 6813.03 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13991873, "moe_kernels.hip", "8e1bcc923c7a6283"),
+    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13991872, "moe_kernels.hip", "8e6a87112a2ceea9"),
     # FETCH_SIZE 1833665.77 KiB x 2.0 + WRITE_SIZE 5753.88 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
     ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761239471, "moe_prefill.hip", "5e0050176b420ab5"),
@@ -197,12 +197,58 @@ def cpu_baseline(wl, xs_host, seconds, args):
             "kind": "oracle", "sample": f"{n} token-layers, {spent:.1f} s"}
 
 
+LOOKAHEAD_RECALL = 0.716  # top-8 recall of the lookahead router on a real model (Colibri README)
+
+
+def topk_sets(W, X, k):
+    """Top-k expert sets (by float64 logit) of the rows of X under router W [E][H]."""
+    lg = X @ W.T
+    return [set(np.argpartition(-row, k)[:k].tolist()) for row in lg]
+
+
+def lookahead_hints(wl, xs_host, rho):
+    """[S][L][1][H] hints, layer l's from its own input (layer 0's unused)."""
+    import synth
+    S, L = xs_host.shape[0], xs_host.shape[1]
+    return np.stack([np.stack([synth.lookahead_hint(wl.seed, l, s, xs_host[s, l], rho)
+                               for l in range(L)]) for s in range(S)])
+
+
+def lookahead_recall(wl, routers, xs_host, rho, steps):
+    """Mean |top-k(hint) & top-k(x)| / k over the given steps and layers 1..L-1."""
+    import synth
+    k, L = wl.top_k, xs_host.shape[1]
+    hit = n = 0
+    for l in range(1, L):
+        X = xs_host[steps, l, 0]
+        Hh = np.stack([synth.lookahead_hint(wl.seed, l, s, xs_host[s, l], rho)[0] for s in steps])
+        for a, b in zip(topk_sets(routers[l], X, k), topk_sets(routers[l], Hh, k)):
+            hit += len(a & b)
+            n += k
+    return hit / n
+
+
+def calibrate_rho(wl, routers, xs_host, target, steps):
+    """The rho whose hints reach the target recall on these steps (bisection;
+    the recall grows with rho)."""
+    lo, hi = 0.0, 1.0
+    for _ in range(14):
+        mid = 0.5 * (lo + hi)
+        if lookahead_recall(wl, routers, xs_host, mid, steps) < target:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
 def run_cached(args, wl):
     """Out-of-core decode: each layer keeps wl.n_slots HBM slots filled from a
     pinned host pool of all its experts (--cache-policy, default LFU; with
     --pin N the N experts used most during the warm-up steps are pinned per
-    layer before the timed steps).  Launched eagerly: every layer synchronises
-    the host on its expert ids."""
+    layer before the timed steps; with --lookahead N each layer l+1 prefetches
+    the top N experts of a hint derived from its input before layer l runs, the
+    hints' noise set so that their top-8 recall is the pages' 71.6 %).
+    Launched eagerly: every layer synchronises the host on its expert ids."""
     import torch
     import synth
     import synth.gpu
@@ -234,6 +280,25 @@ def run_cached(args, wl):
     xs_host = np.stack([make_inputs(wl, l, S) for l in range(L)], axis=1)  # [S][L][1][H]
     xs = torch.from_numpy(synth.quantize_act(xs_host, wl.act).view(np.int16)).to(dev).view(torch.bfloat16)
     ws = layers[0].workspace(1)
+    W = min(args.warmup, S)
+    K = min(args.steps, S - W)
+    la = None
+    if args.lookahead:
+        routers = []
+        for l in range(L):
+            q, rs_ = synth.router(wl.seed, l, E, H)
+            routers.append(q.astype(np.float64) * rs_.view(np.float16).astype(np.float64)[:, None])
+        rho = calibrate_rho(wl, routers, xs_host, LOOKAHEAD_RECALL, list(range(min(32, S))))
+        hs = torch.from_numpy(synth.quantize_act(lookahead_hints(wl, xs_host, rho), wl.act)
+                              .view(np.int16)).to(dev).view(torch.bfloat16)
+        pid = torch.empty(L, 1, k, dtype=torch.int32, device=dev)
+        pw = torch.empty(L, 1, k, dtype=torch.float32, device=dev)
+        ph = torch.empty(L, k, dtype=torch.int32, pin_memory=True)
+        la = {"n_predict": args.lookahead, "mode": args.lookahead_mode, "hint_rho": round(rho, 4),
+              "recall_target": LOOKAHEAD_RECALL,
+              "recall_timed": round(lookahead_recall(wl, routers, xs_host, rho,
+                                                     list(range(W, W + K))), 4)}
+        del routers
     ids = torch.empty(L, 1, k, dtype=torch.int32, device=dev)
     w = torch.empty(L, 1, k, dtype=torch.float32, device=dev)
     y = torch.empty(L, 1, H, dtype=torch.float32, device=dev)
@@ -243,7 +308,15 @@ def run_cached(args, wl):
 
     def run_step(s):
         for l in range(L):
+            nxt = la is not None and l + 1 < L  # layer l+1's experts from its hint, ahead of layer l
+            if nxt and args.lookahead_mode == "call":
+                layers[l + 1].cache_prefetch(hs[s, l + 1, 0], args.lookahead, ws)
+            elif nxt:  # route the hint now, read the ids once layer l's call has synchronised
+                layers[l + 1].route(hs[s, l + 1], ws, out=(pid[l + 1], pw[l + 1]))
+                ph[l + 1].copy_(pid[l + 1, 0], non_blocking=True)
             layers[l].forward(xs[s, l], ws, out=(ids[l], w[l], y[l]))
+            if nxt and args.lookahead_mode == "ids":
+                layers[l + 1].cache_prefetch_ids(ph[l + 1, :args.lookahead].tolist())
 
     # pinned host -> device bandwidth in the same run (1 GiB, the bound's denominator)
     src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
@@ -259,8 +332,6 @@ def run_cached(args, wl):
     h2d_gbs = 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
-    W = min(args.warmup, S)
-    K = min(args.steps, S - W)
     counts = np.zeros((L, E), dtype=np.int64)  # expert selections per layer over the warm-up
     for s in range(W):
         run_step(s)
@@ -275,6 +346,7 @@ def run_cached(args, wl):
         torch.cuda.synchronize()
     h0 = sum(l_.cache_stats()[0] for l_ in layers)
     m0 = sum(l_.cache_stats()[1] for l_ in layers)
+    p0 = [sum(l_.prefetch_stats()[i] for l_ in layers) for i in (0, 1)]
     t0 = time.perf_counter()
     for s in range(W, W + K):
         run_step(s)
@@ -282,12 +354,18 @@ def run_cached(args, wl):
     wall = time.perf_counter() - t0
     h1 = sum(l_.cache_stats()[0] for l_ in layers)
     m1 = sum(l_.cache_stats()[1] for l_ in layers)
+    p1 = [sum(l_.prefetch_stats()[i] for l_ in layers) for i in (0, 1)]
     ms_per_step = wall * 1e3 / K
     hit_timed = (h1 - h0) / max(1, (h1 - h0) + (m1 - m0))
     hit_all = h1 / max(1, h1 + m1)
     miss_bytes_step = (m1 - m0) / K * rb
-    hbm_bytes_step = L * token_layer_bytes(wl, bits) + miss_bytes_step  # reads + slot writes
-    bound_ms = max(hbm_bytes_step / (PEAK_HBM_GBS * 1e9), miss_bytes_step / (h2d_gbs * 1e9)) * 1e3
+    pref_bytes_step = (p1[0] - p0[0]) / K * rb
+    h2d_bytes_step = miss_bytes_step + pref_bytes_step
+    hbm_bytes_step = L * token_layer_bytes(wl, bits) + h2d_bytes_step  # reads + slot writes
+    bound_ms = max(hbm_bytes_step / (PEAK_HBM_GBS * 1e9), h2d_bytes_step / (h2d_gbs * 1e9)) * 1e3
+    if la:
+        la["prefetch_per_step"] = round((p1[0] - p0[0]) / K, 2)
+        la["prefetch_used_frac"] = round((p1[1] - p0[1]) / max(1, p1[0] - p0[0]), 4)
     out = {
         "metric": METRIC, "value": round(L / (ms_per_step * 1e-3), 1), "unit": "tok/s per layer",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
@@ -297,14 +375,17 @@ def run_cached(args, wl):
                    "shared_inter": Is, "layers": L, "batch": 1, "act": wl.act, "bits": bits,
                    "routing": wl.routing, "gate": gate_desc(args), "n_slots": wl.n_slots,
                    "cache_policy": args.cache_policy, "pinned_per_layer": args.pin,
+                   "lookahead": args.lookahead,
                    "pin_source": f"expert counts over the {W} warm-up steps" if args.pin else None},
         "stack_tok_s": round(1e3 / ms_per_step, 2),
         "hit_rate_timed": round(hit_timed, 4), "hit_rate_all_steps": round(hit_all, 4),
-        "miss_bytes_per_step": int(miss_bytes_step), "h2d_gbps": round(h2d_gbs, 1),
-        "roofline": {"bound": "pcie", "achieved": round(miss_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+        "miss_bytes_per_step": int(miss_bytes_step), "h2d_bytes_per_step": int(h2d_bytes_step),
+        "h2d_gbps": round(h2d_gbs, 1), "lookahead": la,
+        "roofline": {"bound": "pcie", "achieved": round(h2d_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
                      "peak": round(h2d_gbs, 1), "unit": "GB/s",
                      "frac": round(bound_ms / ms_per_step, 4), "traffic": None,
-                     "note": "frac = max(HBM bytes / 8 TB/s, miss bytes / measured H2D) / step time"},
+                     "note": "frac = max(HBM bytes / 8 TB/s, H2D bytes (misses + prefetches) / "
+                             "measured H2D) / step time"},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -512,6 +593,12 @@ def main():
     ap.add_argument("--pin", type=int, default=0,
                     help="slot-cache workloads: pin this many experts per layer, the most used "
                          "during the warm-up steps")
+    ap.add_argument("--lookahead", type=int, default=0, metavar="N",
+                    help="slot-cache workloads: prefetch each next layer's top N experts "
+                         "from a hint (router lookahead); 0 = off")
+    ap.add_argument("--lookahead-mode", choices=("ids", "call"), default="ids",
+                    help="ids: route the hint with moe_route_topk and prefetch the ids after the "
+                         "current layer's call (no extra host wait); call: moe_cache_prefetch")
     ap.add_argument("--bits", type=int, choices=(4, 2), default=4,
                     help="decode workloads: width of the expert weight codes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -337,7 +337,6 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     // 2. which expert
     bool bad = false;
     const uint8_t* rec;
-    int Ie;
     if (routed) {
         int e;
         if (a.logits) {
@@ -354,10 +353,8 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
         }
         rec = a.slots ? a.slots + (size_t)a.slot_ids[(size_t)t * a.k + j] * a.rec_bytes
                       : a.experts + (size_t)e * a.rec_bytes;
-        Ie = a.I;
     } else {
         rec = a.shared;
-        Ie = a.Is;
     }
     // a 32-row block is 48*H bytes of nibbles (a 64-input group = two 16-byte
     // chunks per tile row) or 24*H bytes of 2-bit codes (one chunk per group)
@@ -493,7 +490,7 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int t = blockIdx.y;
     const int ot = blockIdx.x / a.n_items, item = blockIdx.x - ot * a.n_items;
-    int j, ga, gb, Ie;
+    int j, ga, gb;
     const uint8_t* rec;
     if (item < a.k) {
         j = item;
@@ -501,13 +498,11 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
         if (e < 0 || e >= a.E) e = 0;  // h of this slot is NaN already
         rec = a.slots ? a.slots + (size_t)a.slot_ids[(size_t)t * a.k + j] * a.rec_bytes
                       : a.experts + (size_t)e * a.rec_bytes;
-        Ie = a.I;
         ga = 0;
         gb = a.I / 64;
     } else {
         j = a.k;
         rec = a.shared;
-        Ie = a.Is;
         ga = (item - a.k) * a.gis;
         gb = min(ga + a.gis, a.Is / 64);
     }

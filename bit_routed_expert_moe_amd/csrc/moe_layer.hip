@@ -42,10 +42,15 @@ struct SlotCache {
     std::vector<uint64_t> count;      // [E]
     std::vector<uint64_t> last_use;   // [n_slots]
     std::vector<char> pinned;         // [n_slots]
+    std::vector<char> prefetched;     // [n_slots]: entered by a prefetch, not yet selected
     int policy = MOE_CACHE_LFU;
     uint64_t tick = 0, hits = 0, misses = 0;
+    uint64_t prefetch_issued = 0, prefetch_used = 0;
+    bool side_pending = false;        // prefetch copies on `side` not yet waited for
     hipStream_t side = nullptr;
     hipEvent_t ev_ids = nullptr, ev_copies = nullptr;
+    hipEvent_t ev_read = nullptr;     // after the last kernels that read the slots
+    bool read_recorded = false;
     int32_t* h_ids = nullptr;         // pinned staging [k]
     int32_t* h_slots = nullptr;       // pinned staging [k]
 };
@@ -118,7 +123,7 @@ moe_status hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t err, rctr, dctr, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
+    size_t err, rctr, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
         x16, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, total;
     int tile_cap;
 };
@@ -167,6 +172,8 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     o.err = take(4);
     o.rctr = take((size_t)kCounterStride * 4);
     o.dctr = take((size_t)(kPrefillMinTokens - 1) * L->n_otiles * kCounterStride * 4);
+    o.pred_ids = take((size_t)L->d.top_k * 4);  // moe_cache_prefetch's selection
+    o.pred_w = take((size_t)L->d.top_k * 4);
     o.logits = take((size_t)T * L->d.n_experts * 4);
     o.slot_ids = take((size_t)T * k * 4);
     if (T < kPrefillMinTokens) {  // per-token (decode) path
@@ -447,6 +454,10 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
         int slot = c.slot_of[ex];
         if (slot >= 0) {
             ++c.hits;
+            if (c.prefetched[slot]) {
+                ++c.prefetch_used;
+                c.prefetched[slot] = 0;
+            }
         } else {
             ++c.misses;
             for (int q = 0; q < c.n_slots && slot < 0; ++q)
@@ -457,6 +468,7 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
             }
             c.expert_in[slot] = ex;
             c.slot_of[ex] = slot;
+            c.prefetched[slot] = 0;
             if (!copies) {  // the side stream must not overwrite a slot still being read
                 if ((e = hipStreamWaitEvent(c.side, c.ev_ids, 0)) != hipSuccess)
                     return hip_fail(e, "side stream wait");
@@ -476,14 +488,54 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
     // shared expert first, overlapping the copies
     if ((e = decode_units(L, fa, 1, routed_units, L->blk_s, s)) != hipSuccess)
         return hip_fail(e, "gate/up launch");
-    if (copies) {
+    if (copies || c.side_pending) {  // this call's copies and any earlier prefetch copies
         if ((e = hipEventRecord(c.ev_copies, c.side)) != hipSuccess ||
             (e = hipStreamWaitEvent(s, c.ev_copies, 0)) != hipSuccess)
             return hip_fail(e, "copy ordering");
+        c.side_pending = false;
     }
     if ((e = decode_units(L, fa, 1, 0, routed_units, s)) != hipSuccess)
         return hip_fail(e, "gate/up launch");
     if ((e = decode_finish(fa, 1, s)) != hipSuccess) return hip_fail(e, "down launch");
+    if ((e = hipEventRecord(c.ev_read, s)) != hipSuccess) return hip_fail(e, "slot read ordering");
+    c.read_recorded = true;
+    return MOE_OK;
+}
+
+// Slots for the predicted experts pred[0..n) (host), their copies on the side
+// stream once the kernels that last read this layer's slots have finished
+// (later work on the caller's stream, such as other layers, is not waited for).
+moe_status prefetch_place(moe_layer* L, const int32_t* pred, int n) {
+    SlotCache& c = L->cache;
+    bool waited = false;
+    for (int j = 0; j < n; ++j) {
+        const int ex = pred[j];
+        if (c.slot_of[ex] >= 0) continue;
+        int slot = -1;
+        for (int q = 0; q < c.n_slots && slot < 0; ++q)
+            if (c.expert_in[q] < 0) slot = q;
+        if (slot < 0) {
+            slot = victim_slot(c, pred, n);
+            if (slot < 0) break;  // every other slot pinned or predicted
+            c.slot_of[c.expert_in[slot]] = -1;
+        }
+        c.expert_in[slot] = ex;
+        c.slot_of[ex] = slot;
+        c.prefetched[slot] = 1;
+        c.last_use[slot] = c.tick;
+        hipError_t e = hipSuccess;
+        if (!waited) {  // a slot being replaced may still be read by this layer's last call
+            if (c.read_recorded && (e = hipStreamWaitEvent(c.side, c.ev_read, 0)) != hipSuccess)
+                return hip_fail(e, "side stream wait");
+            waited = true;
+        }
+        e = hipMemcpyAsync(L->w.slots + (size_t)slot * L->rec_bytes,
+                           L->w.host_pool + (size_t)ex * L->rec_bytes, L->rec_bytes,
+                           hipMemcpyHostToDevice, c.side);
+        if (e != hipSuccess) return hip_fail(e, "prefetch copy into its slot");
+        ++c.prefetch_issued;
+        c.side_pending = true;
+    }
     return MOE_OK;
 }
 
@@ -600,10 +652,12 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         c.count.assign(d.n_experts, 0);
         c.last_use.assign(d.n_slots, 0);
         c.pinned.assign(d.n_slots, 0);
+        c.prefetched.assign(d.n_slots, 0);
         c.policy = d.cache_policy;
         hipError_t e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_ids, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_copies, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_read, hipEventDisableTiming);
         if (e == hipSuccess) e = hipHostMalloc((void**)&c.h_ids, sizeof(int32_t) * d.top_k, 0);
         if (e == hipSuccess) e = hipHostMalloc((void**)&c.h_slots, sizeof(int32_t) * d.top_k, 0);
         if (e != hipSuccess) {
@@ -623,6 +677,7 @@ moe_status moe_layer_destroy(moe_layer_t layer) {
     if (c.h_slots) (void)hipHostFree(c.h_slots);
     if (c.ev_ids) (void)hipEventDestroy(c.ev_ids);
     if (c.ev_copies) (void)hipEventDestroy(c.ev_copies);
+    if (c.ev_read) (void)hipEventDestroy(c.ev_read);
     if (c.side) (void)hipStreamDestroy(c.side);
     delete layer;
     return MOE_OK;
@@ -763,6 +818,12 @@ moe_status moe_cache_pin(moe_layer_t L, const int32_t* experts, int32_t n, void*
             if (experts[j] == experts[i]) return fail(MOE_ERR_ARG, "duplicate expert id");
     }
     hipStream_t s = (hipStream_t)stream;
+    if (c.side_pending) {  // a prefetch copy may still be writing a slot this call replaces
+        hipError_t e = hipEventRecord(c.ev_copies, c.side);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, c.ev_copies, 0);
+        if (e != hipSuccess) return hip_fail(e, "copy ordering");
+        c.side_pending = false;
+    }
     std::fill(c.pinned.begin(), c.pinned.end(), 0);
     ++c.tick;
     for (int i = 0; i < n; ++i) {
@@ -783,8 +844,59 @@ moe_status moe_cache_pin(moe_layer_t L, const int32_t* experts, int32_t n, void*
             if (e != hipSuccess) return hip_fail(e, "pinned expert copy");
         }
         c.pinned[slot] = 1;
+        c.prefetched[slot] = 0;
         c.last_use[slot] = c.tick;
     }
+    return MOE_OK;
+}
+
+moe_status moe_cache_prefetch(moe_layer_t L, const void* x_hint, int32_t n_predict, void* workspace,
+                              int32_t* predicted, void* stream) {
+    moe_status st = check_call(L, x_hint, 1, workspace);
+    if (st != MOE_OK) return st;
+    SlotCache& c = L->cache;
+    if (!c.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    const int k = L->d.top_k;
+    if (n_predict < 1 || n_predict > k) return fail(MOE_ERR_ARG, "n_predict must be in 1..top_k");
+    const WsLayout o = ws_layout(L, 1);
+    uint8_t* ws = (uint8_t*)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* pid = (int32_t*)(ws + o.pred_ids);
+    RouteArgs a = route_args(L, x_hint, pid, (float*)(ws + o.pred_w), ws, o, 0, 1);
+    hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(a, 1, L->d.act_dtype == MOE_BF16, s); });
+    if (e == hipSuccess) e = timed(K_TOPK, s, [&] { return launch_topk(a, 1, s); });
+    if (e != hipSuccess) return hip_fail(e, "lookahead router launch");
+    e = hipMemcpyAsync(c.h_ids, pid, sizeof(int32_t) * k, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(c.ev_ids, s);
+    if (e == hipSuccess) e = hipEventSynchronize(c.ev_ids);
+    if (e != hipSuccess) return hip_fail(e, "reading the predicted experts");
+    for (int j = 0; j < n_predict; ++j)
+        if (c.h_ids[j] < 0 || c.h_ids[j] >= L->d.n_experts)
+            return fail(MOE_ERR_ARG, "predicted expert id out of range");
+    if (predicted) std::copy(c.h_ids, c.h_ids + n_predict, predicted);
+    return prefetch_place(L, c.h_ids, n_predict);
+}
+
+moe_status moe_cache_prefetch_ids(moe_layer_t L, const int32_t* experts, int32_t n, void* stream) {
+    if (!L) return fail(MOE_ERR_ARG, "null layer handle");
+    SlotCache& c = L->cache;
+    if (!c.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    if (n < 1 || n > L->d.top_k) return fail(MOE_ERR_ARG, "n must be in 1..top_k");
+    if (!experts) return fail(MOE_ERR_ARG, "null experts");
+    for (int i = 0; i < n; ++i) {
+        if (experts[i] < 0 || experts[i] >= L->d.n_experts) return fail(MOE_ERR_ARG, "expert id out of range");
+        for (int j = 0; j < i; ++j)
+            if (experts[j] == experts[i]) return fail(MOE_ERR_ARG, "duplicate expert id");
+    }
+    (void)stream;  // the copies are ordered by the layer's own slot reads
+    return prefetch_place(L, experts, n);
+}
+
+moe_status moe_cache_prefetch_stats(moe_layer_t L, uint64_t* issued, uint64_t* used) {
+    if (!L || !issued || !used) return fail(MOE_ERR_ARG, "null argument");
+    if (!L->cache.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    *issued = L->cache.prefetch_issued;
+    *used = L->cache.prefetch_used;
     return MOE_OK;
 }
 

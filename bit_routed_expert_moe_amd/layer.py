@@ -25,6 +25,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIG
 EXPORTS = ["moe_expert_record_bytes", "moe_expert_record_bytes_bits", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
+           "moe_cache_prefetch", "moe_cache_prefetch_ids", "moe_cache_prefetch_stats",
            "moe_poll_device_error",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
            "moe_status_str", "moe_last_error"]
@@ -78,6 +79,9 @@ def lib() -> C.CDLL:
         L.moe_poll_device_error.argtypes = [vp, vp, vp]
         L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
         L.moe_cache_pin.argtypes = [vp, C.POINTER(C.c_int32), i32, vp]
+        L.moe_cache_prefetch.argtypes = [vp, vp, i32, vp, C.POINTER(C.c_int32), vp]
+        L.moe_cache_prefetch_ids.argtypes = [vp, C.POINTER(C.c_int32), i32, vp]
+        L.moe_cache_prefetch_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = C.c_char_p
         L.moe_last_error.restype = C.c_char_p
@@ -87,7 +91,8 @@ def lib() -> C.CDLL:
         for f in ["moe_layer_create", "moe_layer_destroy", "moe_route_topk", "moe_expert_ffn",
                   "moe_combine", "moe_layer_forward", "moe_stack_forward",
                   "moe_poll_device_error", "moe_profile_start", "moe_profile_stop",
-                  "moe_cache_stats", "moe_cache_pin"]:
+                  "moe_cache_stats", "moe_cache_pin", "moe_cache_prefetch", "moe_cache_prefetch_ids",
+                  "moe_cache_prefetch_stats"]:
             getattr(L, f).restype = i32
         _LIB = L
     return _LIB
@@ -192,13 +197,18 @@ class Layer:
             raise ValueError(f"x must be [T][{self.hidden}]")
         return _dev(x, "x", self.act_dtype)
 
-    def route(self, x: torch.Tensor, ws: torch.Tensor | None = None):
+    def route(self, x: torch.Tensor, ws: torch.Tensor | None = None, out=None):
         T = x.shape[0]
         ws = self.workspace(T) if ws is None else ws
-        ids = torch.empty(T, self.top_k, dtype=torch.int32, device="cuda")
-        w = torch.empty(T, self.top_k, dtype=torch.float32, device="cuda")
-        _check(lib().moe_route_topk(self.handle, self._x(x), T, ids.data_ptr(), w.data_ptr(),
-                                    _dev(ws, "workspace"), _stream()))
+        if out is None:
+            ids = torch.empty(T, self.top_k, dtype=torch.int32, device="cuda")
+            w = torch.empty(T, self.top_k, dtype=torch.float32, device="cuda")
+        else:
+            ids, w = out
+            if ids.shape != (T, self.top_k) or w.shape != (T, self.top_k):
+                raise ValueError("out must be ([T][k] int32, [T][k] float32)")
+        _check(lib().moe_route_topk(self.handle, self._x(x), T, _dev(ids, "ids", torch.int32),
+                                    _dev(w, "w", torch.float32), _dev(ws, "workspace"), _stream()))
         return ids, w
 
     def ffn(self, x: torch.Tensor, ids: torch.Tensor, ws: torch.Tensor | None = None):
@@ -240,6 +250,28 @@ class Layer:
         """Pin these expert ids into the slot cache (replacing any pinned set)."""
         ids = (C.c_int32 * max(len(experts), 1))(*[int(e) for e in experts])
         _check(lib().moe_cache_pin(self.handle, ids, len(experts), _stream()))
+
+    def cache_prefetch(self, x_hint: torch.Tensor, n_predict: int | None = None,
+                       ws: torch.Tensor | None = None) -> list[int]:
+        """Router lookahead: fetch the experts x_hint ([H] or [1][H]) selects into
+        the slot cache ahead of this layer's own call; returns the predicted ids."""
+        n = self.top_k if n_predict is None else int(n_predict)
+        ws = self.workspace(1) if ws is None else ws
+        out = (C.c_int32 * max(n, 1))()
+        _check(lib().moe_cache_prefetch(self.handle, self._x(x_hint.reshape(1, -1)), n,
+                                        _dev(ws, "workspace"), out, _stream()))
+        return [int(v) for v in out[:n]]
+
+    def cache_prefetch_ids(self, experts) -> None:
+        """Prefetch these host-side predicted expert ids (no router, no wait)."""
+        ids = (C.c_int32 * max(len(experts), 1))(*[int(e) for e in experts])
+        _check(lib().moe_cache_prefetch_ids(self.handle, ids, len(experts), _stream()))
+
+    def prefetch_stats(self):
+        """(copies issued by cache_prefetch, prefetched experts selected before eviction)."""
+        a, b = C.c_uint64(), C.c_uint64()
+        _check(lib().moe_cache_prefetch_stats(self.handle, C.byref(a), C.byref(b)))
+        return int(a.value), int(b.value)
 
     def poll_error(self, ws: torch.Tensor):
         _check(lib().moe_poll_device_error(self.handle, _dev(ws, "workspace"), _stream()))

@@ -241,6 +241,41 @@ moe_status moe_cache_stats(moe_layer_t layer, uint64_t* hits, uint64_t* misses);
  * neither hit nor miss.  Errors: ARG, STATE (no slot cache), HIP. */
 moe_status moe_cache_pin(moe_layer_t layer, const int32_t* experts, int32_t n, void* stream);
 
+/* Router lookahead: starts copying the experts this layer is predicted to
+ * select before its own router runs, from a hint vector that is available
+ * earlier -- the next layer's router applied to the current layer's state, as
+ * the experimental router-lookahead prefetch of the Colibri README (PILOT=1)
+ * and the Colibri analysis report (section 5) describe.
+ *   x_hint     device [H], the layer's act_dtype: one token's hint vector.
+ *   n_predict  1..top_k: how many of the hint's top-k experts to fetch.
+ *   workspace  as for the compute calls (moe_workspace_bytes(layer, 1) or more).
+ *   predicted  host [n_predict] or NULL: receives the predicted ids, rank order.
+ * Runs the router and top-k on x_hint on `stream`, waits on the host for the
+ * predicted ids, and copies every predicted expert that is not resident from
+ * host_pool into a free slot, else into the slot the cache policy would evict
+ * (never a pinned slot or another predicted expert; with none left the rest
+ * are skipped), on the handle's side stream, ordered after the layer's own
+ * earlier kernels that read its slots (not after other work on `stream`).
+ * The next compute call on the layer waits for those copies
+ * before it reads any slot.  Prefetching changes only which experts are
+ * resident: results stay bit-identical, and hits and misses are counted at the
+ * compute calls as before (a prefetched expert that is then selected is a
+ * hit).  moe_cache_prefetch_stats returns the copies issued and how many of
+ * the prefetched experts were selected before being evicted.
+ * Errors: ARG, ALIGN, STATE (no slot cache), HIP. */
+moe_status moe_cache_prefetch(moe_layer_t layer, const void* x_hint, int32_t n_predict,
+                              void* workspace, int32_t* predicted, void* stream);
+
+/* The same prefetch for predicted ids the caller already holds on the host
+ * (for instance from moe_route_topk on the hint and an asynchronous copy that
+ * the caller has seen complete): no router launch and no host wait.
+ *   experts  host [n] distinct ids in [0, E), most confident first; 1 <= n <= top_k.
+ * Copies are ordered as for moe_cache_prefetch; `stream` is the layer's
+ * stream (unused by the copies themselves).  Errors: ARG, STATE, HIP. */
+moe_status moe_cache_prefetch_ids(moe_layer_t layer, const int32_t* experts, int32_t n,
+                                  void* stream);
+moe_status moe_cache_prefetch_stats(moe_layer_t layer, uint64_t* issued, uint64_t* used);
+
 /* Reads and clears the device error flag kept in `workspace` (synchronises
  * `stream`).  MOE_OK if no kernel reported bad input since the last poll,
  * MOE_ERR_DEVICE otherwise. */

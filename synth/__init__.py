@@ -53,6 +53,8 @@ KIND_GUMBEL = 9
 KIND_Z1 = 10
 KIND_Z2 = 11
 KIND_SEL_BIAS = 12
+KIND_HINT1 = 13
+KIND_HINT2 = 14
 SHARED_INDEX = 0xFFFF  # expert index used for the shared expert's streams
 
 
@@ -172,6 +174,20 @@ def activations(seed: int, layer: int, step: int, hidden: int, n_tokens: int = 1
     n = n_tokens * hidden
     x = normal(key(seed, layer, KIND_X1, step, attempt), key(seed, layer, KIND_X2, step, attempt), n)
     return x.reshape(n_tokens, hidden)
+
+
+def lookahead_hint(seed: int, layer: int, step: int, x: np.ndarray, rho: float) -> np.ndarray:
+    """A noisy preview of the activations x ([n][H] float64) as a lookahead
+    router sees them a layer early: rho * x + sqrt(1 - rho^2) * std(x) * z per
+    token, z ~ N(0, 1) seeded per (layer, step).  In a residual stream the next
+    layer's input is the current state plus the current layer's update; rho
+    sets how far that update moves it.  The pages give the recall such a
+    preview reaches on a real model, not rho, so callers pick rho for a recall."""
+    x = np.asarray(x, dtype=np.float64)
+    z = normal(key(seed, layer, KIND_HINT1, step), key(seed, layer, KIND_HINT2, step), x.size)
+    z = z.reshape(x.shape)
+    sd = x.std(axis=-1, keepdims=True)
+    return rho * x + math.sqrt(max(0.0, 1.0 - rho * rho)) * sd * z
 
 
 def quantize_act(x: np.ndarray, act: str) -> np.ndarray:

@@ -103,6 +103,10 @@ def test_create_rejects_missing_and_misaligned_pointers():
 def test_null_handles():
     lib = L.lib()
     assert lib.moe_cache_pin(None, None, 0, None) == -1
+    assert lib.moe_cache_prefetch(None, None, 8, None, None, None) == -1
+    assert lib.moe_cache_prefetch_ids(None, None, 1, None) == -1
+    a, b = C.c_uint64(), C.c_uint64()
+    assert lib.moe_cache_prefetch_stats(None, C.byref(a), C.byref(b)) == -1
     assert lib.moe_layer_destroy(None) == -1
     assert lib.moe_workspace_bytes(None, 1) == 0
     assert lib.moe_layer_forward(None, None, 1, None, None, None, None, None) == -1

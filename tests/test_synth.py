@@ -102,3 +102,17 @@ def test_selection_bias_is_seeded_and_bounded():
     assert np.array_equal(a, synth.selection_bias(7, 0, 300))
     assert not np.array_equal(a, synth.selection_bias(7, 1, 300))
     assert abs(float(a.mean())) < 0.01 and float(a.std()) > 0.02
+
+
+def test_lookahead_hint_is_a_seeded_noisy_preview():
+    x = synth.activations(5, 2, 3, 4096, n_tokens=2)
+    assert np.array_equal(synth.lookahead_hint(5, 2, 3, x, 1.0), x)
+    h = synth.lookahead_hint(5, 2, 3, x, 0.8)
+    assert np.array_equal(h, synth.lookahead_hint(5, 2, 3, x, 0.8))
+    assert not np.array_equal(h, synth.lookahead_hint(5, 3, 3, x, 0.8))
+    for t in range(2):
+        c = np.corrcoef(x[t], h[t])[0, 1]
+        assert abs(c - 0.8) < 0.02, c
+        assert abs(h[t].std() / x[t].std() - 1.0) < 0.05
+    z = synth.lookahead_hint(5, 2, 3, x, 0.0)
+    assert abs(np.corrcoef(x[0], z[0])[0, 1]) < 0.05
