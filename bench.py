@@ -22,8 +22,8 @@ instead: a step is one 128-token chunk through one layer, cycling over
 --prefill-layers layers of distinct weights; the roofline entry is the grouped
 gate/up kernel's, with its MFMA utilisation.  --workload
 offload_h2816_e256_l40_lfu16 measures the out-of-core decode with the HBM
-slot cache.  --bits 2 runs the decode workloads on 2-bit records of the same
-affine group-64 format.
+slot cache.  --bits 2 runs any workload on 2-bit records of the same affine
+group-64 format.
 """
 from __future__ import annotations
 
@@ -405,21 +405,22 @@ def run_prefill(args, wl):
     NL, C = args.prefill_layers, args.prefill_chunks
     dev = torch.device("cuda:0")
     torch.cuda.set_device(0)
-    rb, rbs = record_bytes(H, I), (record_bytes(H, Is) if Is else 0)
+    bits = args.bits
+    rb, rbs = record_bytes(H, I, bits), (record_bytes(H, Is, bits) if Is else 0)
     t_setup = time.time()
     layers, pools = [], []
     for l in range(NL):
         rq, rs = synth.router(wl.seed, l, E, H)
         pool = torch.empty(E * rb, dtype=torch.uint8, device=dev)
-        synth.gpu.fill_records(pool, H, I, wl.seed, l, 0, E)
+        synth.gpu.fill_records(pool, H, I, wl.seed, l, 0, E, bits=bits)
         shared = None
         if Is:
             shared = torch.empty(rbs, dtype=torch.uint8, device=dev)
-            synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1)
+            synth.gpu.fill_records(shared, H, Is, wl.seed, l, -1, 1, bits=bits)
         pools.append((pool, shared, rq, rs))
         layers.append(Layer(H, E, I, k, Is, torch.from_numpy(rq).to(dev),
                             torch.from_numpy(rs.view(np.float16)).to(dev), pool, shared, act=wl.act,
-                            **gate_kwargs(args, wl, l, dev)))
+                            bits=bits, **gate_kwargs(args, wl, l, dev)))
     S = NL * C  # distinct (layer, chunk) steps
     xs_host = np.empty((S, T, H))
     for l in range(NL):
@@ -500,8 +501,8 @@ def run_prefill(args, wl):
             run_step(s)
 
     recs = kernel_timed_pass(profiled_steps, S * 8 + 64)
-    per_step_bytes = {"grouped_gate_up": uniq * gu_bytes(H, I) + (gu_bytes(H, Is) if Is else 0),
-                      "grouped_down": uniq * down_bytes(H, I) + (down_bytes(H, Is) if Is else 0)}
+    per_step_bytes = {"grouped_gate_up": uniq * gu_bytes(H, I, bits) + (gu_bytes(H, Is, bits) if Is else 0),
+                      "grouped_down": uniq * down_bytes(H, I, bits) + (down_bytes(H, Is, bits) if Is else 0)}
     kernels = {}
     for name in sorted({r[0] for r in recs}):
         ms = np.array([m for n_, m in recs if n_ == name])
@@ -515,7 +516,7 @@ def run_prefill(args, wl):
     gu = kernels["grouped_gate_up"]
     gu_flops = float(np.mean(2.0 * 16 * 2 * H * (tiles * I + shared_tiles * Is)))
     roofline = {"bound": "hbm", "achieved": gu["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4), "traffic": traffic_for(wl.name, "k_gu_grouped"),
+                "frac": round(gu["gbps"] / PEAK_HBM_GBS, 4), "traffic": traffic_for(wl.name, "k_gu_grouped", bits),
                 "kernel": "k_gu_grouped", "alg_bytes_per_launch": gu["alg_bytes_mean"],
                 "avg_launch_us": gu["avg_us"], "timing": "hipExtLaunchKernelGGL start/stop events",
                 "mfma_util": round(gu_flops / (gu["avg_us"] * 1e-6) / mfma_peak, 4)}
@@ -529,9 +530,10 @@ def run_prefill(args, wl):
         "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tok/s per layer",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "u4 weights x f16 activations -> f32 (MFMA)", "data": "synthetic",
+        "dtype": dtype_desc(bits) + " (MFMA)", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "n_experts": E, "inter": I, "top_k": k,
                    "shared_inter": Is, "chunk_tokens": T, "act": wl.act, "routing": wl.routing, "gate": gate_desc(args),
+                   "bits": bits,
                    "weight_sets": NL, "distinct_chunks": S, "graph_chunk": G},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
         "alg_bytes_per_chunk": int(mean_bytes), "unique_experts_mean": round(float(uniq.mean()), 2),
@@ -558,8 +560,9 @@ def prefill_cpu_baseline(wl, pool, x_chunk, seconds, args):
         xd = orc.act_to_f64(wl.act, x_chunk[t])
         t0 = time.perf_counter()
         ids, w, _ = oracle_route(orc, args, wl, 0, rq, rs, xd)
-        yr = np.stack([orc.expert_ffn(H, I, host[int(e) * rb:(int(e) + 1) * rb], xd) for e in ids])
-        ys = orc.expert_ffn(H, Is, shared, xd) if Is else None
+        yr = np.stack([orc.expert_ffn(H, I, host[int(e) * rb:(int(e) + 1) * rb], xd, bits=args.bits)
+                       for e in ids])
+        ys = orc.expert_ffn(H, Is, shared, xd, bits=args.bits) if Is else None
         orc.combine(w, yr, ys)
         spent += time.perf_counter() - t0
         n += 1
@@ -600,7 +603,7 @@ def main():
                     help="ids: route the hint with moe_route_topk and prefetch the ids after the "
                          "current layer's call (no extra host wait); call: moe_cache_prefetch")
     ap.add_argument("--bits", type=int, choices=(4, 2), default=4,
-                    help="decode workloads: width of the expert weight codes")
+                    help="width of the expert weight codes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -630,10 +633,6 @@ def main():
     if wl.n_slots:
         return run_cached(args, wl)
     if wl.n_tokens != 1:
-        if args.bits != 4:
-            print("--bits 2 applies to the decode workloads: the grouped prefill path reads "
-                  "4-bit records only", file=sys.stderr)
-            sys.exit(2)
         return run_prefill(args, wl)
     H, E, I, k, Is, L, T = (wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter,
                             wl.n_layers, wl.n_tokens)

@@ -105,6 +105,7 @@ struct PrefillArgs {
     size_t rec_bytes;
     size_t rec_bytes_shared;
     uint16_t* x16;           // [XP][T][H] fp16 parts of x * 2^e (one e per token), slot order
+    uint16_t* x16b;          // 2-bit records: the same in the 2-bit slot order (gate/up operand)
     float* xsum;             // [T][H/64] sum of each group of x * 2^e
     float* xinv;             // [T] 2^-e
     int32_t* pair_tok;       // [P] token of each expert-sorted (token, slot) pair
@@ -119,7 +120,8 @@ struct PrefillArgs {
     const int8_t* rq;        // router [E][H] (k_route_tiles)
     const uint16_t* rs;      // router row scales [E] fp16
     float* logits;           // [T][E] out (k_route_tiles)
-    int H, E, I, Is, k, T, P, Imax, tile_cap, xparts;
+    size_t sb_off, sb_off_shared;  // scale/bias region of a routed / the shared record
+    int H, E, I, Is, k, T, P, Imax, tile_cap, xparts, bits;
 };
 
 struct CombineArgs {

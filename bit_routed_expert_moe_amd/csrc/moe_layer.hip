@@ -124,7 +124,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
     size_t err, rctr, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
-        x16, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, total;
+        x16, x16b, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, total;
     int tile_cap;
 };
 
@@ -139,27 +139,8 @@ int grouped_chunk(const moe_layer* L) {
     return (int)std::max<int64_t>(c, kPrefillMinTokens);
 }
 
-// 2-bit layers run every call through the per-token kernels, in passes of
-// at most kPrefillMinTokens - 1 tokens that share one workspace (stream order
-// keeps the passes apart).
-template <typename F>
-moe_status token_passes(int T, F&& pass) {
-    constexpr int P = kPrefillMinTokens - 1;
-    for (int c0 = 0; c0 < T; c0 += P) {
-        const moe_status st = pass(c0, std::min(P, T - c0));
-        if (st != MOE_OK) return st;
-    }
-    return MOE_OK;
-}
-
-// activations of token c0
-const void* x_at(const moe_layer* L, const void* x, int c0) {
-    return (const uint8_t*)x + (size_t)c0 * L->d.hidden * (L->d.act_dtype == MOE_BF16 ? 2 : 4);
-}
-
 WsLayout ws_layout(const moe_layer* L, int T) {
     WsLayout o{};
-    if (L->bits == 2) T = std::min(T, kPrefillMinTokens - 1);  // token passes
     const int H = L->d.hidden, k = L->d.top_k;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -194,6 +175,7 @@ WsLayout ws_layout(const moe_layer* L, int T) {
         o.tile_cap = (int)(std::min<size_t>((size_t)L->d.n_experts, P) + (P + kTileRows - 1) / kTileRows +
                            (Tg + kTileRows - 1) / kTileRows);
         o.x16 = take((size_t)L->xparts * Tg * H * 2);
+        o.x16b = take(L->bits == 2 ? (size_t)L->xparts * Tg * H * 2 : 0);  // 2-bit slot order
         o.pxsum = take(Tg * (H / 64) * 4);
         o.pxinv = take(Tg * 4);
         o.pair_tok = take(P * 4);
@@ -313,6 +295,10 @@ PrefillArgs prefill_args(const moe_layer* L, const void* x, const int32_t* ids, 
     a.rec_bytes = L->rec_bytes;
     a.rec_bytes_shared = L->shared_rec_bytes;
     a.x16 = (uint16_t*)(ws + o.x16);
+    a.x16b = (uint16_t*)(ws + o.x16b);
+    a.bits = L->bits;
+    a.sb_off = L->sb_off;
+    a.sb_off_shared = L->sb_off_shared;
     a.xsum = (float*)(ws + o.pxsum);
     a.xinv = (float*)(ws + o.pxinv);
     a.pair_tok = (int32_t*)(ws + o.pair_tok);
@@ -693,11 +679,6 @@ moe_status moe_route_topk(moe_layer_t L, const void* x, int32_t T, int32_t* ids,
     moe_status st = check_call(L, x, T, workspace);
     if (st != MOE_OK) return st;
     if (!ids || !w) return fail(MOE_ERR_ARG, "null ids or w");
-    const size_t k = L->d.top_k;
-    if (L->bits == 2 && T >= kPrefillMinTokens)
-        return token_passes(T, [&](int c0, int Tc) {
-            return moe_route_topk(L, x_at(L, x, c0), Tc, ids + c0 * k, w + c0 * k, workspace, stream);
-        });
     const WsLayout o = ws_layout(L, T);
     hipStream_t s = (hipStream_t)stream;
     if (T >= kPrefillMinTokens)  // the grouped path's router (MFMA tiles), as the forward call
@@ -715,13 +696,6 @@ moe_status moe_expert_ffn(moe_layer_t L, const void* x, int32_t T, const int32_t
     if (st != MOE_OK) return st;
     if (L->cache.n_slots && T != 1) return fail(MOE_ERR_STATE, "the slot cache runs one token per call");
     if (!ids || !expert_out) return fail(MOE_ERR_ARG, "null ids or expert_out");
-    if (L->bits == 2 && T >= kPrefillMinTokens) {
-        const size_t k = L->d.top_k, H = L->d.hidden;
-        return token_passes(T, [&](int c0, int Tc) {
-            return moe_expert_ffn(L, x_at(L, x, c0), Tc, ids + c0 * k, workspace,
-                                  expert_out + c0 * (k + 1) * H, stream);
-        });
-    }
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
@@ -756,13 +730,6 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     if (st != MOE_OK) return st;
     if (L->cache.n_slots && T != 1) return fail(MOE_ERR_STATE, "the slot cache runs one token per call");
     if (!ids || !w || !y) return fail(MOE_ERR_ARG, "null ids, w or y");
-    if (L->bits == 2 && T >= kPrefillMinTokens) {
-        const size_t k = L->d.top_k, H = L->d.hidden;
-        return token_passes(T, [&](int c0, int Tc) {
-            return moe_layer_forward(L, x_at(L, x, c0), Tc, ids + c0 * k, w + c0 * k, y + c0 * H,
-                                     workspace, stream);
-        });
-    }
     const WsLayout o = ws_layout(L, T);
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;

@@ -34,6 +34,15 @@
 // scaled by 16; activations are stored in that order ("slot order") with odd
 // inputs divided by 16, which is exact in fp16.
 //
+// 2-bit records: a 16-byte run of a tile row is a whole 64-input group, and
+// after the lane transpose a lane holds dword kq (inputs 16kq .. 16kq+15) of
+// its rows.  Its codes are taken in place as pairs (q_j, q_{8+j}) scaled by
+// 4^j (j < 5; j >= 5 from the dword shifted by 10, scaled by 4^(j-5)); MFMA
+// step s of the group uses the pairs j = 4s .. 4s+3.  The activations (and h)
+// of that group are stored in the matching 2-bit slot order: input
+// 16kq + 8u + j at position 32(j/4) + 8kq + 2(j%4) + u, times the inverse
+// power of 4 (exact).
+//
 // Streams: weights, scale/bias pairs and activations are read with buffer
 // loads whose per-lane offsets are loop invariant (the loop advances a scalar
 // offset), weights with the nontemporal hint.  A workgroup's waves read the
@@ -73,6 +82,29 @@ struct Unpack {
         asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(hi));
         asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
     }
+    // 8 of the 16 2-bit codes of one dword (pairs j = 4s .. 4s+3, s = 0 or 1)
+    // as fp16 4^j q (4^(j-5) q for j >= 5), in the 2-bit slot order
+    template <int S>
+    __device__ __forceinline__ half8 crumbs(uint32_t w) const {
+        const half2v off = {(_Float16)1024.0f, (_Float16)1024.0f};
+        half2v p0, p1, p2, p3;
+        if (S == 0) {
+            p0 = __builtin_bit_cast(half2v, (w & 0x00030003u) | magic) - off;  // q0, q8
+            p1 = __builtin_bit_cast(half2v, (w & 0x000C000Cu) | magic) - off;  // 4 q1, 4 q9
+            p2 = __builtin_bit_cast(half2v, (w & 0x00300030u) | magic) - off;  // 16 q2, 16 q10
+            p3 = __builtin_bit_cast(half2v, (w & 0x00C000C0u) | magic) - off;  // 64 q3, 64 q11
+        } else {
+            const uint32_t v = w >> 10;
+            p0 = __builtin_bit_cast(half2v, (w & 0x03000300u) | magic) - off;  // 256 q4, 256 q12
+            p1 = __builtin_bit_cast(half2v, (v & 0x00030003u) | magic) - off;  // q5, q13
+            p2 = __builtin_bit_cast(half2v, (v & 0x000C000Cu) | magic) - off;  // 4 q6, 4 q14
+            p3 = __builtin_bit_cast(half2v, (v & 0x00300030u) | magic) - off;  // 16 q7, 16 q15
+        }
+        half8 o;
+        o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+        o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+        return o;
+    }
     // 8 nibbles of one dword -> the exact codes as fp16, in slot order, odd
     // inputs times 16
     __device__ __forceinline__ half8 codes(uint32_t w) const {
@@ -100,6 +132,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t 
 template <int AUX = 0>
 __device__ __forceinline__ uint32_t bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
 }
 template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -146,7 +182,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // ---------------------------------------------------------------------------
 // k_prep_tokens: grid (T), 256 threads.
 // ---------------------------------------------------------------------------
-template <int XP, bool BF16>
+template <int XP, bool BF16, int BITS>
 __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
     __shared__ float row[kMaxHidden];
     __shared__ float red4[kWaves];
@@ -196,6 +232,15 @@ __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
         const size_t dst = (size_t)t * H + 64 * g + (lane & ~7) + slot_of(p);
         a.x16[dst] = hi;
         if (XP == 2) a.x16[(size_t)a.T * H + dst] = f16bits(vq - (float)__builtin_bit_cast(_Float16, hi));
+        if (BITS == 2) {  // the 2-bit slot order for the gate/up operand
+            const int j = lane & 7;
+            const float v2 = vs * ldexpf(1.0f, crumb_scale_log2(j));
+            const uint16_t h2 = f16bits(v2);
+            const size_t d2 = (size_t)t * H + 64 * g + 32 * (j >> 2) + 8 * (lane >> 4) + 2 * (j & 3) +
+                              ((lane >> 3) & 1);
+            a.x16b[d2] = h2;
+            if (XP == 2) a.x16b[(size_t)a.T * H + d2] = f16bits(v2 - (float)__builtin_bit_cast(_Float16, h2));
+        }
         const double gs = wave_sum_d((double)vs);
         if (lane == 0) a.xsum[(size_t)t * NG + g] = (float)gs;
     }
@@ -424,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void k_group(PrefillArgs a) {
 // Dynamic LDS: [H/64][16] group sums of the rows' activations, then the
 // partial sums of the upper-half waves, [2][8][64] float4.
 // ---------------------------------------------------------------------------
-template <int XP>
+template <int XP, int BITS>
 __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
     extern __shared__ float dsm[];
     __shared__ int s_tok[kTileRows];
@@ -461,20 +506,24 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
     if (active && j1 > j0) {
         const uint8_t* rec = shared ? a.shared : a.experts + (size_t)tl.x * a.rec_bytes;
         const __amdgpu_buffer_rsrc_t rw = rsrc(rec, shared ? a.rec_bytes_shared : a.rec_bytes);
-        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x16, (size_t)XP * a.T * H * 2);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(BITS == 2 ? a.x16b : a.x16, (size_t)XP * a.T * H * 2);
         // per-lane offsets (bytes): row 16*kq + n of each GU tile (codes and
         // scale/bias pair; one 16-byte load covers a 1 KB chunk of a tile per
         // wave), and the lane's activations; the rest of each address is
-        // uniform and goes in the scalar offset
+        // uniform and goes in the scalar offset.  A 64-input group is two
+        // chunks of nibbles or one chunk of 2-bit codes.
+        constexpr int NC = BITS == 4 ? 2 : 1;
+        const int blk = (BITS == 4 ? 48 : 24) * H;  // bytes per 32-row block
+        const int sbo = (int)(shared ? a.sb_off_shared : a.sb_off);
         const int rl = 16 * kq + n;
-        const int wo[2] = {48 * H * (2 * gi) + rl * 16, 48 * H * (2 * gi + 1) + rl * 16};
-        const int so[2] = {3 * H * Ie / 2 + 12 * H * gi + rl * 4, 3 * H * Ie / 2 + 12 * H * gi + 4 * H + rl * 4};
+        const int wo[2] = {blk * (2 * gi) + rl * 16, blk * (2 * gi + 1) + rl * 16};
+        const int so[2] = {sbo + 12 * H * gi + rl * 4, sbo + 12 * H * gi + 4 * H + rl * 4};
         const int xo = (max(s_tok[n], 0) * H + 8 * kq) * 2;
         const int xpart = a.T * H * 2;
         const Unpack up;
         struct Regs {
             u32x4 A[2][XP];
-            u32x4 W[2][2];  // [GU tile][chunk], rows 16*kq + n
+            u32x4 W[2][NC];  // [GU tile][chunk], rows 16*kq + n
             uint32_t SB[2];
         };
         auto load = [&](Regs& R, int jg) {  // jg >= j1: a refill past the end
@@ -487,8 +536,8 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], live ? 2048 * jg + 1024 * c : kPastEnd);
+                for (int c = 0; c < NC; ++c)
+                    R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], live ? 1024 * NC * jg + 1024 * c : kPastEnd);
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) R.SB[t2] = bload(rw, so[t2], live ? 256 * jg : kPastEnd);
         };
@@ -496,13 +545,14 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
             const f32x4 xs = *(const f32x4*)&sX[jg * kTileRows + 4 * kq];
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-                const u32x4 w0 = xpose4(R.W[t2][0]), w1 = xpose4(R.W[t2][1]);
+                const u32x4 w0 = xpose4(R.W[t2][0]), w1 = xpose4(R.W[t2][NC - 1]);
                 const u32x4 sb = bcast4(R.SB[t2]);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int nt = 4 * t2 + t;
                     f32x4 pg = {0, 0, 0, 0};
-                    const half8 q0 = up.codes(w0[t]), q1 = up.codes(w1[t]);
+                    const half8 q0 = BITS == 4 ? up.codes(w0[t]) : up.crumbs<0>(w0[t]);
+                    const half8 q1 = BITS == 4 ? up.codes(w1[t]) : up.crumbs<1>(w0[t]);
 #pragma unroll
                     for (int p = 0; p < XP; ++p) pg = mfma(R.A[0][p], q0, pg);
 #pragma unroll
@@ -513,18 +563,19 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
                 }
             }
         };
-        // ring of kGuDepth groups in flight
-        Regs R[kGuDepth];
+        // ring of kGuDepth groups in flight (also for 2-bit groups: deeper measured slower)
+        constexpr int GD = kGuDepth;
+        Regs R[GD];
 #pragma unroll
-        for (int q = 0; q < kGuDepth; ++q) {
+        for (int q = 0; q < GD; ++q) {
             load(R[q], j0 + q);
             __builtin_amdgcn_sched_barrier(0);
         }
-        for (int jb = j0; jb < j1; jb += kGuDepth) {
+        for (int jb = j0; jb < j1; jb += GD) {
 #pragma unroll
-            for (int q = 0; q < kGuDepth; ++q) {
+            for (int q = 0; q < GD; ++q) {
                 if (jb + q < j1) compute(R[q], jb + q);
-                load(R[q], jb + q + kGuDepth);
+                load(R[q], jb + q + GD);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -559,8 +610,10 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
         hs[r] = row16_sum(hs[r]);
     }
     const int NGi = a.Imax / 64;
-    const float odd = (n & 1) ? 0.0625f : 1.0f;
-    const int pslot = (n & ~7) + slot_of(n & 7);
+    // column 16*c4 + n of the group at pslot + pstride*c4, times the slot's factor
+    const float odd = BITS == 4 ? ((n & 1) ? 0.0625f : 1.0f) : ldexpf(1.0f, crumb_scale_log2(n & 7));
+    const int pslot = BITS == 4 ? (n & ~7) + slot_of(n & 7) : 32 * ((n & 7) >> 2) + 2 * (n & 3) + (n >> 3);
+    constexpr int pstride = BITS == 4 ? 16 : 8;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * kq + r;
@@ -570,7 +623,7 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
         const size_t hrow = shared ? (size_t)a.P + tl.y + m : (size_t)(tl.y + m);
         uint16_t* hp = a.h16 + hrow * a.Imax + 64 * gi + pslot;
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) hp[16 * c4] = f16bits(h[r][c4] * sc);
+        for (int c4 = 0; c4 < 4; ++c4) hp[pstride * c4] = f16bits(h[r][c4] * sc);
         if (n == 0) {
             a.hsum[hrow * NGi + gi] = hs[r];
             a.hinv[hrow * NGi + gi] = ldexpf(1.0f, -e);
@@ -584,6 +637,7 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
 // of 16) over all of I; a wave visit reads 2 KB of contiguous record bytes.
 // Dynamic LDS: [Ie/64][16] group sums of h, then [Ie/64][16] 2^-e of h.
 // ---------------------------------------------------------------------------
+template <int BITS>
 __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     extern __shared__ float dsm[];
     __shared__ int s_row[kTileRows];
@@ -613,10 +667,13 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t rw = rsrc(rec, shared ? a.rec_bytes_shared : a.rec_bytes);
     const __amdgpu_buffer_rsrc_t rh = rsrc(a.h16, (size_t)(a.P + a.T) * a.Imax * 2);
     // lane row o0 + 64*hh + 16*kq + n: one 16-byte load covers 64 rows of a
-    // down chunk, one dword load their scale/bias pairs
+    // down chunk of nibbles (two 8-byte loads, of the group's two 32-input
+    // blocks, for 2-bit codes), one dword load their scale/bias pairs
+    constexpr int RB = BITS == 4 ? 16 : 8;       // bytes per row per 32-input block
+    const int blk = (BITS == 4 ? 48 : 24) * H;  // bytes per 32-row block of the record
     const int rl = o0 + 16 * kq + n;
-    const int wo = 32 * H + rl * 16;
-    const int so = 3 * H * Ie / 2 + 8 * H + rl * 4;
+    const int wo = (BITS == 4 ? 32 : 16) * H + rl * RB;
+    const int so = (int)(shared ? a.sb_off_shared : a.sb_off) + 8 * H + rl * 4;
     const int ho = (max(s_row[n], 0) * a.Imax + 8 * kq) * 2;
     const Unpack up;
     f32x4 acc[kNtDn];
@@ -624,7 +681,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     for (int nt = 0; nt < kNtDn; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
     struct Regs {
         u32x4 A[2];
-        u32x4 W[2][2];  // [half][chunk]
+        u32x4 W[2][2];  // [half][chunk] (2-bit: the two blocks' 8 bytes in W[half][0])
         uint32_t SB[2];
     };
     auto load = [&](Regs& R, int jg) {  // jg >= NGe: a refill past the end
@@ -634,9 +691,15 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const bool live = jg < NGe && (hh == 0 || hi_ok);
+            if (BITS == 4) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-                R.W[hh][c] = bload4<kAuxNT>(rw, wo, live ? 48 * H * (2 * jg + c) + 1024 * hh : kPastEnd);
+                for (int c = 0; c < 2; ++c)
+                    R.W[hh][c] = bload4<kAuxNT>(rw, wo, live ? blk * (2 * jg + c) + 1024 * hh : kPastEnd);
+            } else {
+                const u32x2 b0 = bload2<kAuxNT>(rw, wo, live ? blk * (2 * jg) + 512 * hh : kPastEnd);
+                const u32x2 b1 = bload2<kAuxNT>(rw, wo, live ? blk * (2 * jg + 1) + 512 * hh : kPastEnd);
+                R.W[hh][0] = u32x4{b0[0], b0[1], b1[0], b1[1]};
+            }
             R.SB[hh] = bload(rw, so, live ? 12 * H * jg + 256 * hh : kPastEnd);
         }
     };
@@ -645,31 +708,33 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
         const f32x4 hsum = *(const f32x4*)&sH[jg * kTileRows + 4 * kq];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 w0 = xpose4(R.W[hh][0]), w1 = xpose4(R.W[hh][1]);
+            const u32x4 w0 = xpose4(R.W[hh][0]);
+            const u32x4 w1 = BITS == 4 ? xpose4(R.W[hh][1]) : w0;
             const u32x4 sb = bcast4(R.SB[hh]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int nt = 4 * hh + t;
                 f32x4 pd = {0, 0, 0, 0};
-                pd = mfma(R.A[0], up.codes(w0[t]), pd);
-                pd = mfma(R.A[1], up.codes(w1[t]), pd);
+                pd = mfma(R.A[0], BITS == 4 ? up.codes(w0[t]) : up.crumbs<0>(w0[t]), pd);
+                pd = mfma(R.A[1], BITS == 4 ? up.codes(w1[t]) : up.crumbs<1>(w0[t]), pd);
                 const float sd = f16lo(sb[t]), bd = f16hi(sb[t]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[nt][r] = fmaf(bd, hsum[r], fmaf(sd, pd[r] * hi[r], acc[nt][r]));
             }
         }
     };
-    Regs R[kDnDepth];
+    constexpr int DD = kDnDepth;
+    Regs R[DD];
 #pragma unroll
-    for (int q = 0; q < kDnDepth; ++q) {
+    for (int q = 0; q < DD; ++q) {
         load(R[q], q);
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int jb = 0; jb < NGe; jb += kDnDepth) {
+    for (int jb = 0; jb < NGe; jb += DD) {
 #pragma unroll
-        for (int q = 0; q < kDnDepth; ++q) {
+        for (int q = 0; q < DD; ++q) {
             if (jb + q < NGe) compute(R[q], jb + q);
-            load(R[q], jb + q + kDnDepth);
+            load(R[q], jb + q + DD);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -700,16 +765,24 @@ __global__ void k_zero_shared_rows(PrefillArgs a) {  // no shared expert: eo[:, 
     if (o < a.H) a.eo[((size_t)t * (a.k + 1) + a.k) * a.H + o] = 0.0f;
 }
 
-hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s) {
+template <int BITS>
+static void launch_prep_bits(const PrefillArgs& a, int act_bf16, hipStream_t s) {
     const dim3 grid(a.T);
     if (a.xparts == 1 && act_bf16)
-        launch_kernel(k_prep_tokens<1, true>, grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<1, true, BITS>, grid, dim3(kBlock), 0, s, a);
     else if (a.xparts == 1)
-        launch_kernel(k_prep_tokens<1, false>, grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<1, false, BITS>, grid, dim3(kBlock), 0, s, a);
     else if (act_bf16)
-        launch_kernel(k_prep_tokens<2, true>, grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<2, true, BITS>, grid, dim3(kBlock), 0, s, a);
     else
-        launch_kernel(k_prep_tokens<2, false>, grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_prep_tokens<2, false, BITS>, grid, dim3(kBlock), 0, s, a);
+}
+
+hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s) {
+    if (a.bits == 2)
+        launch_prep_bits<2>(a, act_bf16, s);
+    else
+        launch_prep_bits<4>(a, act_bf16, s);
     return hipGetLastError();
 }
 
@@ -730,16 +803,24 @@ hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s) {
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s) {
     const dim3 grid(a.tile_cap, (a.Imax + 127) / 128);
     const size_t lds = (size_t)(a.H / 64) * kTileRows * 4 + (size_t)2 * kNtGu * 64 * 16;
-    if (a.xparts == 1)
-        launch_kernel(k_gu_grouped<1>, grid, dim3(kBlock), lds, s, a);
+    if (a.xparts == 1 && a.bits == 2)
+        launch_kernel(k_gu_grouped<1, 2>, grid, dim3(kBlock), lds, s, a);
+    else if (a.xparts == 1)
+        launch_kernel(k_gu_grouped<1, 4>, grid, dim3(kBlock), lds, s, a);
+    else if (a.bits == 2)
+        launch_kernel(k_gu_grouped<2, 2>, grid, dim3(kBlock), lds, s, a);
     else
-        launch_kernel(k_gu_grouped<2>, grid, dim3(kBlock), lds, s, a);
+        launch_kernel(k_gu_grouped<2, 4>, grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s) {
     const size_t lds = (size_t)(a.Imax / 64) * kTileRows * 8;
-    launch_kernel(k_down_grouped, dim3(a.tile_cap, (a.H + 511) / 512), dim3(kBlock), lds, s, a);
+    const dim3 grid(a.tile_cap, (a.H + 511) / 512);
+    if (a.bits == 2)
+        launch_kernel(k_down_grouped<2>, grid, dim3(kBlock), lds, s, a);
+    else
+        launch_kernel(k_down_grouped<4>, grid, dim3(kBlock), lds, s, a);
     if (!a.Is) launch_kernel(k_zero_shared_rows, dim3((a.H + kBlock - 1) / kBlock, a.T), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }

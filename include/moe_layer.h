@@ -115,9 +115,7 @@ typedef struct moe_layer_desc {
     int32_t cache_policy;  /* n_slots > 0: MOE_CACHE_LFU or MOE_CACHE_LRU (see
                               moe_cache_stats); must be MOE_CACHE_LFU otherwise     */
     int32_t bits;          /* width of the expert weight codes: 4 (0 reads as 4) or 2;
-                              router rows stay int8.  Layers of 2-bit records run
-                              every call through the per-token kernels, at most 3
-                              tokens per pass (the grouped prefill path is 4-bit only) */
+                              router rows stay int8                                */
     int32_t reserved[4];
 } moe_layer_desc;
 

@@ -13,6 +13,7 @@ selected expert once over all of its tokens.  Checked here:
 * a token's result does not depend on the other tokens of its batch
   (permuting the batch permutes the result exactly);
 * out-of-range expert ids raise the device error and poison only their slots.
+Shapes, the API path and the batch invariance run for 4-bit and 2-bit records.
 """
 import sys
 
@@ -66,11 +67,12 @@ def check(dl, orc, xd, ids, w, y, tag, sample=None):
     (8192, 16, 64, 2, 128, "bf16", 9),     # largest hidden
     (256, 8, 128, 2, 8192, "bf16", 6),     # wide shared expert (128 groups of I)
 ])
-def test_grouped_shapes(orc, H, E, I, k, Is, act, T):
-    dl = DeviceLayer(0xB17E0600 + H + E + T, 2, H, E, I, k, Is, act)
+@pytest.mark.parametrize("bits", [4, 2])
+def test_grouped_shapes(orc, H, E, I, k, Is, act, T, bits):
+    dl = DeviceLayer(0xB17E0600 + H + E + T, 2, H, E, I, k, Is, act, bits=bits)
     xq, xd = tokens(dl, orc, T)
     ids, w, y = dl.layer_obj.forward(to_dev(xq, act))
-    check(dl, orc, xd, ids, w, y, f"H{H} E{E} I{I} k{k} S{Is} {act} T{T}")
+    check(dl, orc, xd, ids, w, y, f"{bits}-bit H{H} E{E} I{I} k{k} S{Is} {act} T{T}")
 
 
 def test_repeated_tokens_fill_many_tiles(orc):
@@ -87,8 +89,9 @@ def test_repeated_tokens_fill_many_tiles(orc):
     check(dl, orc, [xd[o] for o in order], ids, w, y, "repeated token", sample=[0, 45, 46, 47, 48, 49])
 
 
-def test_batch_permutation_invariance(orc):
-    dl = DeviceLayer(0xB17E0620, 0, 512, 64, 256, 8, 256, "bf16")
+@pytest.mark.parametrize("bits", [4, 2])
+def test_batch_permutation_invariance(orc, bits):
+    dl = DeviceLayer(0xB17E0620, 0, 512, 64, 256, 8, 256, "bf16", bits=bits)
     xq, xd = tokens(dl, orc, 48)
     perm = np.random.default_rng(1).permutation(48)
     a = dl.layer_obj.forward(to_dev(xq, "bf16"))
@@ -101,8 +104,9 @@ def test_batch_permutation_invariance(orc):
         assert torch.equal(u[10:17], v)
 
 
-def test_api_expert_outputs_and_fused_forward(orc):
-    dl = DeviceLayer(0xB17E0630, 0, 384, 20, 192, 5, 128, "f32")
+@pytest.mark.parametrize("bits", [4, 2])
+def test_api_expert_outputs_and_fused_forward(orc, bits):
+    dl = DeviceLayer(0xB17E0630, 0, 384, 20, 192, 5, 128, "f32", bits=bits)
     xq, xd = tokens(dl, orc, 29)
     x = to_dev(xq, "f32")
     ws = dl.layer_obj.workspace(29)
@@ -118,7 +122,7 @@ def test_api_expert_outputs_and_fused_forward(orc):
         for j in range(dl.k):
             worst = max(worst, rel_err(eo[t, j], yr[j]))
         worst = max(worst, rel_err(eo[t, dl.k], ys))
-    say(f"per-slot expert outputs: max rel err {worst:.2e}")
+    say(f"{bits}-bit per-slot expert outputs: max rel err {worst:.2e}")
     assert worst <= Y_TOL
 
 

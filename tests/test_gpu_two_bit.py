@@ -3,11 +3,12 @@
 The affine group-64 format with 2-bit codes, checked against the oracle's
 expert FFN on the same records (bits=2) and the oracle's routing: ids
 bit-exact, gates within 1e-6, outputs within the usual 2e-3 relative per token.
-Calls of 4 or more tokens run the per-token kernels in passes of at most 3
-tokens, so a token's result must not depend on its batch.  The three-call API
-agrees with the fused forward bit for bit, a slot-cached 2-bit layer agrees
-with the resident one, and the Gemma-scale stack (30 layers, the shape and the
-call the benchmark times) is checked on two decode steps of every layer.
+Calls of 4 or more tokens take the grouped (MFMA) path, where a token's
+result does not depend on the rest of its batch.  The three-call API agrees
+with the fused forward bit for bit, a slot-cached 2-bit layer agrees with the
+resident one, and the Gemma-scale stack (30 layers, the shape and the call the
+benchmark times) is checked on two decode steps of every layer.  More grouped
+shapes run 2-bit records in the prefill tests.
 """
 import numpy as np
 import pytest
@@ -42,12 +43,12 @@ def check(dl, orc, toks, ids, w, y, tag):
 @pytest.mark.parametrize("H,E,I,k,Is,T,act", [
     (256, 32, 128, 8, 256, 1, "f32"),
     (256, 32, 128, 8, 256, 3, "bf16"),
-    (320, 64, 192, 6, 320, 7, "bf16"),    # three passes (3 + 3 + 1), ragged splits
+    (320, 64, 192, 6, 320, 7, "bf16"),    # grouped path, ragged splits
     (192, 7, 64, 3, 0, 2, "bf16"),        # fewer input groups than waves, no shared expert
     (64, 1, 64, 1, 64, 1, "f32"),         # minimum sizes, a single expert
     (1024, 1024, 128, 16, 0, 1, "bf16"),  # most experts, largest k
     (8192, 16, 64, 2, 128, 1, "bf16"),    # largest hidden
-    (2816, 128, 704, 8, 2112, 5, "f32"),  # Gemma-scale shapes, fp32 activations, two passes
+    (2816, 128, 704, 8, 2112, 5, "f32"),  # Gemma-scale shapes, fp32 activations, grouped
 ])
 def test_two_bit_matches_oracle(orc, H, E, I, k, Is, T, act):
     dl = DeviceLayer(0xB17E2B00 + H + E + T, 0, H, E, I, k, Is, act, bits=2)
@@ -55,10 +56,9 @@ def test_two_bit_matches_oracle(orc, H, E, I, k, Is, T, act):
     xq = np.stack([t[0] for t in toks])
     ids, w, y = dl.layer_obj.forward(to_dev(xq, act))
     check(dl, orc, toks, ids, w, y, f"2-bit H{H} E{E} I{I} k{k} Is{Is} T{T} {act}")
-    if T >= 4:  # each token alone gives exactly its result in the batch
-        for t in range(T):
-            i1, w1, y1 = dl.layer_obj.forward(to_dev(xq[t:t + 1], act))
-            assert torch.equal(i1[0], ids[t]) and torch.equal(w1[0], w[t]) and torch.equal(y1[0], y[t])
+    if T >= 5:  # a 4-token sub-batch (also grouped) gives exactly its rows of the batch
+        i4, w4, y4 = dl.layer_obj.forward(to_dev(xq[1:5], act))
+        assert torch.equal(i4, ids[1:5]) and torch.equal(w4, w[1:5]) and torch.equal(y4, y[1:5])
 
 
 def test_two_bit_sigmoid_router(orc):
@@ -72,10 +72,10 @@ def test_two_bit_sigmoid_router(orc):
 
 
 def test_two_bit_api_calls_match_fused_forward_bitwise(orc):
-    """route -> expert_ffn -> combine on 5 tokens (two passes each) gives exactly
+    """route -> expert_ffn -> combine on 3 tokens (per-token path) gives exactly
     the fused forward's result; each per-expert output matches the oracle's."""
     dl = DeviceLayer(0xB17E2B20, 0, 512, 40, 192, 6, 320, "bf16", bits=2)
-    toks = [dl.natural_token(orc, s) for s in range(5)]
+    toks = [dl.natural_token(orc, s) for s in range(3)]
     x = to_dev(np.stack([t[0] for t in toks]), "bf16")
     ws = dl.layer_obj.workspace(x.shape[0])
     ids_f, w_f, y_f = dl.layer_obj.forward(x, ws)
@@ -90,12 +90,6 @@ def test_two_bit_api_calls_match_fused_forward_bitwise(orc):
         for j in range(dl.k):
             assert rel_err(eo[t, j], yr[j]) <= Y_TOL
         assert rel_err(eo[t, dl.k], ys) <= Y_TOL
-
-
-def test_two_bit_workspace_is_bounded_by_a_pass():
-    dl = DeviceLayer(0xB17E2B30, 0, 256, 32, 128, 8, 256, "bf16", bits=2)
-    assert dl.layer_obj.workspace_bytes(3) == dl.layer_obj.workspace_bytes(4096)
-    assert dl.layer_obj.workspace_bytes(1) < dl.layer_obj.workspace_bytes(3)
 
 
 def test_two_bit_slot_cache_matches_resident(orc):

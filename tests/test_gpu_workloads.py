@@ -72,14 +72,17 @@ def test_glm_layer_zipf_full_size(orc):
     assert worst <= Y_TOL
 
 
-def test_glm_prefill_chunk_full_size(orc):
+@pytest.mark.parametrize("bits", [4, 2])
+def test_glm_prefill_chunk_full_size(orc, bits):
     """GLM-scale 128-token chunk (uniform random routing realised through the
     router) through the grouped path: every token's ids and
     gate weights against the oracle router, outputs on 4 sampled tokens (the
     oracle regenerates each selected record on the CPU, about a second each),
-    and the whole chunk's result permuted exactly with its tokens."""
+    and the whole chunk's result permuted exactly with its tokens.  4-bit and
+    2-bit records."""
     wl = synth.WORKLOADS["glm_prefill_h6144_e256_t128"]
-    dl = DeviceLayer(wl.seed, 0, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
+    dl = DeviceLayer(wl.seed, 0, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act,
+                     bits=bits)
     Wd = dl.rq.astype(np.float64) * dl.rs.view(np.float16).astype(np.float64)[:, None]
     zr = synth.ZipfRealiser(Wd, wl.zipf_s, wl.seed, 0)  # s = 0: uniform Gumbel-top-8 targets
     toks = []
@@ -108,7 +111,7 @@ def test_glm_prefill_chunk_full_size(orc):
         _, _, ry, _, _ = dl.oracle(orc, toks[t][1])
         worst_y = max(worst_y, rel_err(y_h[t], ry))
         print(f"glm prefill token {t}: rel y err {rel_err(y_h[t], ry):.2e}", flush=True)
-    print(f"glm prefill chunk: {wl.n_tokens} tokens, max |w err| {worst_w:.2e}, "
+    print(f"{bits}-bit glm prefill chunk: {wl.n_tokens} tokens, max |w err| {worst_w:.2e}, "
           f"max rel y err (sampled) {worst_y:.2e}")
     assert worst_y <= Y_TOL
     perm = np.random.default_rng(2).permutation(wl.n_tokens)
