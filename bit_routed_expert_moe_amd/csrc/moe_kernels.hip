@@ -300,17 +300,20 @@ __global__ __launch_bounds__(kBlock) void k_prep(RouteArgs a) {
 // k_gate_up: grid (k*blk_r + blk_s, T).  Lane = row of the 64-row GU tile
 // (rows 0..31 gate, 32..63 up); waves split the H/64 input groups.
 // ---------------------------------------------------------------------------
-constexpr int kXPrepVecsPerThread = kMaxHidden / 8 * 2 / kBlock;  // 16-byte vectors
-
-template <int XP, int MAXG, int Q, int BITS>
-__global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
+template <int XP, int MAXG, int Q, int BITS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
+    constexpr int kGuBlock = 64 * WAVES;
+    // 16-byte vectors of prepared activations per thread, at the largest hidden
+    // size the wave count is used for
+    constexpr int kXPrepVecsPerThread =
+        (WAVES == kGuWavesSmallH ? kGuSmallHMax : kMaxHidden) / 8 * 2 / kGuBlock;
     extern __shared__ uint32_t smem[];
     const int H = a.H, NG = H / 64;
     uint32_t* xp = smem;                                 // [H/2*XP]
     float* sK = (float*)(xp + (H / 2) * XP);             // [NG]
     float* sX = sK + NG;                                 // [NG]
     float* sI = sX + NG;                                 // [NG]
-    float* red = sI + NG;                                // [4][64]
+    float* red = sI + NG;                                // [WAVES][64]
     __shared__ TopkScratch s_topk;
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     u32x4 xv[kXPrepVecsPerThread];
 #pragma unroll
     for (int i = 0; i < kXPrepVecsPerThread; ++i)
-        xv[i] = gx[min((int)threadIdx.x + kBlock * i, nvec - 1)];
+        xv[i] = gx[min((int)threadIdx.x + kGuBlock * i, nvec - 1)];
     const int gq = min((int)threadIdx.x, NG - 1);
     const float kx = a.xK[(size_t)t * NG + gq];
     const float xx = a.xX[(size_t)t * NG + gq];
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     // 4. activations to LDS (waits only for the loads issued before the weights)
 #pragma unroll
     for (int i = 0; i < kXPrepVecsPerThread; ++i) {
-        const int v = threadIdx.x + kBlock * i;
+        const int v = threadIdx.x + kGuBlock * i;
         if (v < nvec) ((u32x4*)xp)[v] = xv[i];
     }
     if ((int)threadIdx.x < NG) {
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(FfnArgs a) {
     if (lane < 32) {
         float g = 0.0f, uu = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < WAVES; ++w) {
             g += red[w * 64 + lane];
             uu += red[w * 64 + 32 + lane];
         }
@@ -699,15 +702,16 @@ template <int XP, int Q, int BITS>
 static hipError_t launch_gu_xq(const FfnArgs& a, int T, int n_units, hipStream_t s) {
     const dim3 grid(n_units, T);
     const int NG = a.H / 64;
-    const size_t sh = ((size_t)(a.H / 2) * XP + 3 * NG + kWaves * 64) * 4;
-    const int m = a.gpw_gu;
-#define MOE_GU(MG) launch_kernel(k_gate_up<XP, MG, Q, BITS>, grid, dim3(kBlock), sh, s, a)
-    if (m <= 4) MOE_GU(4);
-    else if (m <= 8) MOE_GU(8);
-    else if (m <= 12) MOE_GU(12);
-    else if (m <= 16) MOE_GU(16);
-    else if (m <= 24) MOE_GU(24);
-    else MOE_GU(32);
+    const size_t sh = ((size_t)(a.H / 2) * XP + 3 * NG + a.gu_waves * 64) * 4;
+    const int m = a.gpw_gu;  // groups per wave: <= 8 with 8 waves, 17..32 with 4 (H > 4096)
+#define MOE_GU(MG, W) launch_kernel(k_gate_up<XP, MG, Q, BITS, W>, grid, dim3(64 * W), sh, s, a)
+    if (a.gu_waves == kGuWavesSmallH) {
+        if (m <= 4) MOE_GU(4, kGuWavesSmallH);
+        else MOE_GU(8, kGuWavesSmallH);
+    } else {
+        if (m <= 24) MOE_GU(24, kGuWavesLargeH);
+        else MOE_GU(32, kGuWavesLargeH);
+    }
 #undef MOE_GU
     return hipGetLastError();
 }

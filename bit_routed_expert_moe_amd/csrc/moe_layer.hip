@@ -74,6 +74,7 @@ struct moe_layer {
     int n_items;   // down items per output tile
     int n_otiles;  // H / 64
     int gpw_gu, gpw_dn;
+    int gu_waves;  // waves per gate/up workgroup
 };
 
 namespace moe {
@@ -277,6 +278,7 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.blk_s = L->blk_s;
     a.blk_max = L->blk_max;
     a.gpw_gu = L->gpw_gu;
+    a.gu_waves = L->gu_waves;
     a.n_otiles = L->n_otiles;
     a.n_items = L->n_items;
     a.gi = L->gi;
@@ -625,7 +627,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     L->n_items = d.top_k + (sg + L->gis - 1) / L->gis;
     L->gpw_dn = (std::max(L->gi, L->gis) + kWaves - 1) / kWaves;
     L->n_otiles = d.hidden / 64;
-    L->gpw_gu = (L->NG + kWaves - 1) / kWaves;
+    L->gu_waves = d.hidden <= kGuSmallHMax ? kGuWavesSmallH : kGuWavesLargeH;
+    L->gpw_gu = (L->NG + L->gu_waves - 1) / L->gu_waves;
     if (L->gpw_gu > kMaxGateUpGroupsPerWave || std::max(L->gi, L->gis) > kMaxDownGroups) {
         delete L;
         return fail(MOE_ERR_SHAPE, "shape exceeds the kernels' per-wave register tiles");
