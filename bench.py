@@ -53,9 +53,9 @@ TRAFFIC = {
     ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24996266, "moe_kernels.hip", "faf7581f556c823f"),
     # 2-bit records: FETCH_SIZE 6786.01 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
     ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13936528, "moe_kernels.hip", "faf7581f556c823f"),
-    # FETCH_SIZE 1833777.19 KiB x 2.0 + WRITE_SIZE 5753.18 KiB x 1.0 per launch (mean over
+    # FETCH_SIZE 1833761.89 KiB x 2.0 + WRITE_SIZE 5753.64 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761466944, "moe_prefill.hip", "36b4fd2cbeb8f594"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761436081, "moe_prefill.hip", "d867d4412df61e4d"),
 }
 
 
