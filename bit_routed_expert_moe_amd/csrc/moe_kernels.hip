@@ -79,8 +79,8 @@ __device__ void prep_group(const void* x, int t, int H, int g, uint32_t* pairs, 
 // all threads must call it (it synchronises the workgroup).
 //   1. order-preserving 32-bit keys u (larger logit -> larger u);
 //   2. radix select, most significant bit first: T = the largest value with
-//      #{u >= T} >= k (32 steps of one compare per key slot, a ballot and a
-//      scalar popcount);
+//      #{u >= T} >= k (up to 32 steps of one compare per key slot, a ballot
+//      and a scalar popcount; it stops as soon as exactly k keys are >= T);
 //   3. the selection = every key above T plus the lowest ids among the keys
 //      equal to T, as many as are needed;
 //   4. its order: each selected key counts the selected keys ahead of it
@@ -133,13 +133,18 @@ __device__ __forceinline__ int topk_select(const float* lg, int E, int k, int wa
 #pragma unroll
     for (int q = 0; q < Q; ++q)
         if (lane + 64 * q >= E) u[q] = 0u;  // 0: below every key
+    // once exactly k keys are >= T the selection is fixed: the keys equal to T
+    // (if any) are then all taken below, so the search may stop there
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
         int c = 0;
 #pragma unroll
         for (int q = 0; q < Q; ++q) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(u[q] >= cand));
-        if (c >= k) T = cand;
+        if (c >= k) {
+            T = cand;
+            if (c == k) break;
+        }
     }
     int gt = 0;
 #pragma unroll
