@@ -28,6 +28,7 @@ constexpr int kCounterStride = 64;  // arrival counters 256 bytes apart (own cac
 // and 12 at hidden 2816 and 6144, for 4-bit and 2-bit records).
 constexpr int kDepth = 3;
 constexpr int kMaxSharedItems = 8;  // down work items of the shared expert
+constexpr int kDnRing = 2;          // k_down: groups in flight per wave (A/B: 2 beats 4 and all-at-once)
 constexpr int kMaxItems = kMaxTopK + kMaxSharedItems;
 
 // Prepared activations of one vector of length n (n multiple of 64):

@@ -545,10 +545,13 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     const float hi = a.hinv[slot0 + bq];
     __builtin_amdgcn_sched_barrier(0);
 
-    RowT W[2 * MAXG];
-    uint32_t SB[MAXG];
+    // a ring of DD groups in flight per wave (every group at once when a wave
+    // has at most kDnRing groups)
+    constexpr int DD = MAXG > kDnRing ? kDnRing : MAXG;
+    RowT W[2 * DD];
+    uint32_t SB[DD];
 #pragma unroll
-    for (int q = 0; q < MAXG; ++q) {
+    for (int q = 0; q < DD; ++q) {
         const int g = min(g0 + q, gb - 1);  // past this wave's range: re-read a valid group
         W[2 * q] = ldg_nt((const RowT*)(dblk + blk * (2 * g)));
         W[2 * q + 1] = ldg_nt((const RowT*)(dblk + blk * (2 * g + 1)));
@@ -571,12 +574,13 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
 #pragma unroll
     for (int q = 0; q < MAXG; ++q) {
         const int g = g0 + q;
+        const int slot = q % DD;
         if (g < g1) {
             float part = 0.0f;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int lb = 2 * (g - ga) + half;  // local h block
-                const RowT wv = W[2 * q + half];
+                const RowT wv = W[2 * slot + half];
                 const uint32_t* hc = sp + (size_t)lb * 16 * kHParts;
                 float a0 = 0.0f, a1 = 0.0f;
                 if constexpr (BITS == 4) {
@@ -597,9 +601,16 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
                 part = fmaf((a0 + a1) - sK[lb], sI[lb], part);
             }
             const int lb0 = 2 * (g - ga);
-            row = fmaf(f16lo(SB[q]), part, row);
-            row = fmaf(f16hi(SB[q]), sH[lb0] + sH[lb0 + 1], row);
+            row = fmaf(f16lo(SB[slot]), part, row);
+            row = fmaf(f16hi(SB[slot]), sH[lb0] + sH[lb0 + 1], row);
         }
+        if (q + DD < MAXG) {  // refill the slot just consumed
+            const int gn = min(g0 + q + DD, gb - 1);
+            W[2 * slot] = ldg_nt((const RowT*)(dblk + blk * (2 * gn)));
+            W[2 * slot + 1] = ldg_nt((const RowT*)(dblk + blk * (2 * gn + 1)));
+            SB[slot] = ldg_nt((const uint32_t*)(dsb + (size_t)12 * H * gn));
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     red[wave * 64 + lane] = row;
     __syncthreads();
