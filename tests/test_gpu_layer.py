@@ -3,6 +3,9 @@
 Bar: expert ids bit-exact (tokens are drawn so the oracle's top-(k+1) logits
 are separated by more than 1e-4), gate weights within 1e-6, outputs within a
 max relative error of 2e-3 per token (max |y - y_ref| / max |y_ref|).
+Special cases with closed forms: one dominant expert (a dense SwiGLU),
+constant weights, zero scales (bias terms only), integer activations (exact
+logits, ties included).
 """
 import sys
 
@@ -153,6 +156,53 @@ def test_constant_weights_closed_form():
     yref = (s2 * c2 + b2) * I * gamma / (1 + np.exp(-gamma)) * gamma
     _, _, y = lay.forward(torch.from_numpy(x[None]).cuda())
     assert rel_err(y.cpu().numpy()[0], np.full(H, yref)) <= Y_TOL
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_zero_scales_leave_the_bias_terms(bits):
+    """Every scale 0: W = bias per group, whatever the codes, so the output is
+    the dense SwiGLU of the bias-only matrices (the code products must vanish
+    and the bias * sum(x) terms carry everything)."""
+    from bit_routed_expert_moe_amd import Layer
+    rng = np.random.default_rng(8)
+    H, I = 320, 192
+    z = lambda shape: np.zeros(shape, dtype=np.uint16)  # fp16 +0
+    f16 = lambda shape: rng.uniform(-8e-3, 8e-3, shape).astype(np.float16).view(np.uint16)
+    ex = DenseExpert(H, I, rng, sb=(z((I, H // 64)), f16((I, H // 64)), z((I, H // 64)),
+                                    f16((I, H // 64)), z((H, I // 64)), f16((H, I // 64))), bits=bits)
+    assert not np.any(ex.G - np.repeat(ex.G[:, ::64], 64, axis=1))  # bias-only, constant per group
+    lay = Layer(H, 1, I, 1, 0, torch.zeros(1, H, dtype=torch.int8).cuda(),
+                torch.ones(1, dtype=torch.float16).cuda(), torch.from_numpy(ex.rec).cuda(), None,
+                act="f32", bits=bits)
+    for _ in range(3):
+        x = rng.standard_normal(H).astype(np.float32)
+        _, _, y = lay.forward(torch.from_numpy(x[None]).cuda())
+        assert rel_err(y.cpu().numpy()[0], ex.ffn(x.astype(np.float64))) <= Y_TOL
+
+
+def test_integer_activations_give_exact_logits():
+    """Integer activations make every router logit an exact integer times the
+    row scale (all products and partial sums are exact in fp32), ties included:
+    ids must follow (logit descending, lower id first) exactly and the gates
+    are the softmax of those exact logits."""
+    from bit_routed_expert_moe_amd import Layer
+    rng = np.random.default_rng(9)
+    H, E, I, k = 256, 48, 64, 8
+    rq = rng.integers(-3, 4, (E, H)).astype(np.int8)
+    rq[7] = rq[3]  # an exact tie between experts 3 and 7
+    rs = np.full(E, 1.0 / 256, dtype=np.float16)
+    pool = torch.zeros(E * DenseExpert(H, I, rng).rec.size, dtype=torch.uint8).cuda()
+    lay = Layer(H, E, I, k, 0, torch.from_numpy(rq).cuda(), torch.from_numpy(rs).cuda(), pool, None,
+                act="f32")
+    for trial in range(4):
+        x = rng.integers(-4, 5, H).astype(np.float32)
+        ids, w = lay.route(torch.from_numpy(x[None]).cuda())
+        exact = (rq.astype(np.int64) @ x.astype(np.int64)).astype(np.float64) / 256.0
+        order = sorted(range(E), key=lambda e: (-exact[e], e))[:k]
+        assert ids.cpu().numpy()[0].tolist() == order, trial
+        sel = exact[order]
+        wref = np.exp(sel - sel.max()) / np.exp(sel - sel.max()).sum()
+        assert np.max(np.abs(w.cpu().numpy()[0] - wref)) <= W_TOL
 
 
 def test_rerun_is_bitwise_identical(orc):
