@@ -27,6 +27,9 @@ constexpr int kCounterStride = 64;  // arrival counters 256 bytes apart (own cac
 // wave's first groups behind the others' later ones (measured: 3 beats 4, 6, 8
 // and 12 at hidden 2816 and 6144, for 4-bit and 2-bit records).
 constexpr int kDepth = 3;
+constexpr int kDepthLargeH = 2;  // the same for 4-bit records with 4-wave workgroups (hidden
+                                 // above 4096): 2.5 % per layer at hidden 6144 (2-bit groups,
+                                 // half the bytes, keep 3)
 constexpr int kMaxSharedItems = 8;  // down work items of the shared expert
 constexpr int kDnRing = 2;          // k_down: groups in flight per wave (A/B: 2 beats 4 and all-at-once)
 constexpr int kMaxItems = kMaxTopK + kMaxSharedItems;

@@ -376,7 +376,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     // 3. weight stream: a ring of kDepth groups in flight per wave.  Loads are
     // unconditional (clamped to a valid group) and kept in program order, so
     // each group's compute waits only for that group's loads.
-    constexpr int D = kDepth < MAXG ? kDepth : MAXG;
+    constexpr int DK = WAVES == kGuWavesLargeH && BITS == 4 ? kDepthLargeH : kDepth;
+    constexpr int D = DK < MAXG ? DK : MAXG;
     u32x4 W[D][NW];
     uint32_t SB[D];
 #pragma unroll
