@@ -49,13 +49,13 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12185.89 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24995496, "moe_kernels.hip", "5cee7758ef390c16"),
-    # 2-bit records: FETCH_SIZE 6788.62 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13941877, "moe_kernels.hip", "5cee7758ef390c16"),
-    # FETCH_SIZE 1833659.12 KiB x 2.0 + WRITE_SIZE 5752.21 KiB x 1.0 per launch (mean over
+    # FETCH_SIZE 12181.62 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24986743, "moe_kernels.hip", "2b68481564f4b4f2"),
+    # 2-bit records: FETCH_SIZE 6785.41 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13935311, "moe_kernels.hip", "2b68481564f4b4f2"),
+    # FETCH_SIZE 1833775.34 KiB x 2.0 + WRITE_SIZE 5752.50 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761224137, "moe_prefill.hip", "f0db80b0f9d539d2"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761462458, "moe_prefill.hip", "eceadcbea60444a9"),
 }
 
 
