@@ -14,7 +14,16 @@ constexpr int kWaves = kBlock / 64;
 // most 8 groups of 64 inputs per wave), else 4 (measured: 8 waves save 1.5-4 %
 // per layer at hidden 2816, 4 waves are 1 % faster at hidden 6144).
 constexpr int kGuWavesSmallH = 8, kGuWavesLargeH = 4, kGuSmallHMax = 4096;
-constexpr int kRouterRowsPerWave = 2;
+// Polls of the router's logit words that a fused gate/up workgroup makes
+// before it computes the logits itself (each poll waits for its load, well
+// under a microsecond): a bound on the wait, never reached when the router
+// units run beside the gate/up units.
+constexpr int kRouteSpinLimit = 1 << 14;
+// Largest hidden size routed inside the gate/up launch: there every gate/up
+// workgroup prepares its own activations, a few groups per wave (measured:
+// 2 % less per decode step at hidden 2816; at hidden 6144 the separate router
+// launch is 16 % faster).
+constexpr int kFusedMaxHidden = kGuSmallHMax;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxHidden = 8192;
@@ -44,7 +53,6 @@ struct RouteArgs {
     const int8_t* rq;        // [E][H]
     const uint16_t* rs;      // [E] fp16
     float* logits;           // [T][E]
-    uint32_t* ctr;           // [T] arrival counters (zero between calls)
     int32_t* ids;            // [T][k]
     float* w;                // [T][k]
     uint32_t* xpairs;        // [T][H/2*XP] (written only if prep != 0)
@@ -68,6 +76,17 @@ struct FfnArgs {
     const int32_t* ids;      // [T][k] selection (read by k_down; by k_gate_up unless logits)
     const float* w;          // [T][k] gate weights (fused combine only)
     const float* logits;     // [T][E]: if set, k_gate_up selects the experts itself
+    // fused routing (route_units > 0, hidden <= kFusedMaxHidden): the first
+    // route_units workgroups of each token row compute the router logits, one
+    // row per wave, into flog; the gate/up units prepare x themselves and
+    // select from flog
+    int route_units;
+    const void* x;           // [T][H] activations
+    const int8_t* rq;        // [E][H] router rows
+    const uint16_t* rs;      // [E] fp16 row scales
+    uint32_t* flog;          // [T][E] logits stored bit-inverted, 0 = not yet written;
+                             // k_down returns the words to 0 when set
+    int spin_limit;          // polls before computing the logits locally (< 0: none)
     const float* bias;       // [E] selection bias (sigmoid gate) or nullptr
     float rscale;            // sigmoid gate: routed scaling factor
     int gate;                // 0 softmax, 1 sigmoid

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -75,6 +76,7 @@ struct moe_layer {
     int n_otiles;  // H / 64
     int gpw_gu, gpw_dn;
     int gu_waves;  // waves per gate/up workgroup
+    int spin_limit; // fused routing: polls of the logit words before computing them locally
 };
 
 namespace moe {
@@ -124,7 +126,7 @@ moe_status hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t err, rctr, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
+    size_t err, flog, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
         x16, x16b, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, total;
     int tile_cap;
 };
@@ -152,7 +154,7 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     // counters first, at offsets that do not depend on T: every call leaves
     // them at zero, so a workspace zero-filled once serves calls of any size
     o.err = take(4);
-    o.rctr = take((size_t)kCounterStride * 4);
+    o.flog = take((size_t)(kPrefillMinTokens - 1) * L->d.n_experts * 4);  // fused routing's logit words
     o.dctr = take((size_t)(kPrefillMinTokens - 1) * L->n_otiles * kCounterStride * 4);
     o.pred_ids = take((size_t)L->d.top_k * 4);  // moe_cache_prefetch's selection
     o.pred_w = take((size_t)L->d.top_k * 4);
@@ -213,7 +215,6 @@ RouteArgs route_args(const moe_layer* L, const void* x, int32_t* ids, float* w, 
     a.rq = L->w.router_q;
     a.rs = L->w.router_scale;
     a.logits = (float*)(ws + o.logits);
-    a.ctr = (uint32_t*)(ws + o.rctr);
     a.ids = ids;
     a.w = w;
     a.xpairs = (uint32_t*)(ws + o.xpairs);
@@ -628,6 +629,12 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     L->gpw_dn = (std::max(L->gi, L->gis) + kWaves - 1) / kWaves;
     L->n_otiles = d.hidden / 64;
     L->gu_waves = d.hidden <= kGuSmallHMax ? kGuWavesSmallH : kGuWavesLargeH;
+    L->spin_limit = kRouteSpinLimit;
+    if (const char* sl = std::getenv("MOE_ROUTE_SPIN_LIMIT")) {  // test hook: -1 computes the logits locally
+        char* end = nullptr;
+        const long v = std::strtol(sl, &end, 10);
+        if (end != sl && *end == '\0' && v >= -1 && v <= kRouteSpinLimit) L->spin_limit = (int)v;
+    }
     L->gpw_gu = (L->NG + L->gu_waves - 1) / L->gu_waves;
     if (L->gpw_gu > kMaxGateUpGroupsPerWave || std::max(L->gi, L->gis) > kMaxDownGroups) {
         delete L;
@@ -737,15 +744,26 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
     uint8_t* ws = (uint8_t*)workspace;
     hipStream_t s = (hipStream_t)stream;
     if (T >= kPrefillMinTokens) return grouped_ffn(L, x, T, ids, w, y, nullptr, ws, o, s, true, true);
-    RouteArgs ra = route_args(L, x, ids, w, ws, o, 1, T);
-    hipError_t e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); });
-    if (e != hipSuccess) return hip_fail(e, "router launch");
-    if (L->cache.n_slots) {
-        if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
-            return hip_fail(e, "top-k launch");
-        return cached_ffn(L, ids, ffn_args(L, ids, w, ws, o, y, nullptr, false), o, ws, s);
-    }
+    hipError_t e;
     FfnArgs fa = ffn_args(L, ids, w, ws, o, y, nullptr, true);
+    if (L->cache.n_slots || L->d.hidden > kFusedMaxHidden) {
+        RouteArgs ra = route_args(L, x, ids, w, ws, o, 1, T);
+        if ((e = timed(K_ROUTE, s, [&] { return launch_route(ra, T, L->d.act_dtype == MOE_BF16, s); })) != hipSuccess)
+            return hip_fail(e, "router launch");
+        if (L->cache.n_slots) {
+            if ((e = timed(K_TOPK, s, [&] { return launch_topk(ra, T, s); })) != hipSuccess)
+                return hip_fail(e, "top-k launch");
+            return cached_ffn(L, ids, ffn_args(L, ids, w, ws, o, y, nullptr, false), o, ws, s);
+        }
+    } else {  // resident, hidden <= kFusedMaxHidden: routing inside the gate/up launch
+        fa.logits = nullptr;
+        fa.route_units = (L->d.n_experts + L->gu_waves - 1) / L->gu_waves;
+        fa.x = x;
+        fa.rq = L->w.router_q;
+        fa.rs = L->w.router_scale;
+        fa.flog = (uint32_t*)(ws + o.flog);
+        fa.spin_limit = L->spin_limit;
+    }
     if ((e = decode_units(L, fa, T, 0, fa.n_units, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
     if ((e = decode_finish(fa, T, s)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;

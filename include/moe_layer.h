@@ -152,9 +152,11 @@ moe_status moe_layer_destroy(moe_layer_t layer);
 
 /* Device workspace bytes needed by the compute calls for n_tokens tokens.
  * The workspace must be zero-filled before its first use; its arrival
- * counters sit at fixed offsets at its start and every call returns them to
- * zero, so it can be reused without clearing, for any n_tokens it is large
- * enough for.  Two calls that overlap in time must not share a workspace. */
+ * counters and the fused router's logit words sit at fixed offsets at its
+ * start and every call returns them to zero, so it can be reused without
+ * clearing, for any n_tokens it is large enough for (after a call that
+ * returned MOE_ERR_HIP, zero-fill it again).  Two calls that overlap in time
+ * must not share a workspace. */
 size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens);
 
 /* Router + exact top-k + gates for n_tokens tokens.
@@ -195,7 +197,13 @@ moe_status moe_combine(moe_layer_t layer, const float* expert_out, const float* 
 
 /* The whole layer in one call: route, experts, combine, with the per-expert
  * outputs reduced inside the FFN kernels (no expert_out round trip).
- * ids, w as moe_route_topk; y device [T][H] fp32.  Errors: ARG, ALIGN, HIP. */
+ * ids, w as moe_route_topk; y device [T][H] fp32.  Errors: ARG, ALIGN, HIP.
+ * Up to hidden 4096 a resident layer routes inside its gate/up launch: leading
+ * workgroups compute the logits while the gate/up workgroups prepare the
+ * activations, then read the logits as they land.  A gate/up workgroup that
+ * has polled for them MOE_ROUTE_SPIN_LIMIT times (environment variable read
+ * by moe_layer_create, default 16384, -1 = at once) computes them itself,
+ * with the same arithmetic: results never depend on it. */
 moe_status moe_layer_forward(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
                              float* w, float* y, void* workspace, void* stream);
 
