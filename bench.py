@@ -49,13 +49,14 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12181.62 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (24986743, "moe_kernels.hip", "2b68481564f4b4f2"),
-    # 2-bit records: FETCH_SIZE 6785.41 KiB x 2.0 + WRITE_SIZE 37.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (13935311, "moe_kernels.hip", "2b68481564f4b4f2"),
-    # FETCH_SIZE 1833775.34 KiB x 2.0 + WRITE_SIZE 5752.50 KiB x 1.0 per launch (mean over
+    # FETCH_SIZE 12463.48 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
+    # also runs the router)
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25568087, "moe_kernels.hip", "a77a2646aa726983"),
+    # 2-bit records: FETCH_SIZE 7057.03 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (14495676, "moe_kernels.hip", "a77a2646aa726983"),
+    # FETCH_SIZE 1833801.68 KiB x 2.0 + WRITE_SIZE 5753.57 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761462458, "moe_prefill.hip", "eceadcbea60444a9"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761517496, "moe_prefill.hip", "44cc6cfd0e4a0fe1"),
 }
 
 
