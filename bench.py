@@ -94,6 +94,19 @@ def down_bytes(H, I, bits=4):
     return H * I * bits // 8 + H * I // 16
 
 
+def launch_bytes(wl, bits, T, fused_route):
+    """Algorithmic bytes per launch of the per-token path's kernels for T
+    tokens: the router (int8 rows + fp16 scales), the gate/up halves and the
+    down halves of the k routed records plus the shared one.  With
+    fused_route the router runs inside the gate/up launch, which then reads
+    both."""
+    H, E, I, k, Is = wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter
+    rt = T * (E * H + 2 * E)
+    gu = T * (k * gu_bytes(H, I, bits) + (gu_bytes(H, Is, bits) if Is else 0))
+    dn = T * (k * down_bytes(H, I, bits) + (down_bytes(H, Is, bits) if Is else 0))
+    return {"route": rt, "gate_up": gu + (rt if fused_route else 0), "down_combine": dn}
+
+
 def token_layer_bytes(wl, bits):
     """Algorithmic HBM bytes of one decode token through one layer: the router,
     the top_k selected records and the shared record."""
@@ -720,13 +733,10 @@ def main():
             run_step(s)
 
     recs = kernel_timed_pass(profiled_steps, P * L * 4 + 64)
-    kb_gu = T * (k * gu_bytes(H, I, bits) + (gu_bytes(H, Is, bits) if Is else 0))
-    kb_dn = T * (k * down_bytes(H, I, bits) + (down_bytes(H, Is, bits) if Is else 0))
-    kb_rt = T * (E * H + 2 * E)  # int8 router rows + fp16 scales
     # up to hidden 4096 the resident forward routes inside the gate/up launch
     # (no route launch): that launch then also reads the router
     fused_route = "route" not in {r[0] for r in recs}
-    kbytes = {"route": kb_rt, "gate_up": kb_gu + (kb_rt if fused_route else 0), "down_combine": kb_dn}
+    kbytes = launch_bytes(wl, bits, T, fused_route)
     kernels = {}
     for name in sorted({r[0] for r in recs}):
         ms = np.array([m for n_, m in recs if n_ == name])

@@ -49,3 +49,19 @@ def test_lookahead_recall_grows_with_rho_and_calibration_hits_the_target():
     assert rec[0] < rec[1] < rec[2] < rec[3]
     rho = bench.calibrate_rho(wl, routers, xs, 0.716, steps)
     assert abs(bench.lookahead_recall(wl, routers, xs, rho, steps) - 0.716) < 0.03
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_launch_bytes_cover_the_token_layer(bits):
+    """The three launches' bytes add up to the token-layer total, and with the
+    router inside the gate/up launch that launch carries the router's bytes
+    (the Gemma-scale figure the roofline quotes: 24,893,696 B with 4-bit
+    records)."""
+    wl = synth.WORKLOADS["gemma_a4b_h2816_e128_l30"]
+    sep = bench.launch_bytes(wl, bits, 1, False)
+    fused = bench.launch_bytes(wl, bits, 1, True)
+    assert sum(sep.values()) == bench.token_layer_bytes(wl, bits)
+    assert fused["gate_up"] == sep["gate_up"] + sep["route"] and fused["down_combine"] == sep["down_combine"]
+    assert bench.launch_bytes(wl, bits, 3, True)["gate_up"] == 3 * fused["gate_up"]
+    if bits == 4:
+        assert fused["gate_up"] == 24_893_696 and sep["route"] == 360_704
