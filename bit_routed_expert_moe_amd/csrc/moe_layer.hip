@@ -151,11 +151,13 @@ WsLayout ws_layout(const moe_layer* L, int T) {
         off = align256(off + bytes);
         return at;
     };
-    // counters first, at offsets that do not depend on T: every call leaves
-    // them at zero, so a workspace zero-filled once serves calls of any size
+    // counters first, at offsets and extents that depend neither on T nor on
+    // the layer's shape: every call leaves them at zero, so a workspace
+    // zero-filled once serves calls of any size, of any layer it is large
+    // enough for
     o.err = take(4);
-    o.flog = take((size_t)(kPrefillMinTokens - 1) * L->d.n_experts * 4);  // fused routing's logit words
-    o.dctr = take((size_t)(kPrefillMinTokens - 1) * L->n_otiles * kCounterStride * 4);
+    o.flog = take((size_t)(kPrefillMinTokens - 1) * kMaxExperts * 4);  // fused routing's logit words
+    o.dctr = take((size_t)(kPrefillMinTokens - 1) * (kMaxHidden / 64) * kCounterStride * 4);
     o.pred_ids = take((size_t)L->d.top_k * 4);  // moe_cache_prefetch's selection
     o.pred_w = take((size_t)L->d.top_k * 4);
     o.logits = take((size_t)T * L->d.n_experts * 4);

@@ -8,7 +8,8 @@ MOE_ROUTE_SPIN_LIMIT=-1 always computes them locally and one created with 0
 polls once: both must give the default layer's ids, gates and outputs bit for
 bit, and the oracle's selection.  The logit words go back to zero after every
 call (a later call would otherwise select from stale logits): a sequence of
-different tokens on one workspace gives what fresh workspaces give.
+different tokens on one workspace gives what fresh workspaces give, also
+when layers of different shapes take turns on it.
 """
 import numpy as np
 import pytest
@@ -87,3 +88,26 @@ def test_logit_words_return_to_zero_between_calls(orc):
             assert torch.equal(a_, b_), f"step {step}: reused workspace differs"
         for t, (_, xd) in enumerate(toks):
             assert shared_ws[0].cpu().numpy()[t].tolist() == dl.oracle(orc, xd)[0].tolist()
+
+
+def test_layers_of_different_shapes_share_one_workspace(orc):
+    """Layers of three shapes take turns on one workspace sized for the largest;
+    each call equals the same call on a fresh zero-filled workspace (the
+    arrival counters and logit words sit at the same offsets, with the same
+    extents, for every shape)."""
+    shapes = [(512, 48, 192, 8, 256, "bf16"), (4096, 200, 128, 6, 128, "f32"), (256, 16, 64, 4, 0, "bf16"),
+              (6144, 64, 128, 8, 128, "bf16")]
+    dls = [DeviceLayer(0xF05E0200 + i, 0, H, E, I, k, Is, act) for i, (H, E, I, k, Is, act) in enumerate(shapes)]
+    nbytes = max(dl.layer_obj.workspace_bytes(3) for dl in dls)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for step in range(12):
+        dl = dls[step % len(dls)]
+        T = 1 + step % 3
+        toks = [dl.natural_token(orc, 3 * step + t) for t in range(T)]
+        x = to_dev(np.stack([t[0] for t in toks]), dl.act)
+        got = dl.layer_obj.forward(x, ws)
+        fresh = dl.layer_obj.forward(x, dl.layer_obj.workspace(T))
+        for a_, b_ in zip(got, fresh):
+            assert torch.equal(a_, b_), f"step {step} (H {dl.H}, E {dl.E}, T {T}): shared workspace differs"
+        for t, (_, xd) in enumerate(toks):
+            assert got[0].cpu().numpy()[t].tolist() == dl.oracle(orc, xd)[0].tolist()
