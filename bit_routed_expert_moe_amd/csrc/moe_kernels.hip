@@ -2,8 +2,8 @@
 //
 //   k_route       router GEMV (int8 rows x activations), one row per wave,
 //                 every load issued before any use; extra workgroups beside
-//                 the router prepare the activations for the FFN kernels (one
-//                 wave per 64-input group).  The API route and the slot-cache
+//                 the router prepare the activations for the FFN kernels (four
+//                 64-input groups per wave).  The API route and the slot-cache
 //                 path use it; the resident forward routes inside k_gate_up.
 //   k_topk        exact top-k and gate weights from the logits (API route and
 //                 the grouped path).
@@ -38,55 +38,107 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// activation preparation of one 64-input group by one wave (lane = input).
-// Each group gets its own power-of-two scale 2^e so that its largest value
-// lands below 2^14 in fp16.  4-bit weights: odd positions of each 8-set are
-// also divided by 16 to pair with the x16 nibble slots, pairs (a_p, a_{p+4})
-// per 8-set; 2-bit weights: pairs (a_j, a_{j+8}) per 16-set, unscaled.
-// Writes the group's 16*XP pair dwords, K = 1024 * sum of the fp16 values (in
-// double), X = sum of the inputs and inv = 2^-e.
+// activation preparation, four 64-input groups g0..g0+3 per wave: the 16
+// lanes of row r (lanes 16r..16r+15) take group g0 + r, lane m of the row its
+// inputs 4m..4m+3.  Each group gets its own power-of-two scale 2^e so that its
+// largest value lands below 2^14 in fp16.  4-bit weights: odd positions of
+// each 8-set are also divided by 16 to pair with the x16 nibble slots, pairs
+// (a_p, a_{p+4}) per 8-set; 2-bit weights: pairs (a_j, a_{j+8}) per 16-set
+// with pair j's in-place factor.  Writes each group's 32*XP pair dwords,
+// K = 1024 * sum of the fp16 values (in double), X = sum of the inputs and
+// inv = 2^-e, for groups below NG.  Sums run in a fixed order (a lane's four
+// inputs in order, then the row's DPP tree; lane 0 of the row writes).
+// xrow, pairs, K, X, inv are the token's own.
 // ---------------------------------------------------------------------------
-
+__device__ __forceinline__ float row_max(float v) {  // max over the lane's row of 16
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x124>(v));
+    return fmaxf(v, dpp<0x128>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x124>(v);
+    return v + dpp<0x128>(v);
+}
+__device__ __forceinline__ double row_sum_d(double v) {
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x124>(v);
+    return v + dpp_f64<0x128>(v);
+}
+// the lane's four inputs of group g: x[64 g + 4 m ...] (one 8- or 16-byte load);
+// element by element through scalars (a bit-cast of a vector element reads
+// element 0 with this compiler)
 template <bool BF16>
-__device__ __forceinline__ float load_act(const void* x, size_t i) {
-    return BF16 ? bf16_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
+__device__ __forceinline__ void load_act4(const void* xrow, int g, float (&v)[4]) {
+    const int i0 = 64 * g + 4 * (threadIdx.x & 15);
+    if (BF16) {
+        const u32x2 w = *(const u32x2*)((const uint16_t*)xrow + i0);
+        const uint32_t w0 = w[0], w1 = w[1];
+        v[0] = __builtin_bit_cast(float, w0 << 16);
+        v[1] = __builtin_bit_cast(float, w0 & 0xFFFF0000u);
+        v[2] = __builtin_bit_cast(float, w1 << 16);
+        v[3] = __builtin_bit_cast(float, w1 & 0xFFFF0000u);
+    } else {
+        const u32x4 w = *(const u32x4*)((const float*)xrow + i0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wi = w[i];
+            v[i] = __builtin_bit_cast(float, wi);
+        }
+    }
 }
-
-// the group's arithmetic, v = this lane's input
+// the four groups' arithmetic, v = this lane's inputs
 template <int XP, int BITS>
-__device__ __forceinline__ void prep_group_v(float v, int t, int H, int g, uint32_t* pairs, float* K, float* X,
-                                             float* inv) {
-    const int lane = threadIdx.x & 63;
-    const int e = act_exponent(wave_max(fabsf(v)));
-    constexpr int SET = BITS == 4 ? 8 : 16;  // inputs per pairing set
-    constexpr int PD = SET / 2;              // pair dwords per set and part
-    const int p = lane % SET, set = lane / SET;
-    // nibbles: odd p / 16; 2-bit codes: the in-place factor of pair p % 8
-    const int sh = BITS == 4 ? ((p & 1) ? -4 : 0) : crumb_scale_log2(p & 7);
-    const float vs = v * ldexpf(1.0f, e + sh);
-    const _Float16 hi = (_Float16)vs;
-    const _Float16 lo = (_Float16)(vs - (float)hi);
-    const double kd = wave_sum_d((double)(float)hi + (XP == 2 ? (double)(float)lo : 0.0));
-    const float xs = wave_sum(v);
-    const uint32_t bh = __builtin_bit_cast(uint16_t, hi), bl = __builtin_bit_cast(uint16_t, lo);
-    const uint32_t ph = __shfl_down(bh, PD, 64), pl = __shfl_down(bl, PD, 64);
-    uint32_t* gp = pairs + ((size_t)t * (H / 8) + 8 * g) * XP * 4;
-    if (p < PD) {
-        gp[(set * XP + 0) * PD + p] = bh | (ph << 16);
-        if (XP == 2) gp[(set * XP + 1) * PD + p] = bl | (pl << 16);
+__device__ __forceinline__ void prep_quad_v(const float (&v)[4], int NG, int g0, uint32_t* pairs, float* K, float* X,
+                                            float* inv) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = g0 + (lane >> 4);
+    const int e = act_exponent(row_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])))));
+    uint32_t h[2] = {0u, 0u}, l[2] = {0u, 0u};
+    double kd = 0.0;
+    float xs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sh = BITS == 4 ? ((i & 1) ? -4 : 0) : crumb_scale_log2(4 * (m & 1) + i);
+        const float vs = v[i] * ldexpf(1.0f, e + sh);
+        const _Float16 hi = (_Float16)vs;
+        const _Float16 lo = (_Float16)(vs - (float)hi);
+        h[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, hi) << (16 * (i & 1));
+        l[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, lo) << (16 * (i & 1));
+        kd += (double)(float)hi + (XP == 2 ? (double)(float)lo : 0.0);
+        xs += v[i];
     }
-    if (lane == 0) {
-        const size_t gi = (size_t)t * (H / 64) + g;
-        K[gi] = (float)(1024.0 * kd);
-        X[gi] = xs;
-        inv[gi] = ldexpf(1.0f, -e);
+    kd = row_sum_d(kd);
+    xs = row_sum(xs);
+    // partner lane with the other members of this lane's pairs: m ^ 1 (8-sets
+    // over two lanes), m ^ 2 (16-sets over four lanes, j and j + 8)
+    constexpr int CTRL = BITS == 4 ? 0xB1 : 0x4E;
+    const bool writer = BITS == 4 ? (m & 1) == 0 : (m & 2) == 0;
+    uint32_t* gp = pairs + (size_t)g * 32 * XP;
+    // 4-bit: 8-set m/2, 4 pair dwords per part; 2-bit: 16-set m/4, 8 pair dwords per part, 4(m & 1) onward
+    const int off = BITS == 4 ? (m >> 1) * XP * 4 : (m >> 2) * XP * 8 + 4 * (m & 1);
+    const int part_stride = BITS == 4 ? 4 : 8;
+#pragma unroll
+    for (int part = 0; part < XP; ++part) {
+        const uint32_t w01 = part ? l[0] : h[0], w23 = part ? l[1] : h[1];
+        const uint32_t q01 = dpp_u32<CTRL>(w01), q23 = dpp_u32<CTRL>(w23);
+        const u32x4 pd = {(w01 & 0xFFFFu) | (q01 << 16), (w01 >> 16) | (q01 & 0xFFFF0000u),
+                          (w23 & 0xFFFFu) | (q23 << 16), (w23 >> 16) | (q23 & 0xFFFF0000u)};
+        if (writer && g < NG) *(u32x4*)(gp + off + part * part_stride) = pd;
+    }
+    if (m == 0 && g < NG) {
+        K[g] = (float)(1024.0 * kd);
+        X[g] = xs;
+        inv[g] = ldexpf(1.0f, -e);
     }
 }
-
 template <int XP, bool BF16, int BITS>
-__device__ void prep_group(const void* x, int t, int H, int g, uint32_t* pairs, float* K, float* X, float* inv) {
-    const float v = load_act<BF16>(x, (size_t)t * H + 64 * g + (threadIdx.x & 63));
-    prep_group_v<XP, BITS>(v, t, H, g, pairs, K, X, inv);
+__device__ void prep_quad(const void* xrow, int NG, int g0, uint32_t* pairs, float* K, float* X, float* inv) {
+    float v[4];
+    load_act4<BF16>(xrow, min(g0 + (int)((threadIdx.x & 63) >> 4), NG - 1), v);
+    prep_quad_v<XP, BITS>(v, NG, g0, pairs, K, X, inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,9 +393,12 @@ template <int XP, bool BF16, int BITS>
 __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int rb = (a.E + kWaves - 1) / kWaves;
-    if ((int)blockIdx.x >= rb) {  // activation preparation blocks (one token each)
-        const int g = ((int)blockIdx.x - rb) * kWaves + wave;
-        if (g < a.H / 64) prep_group<XP, BF16, BITS>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+    if ((int)blockIdx.x >= rb) {  // activation preparation blocks (one token each, four groups a wave)
+        const int g0 = 4 * (((int)blockIdx.x - rb) * kWaves + wave), NG = a.H / 64, t = blockIdx.y;
+        if (g0 < NG)
+            prep_quad<XP, BF16, BITS>((const uint8_t*)a.x + (size_t)t * a.H * (BF16 ? 2 : 4), NG, g0,
+                                      a.xpairs + (size_t)t * (a.H / 2) * XP, a.xK + (size_t)t * NG,
+                                      a.xX + (size_t)t * NG, a.xinv + (size_t)t * NG);
         return;
     }
     const int e = blockIdx.x * kWaves + wave;
@@ -401,8 +456,11 @@ __global__ __launch_bounds__(64) void k_topk(RouteArgs a) {
 // k_prep: grid (ceil(H/256), T); one wave per 64-input group.
 template <int XP, bool BF16, int BITS>
 __global__ __launch_bounds__(kBlock) void k_prep(RouteArgs a) {
-    const int g = blockIdx.x * kWaves + wave_id();
-    if (g < a.H / 64) prep_group<XP, BF16, BITS>(a.x, blockIdx.y, a.H, g, a.xpairs, a.xK, a.xX, a.xinv);
+    const int g0 = 4 * (blockIdx.x * kWaves + wave_id()), NG = a.H / 64, t = blockIdx.y;
+    if (g0 < NG)
+        prep_quad<XP, BF16, BITS>((const uint8_t*)a.x + (size_t)t * a.H * (BF16 ? 2 : 4), NG, g0,
+                                  a.xpairs + (size_t)t * (a.H / 2) * XP, a.xK + (size_t)t * NG, a.xX + (size_t)t * NG,
+                                  a.xinv + (size_t)t * NG);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,6 +500,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
         }
         return;
     }
+    const uint64_t t_launch = wall_clock64();  // 100 MHz device clock
     const int u = blockIdx.x - route_units + a.unit_offset;
     const bool fused = route_units > 0;
     const bool routed = u < a.k * a.blk_r;
@@ -457,14 +516,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     u32x4 xv[kXPrepVecsPerThread];
     float kx = 0.0f, xx = 0.0f, xi = 0.0f;
     if (fused) {
-        constexpr int R = kFusedMaxHidden / 64 / WAVES;  // groups per wave at most
+        constexpr int R = (kFusedMaxHidden / 256 + WAVES - 1) / WAVES;  // four-group rounds per wave at most
         const uint8_t* xrow = (const uint8_t*)a.x + (size_t)t * H * (XP == 1 ? 2 : 4);
-        float v[R];
+        float v[R][4];
 #pragma unroll
-        for (int r = 0; r < R; ++r) v[r] = load_act<XP == 1>(xrow, min(wave + WAVES * r, NG - 1) * 64 + lane);
+        for (int r = 0; r < R; ++r) load_act4<XP == 1>(xrow, min(4 * (wave + WAVES * r) + (lane >> 4), NG - 1), v[r]);
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            if (wave + WAVES * r < NG) prep_group_v<XP, BITS>(v[r], 0, H, wave + WAVES * r, xp, sK, sX, sI);
+            if (4 * (wave + WAVES * r) < NG) prep_quad_v<XP, BITS>(v[r], NG, 4 * (wave + WAVES * r), xp, sK, sX, sI);
     } else {
         const u32x4* gx = (const u32x4*)(a.xpairs + (size_t)t * (H / 2) * XP);
         // Loads are unconditional with clamped addresses so that the number of
@@ -488,7 +547,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
         float* w_out = first ? a.w_out + (size_t)t * a.k : nullptr;
         if (fused) {
             float lv[Q] = {};
-            if (wave == 0) fused_logits<Q, XP == 1>(a, t, lv);
+            if (wave == 0) {
+                // first read no earlier than the router units' span (bounded wait)
+                while (wall_clock64() - t_launch < (uint64_t)kLogitPollDelayTicks) __builtin_amdgcn_s_sleep(1);
+                fused_logits<Q, XP == 1>(a, t, lv);
+            }
             e = topk_select_v<Q>(lv, a.E, a.k, j, s_topk, ids_out, w_out, GateFn{a.gate, a.bias, a.rscale});
         } else if (a.logits) {
             e = topk_select<Q>(a.logits + (size_t)t * a.E, a.E, a.k, j, s_topk, ids_out, w_out,
@@ -830,7 +893,7 @@ __global__ void k_clear_word(uint32_t* p) { *p = 0u; }
 // beside them, one token per block row.
 hipError_t launch_route(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
     const int rpb = kWaves;  // one router row per wave
-    const int nb = (a.E + rpb - 1) / rpb + (a.prep ? (a.H / 64 + kWaves - 1) / kWaves : 0);
+    const int nb = (a.E + rpb - 1) / rpb + (a.prep ? ((a.H / 64 + 3) / 4 + kWaves - 1) / kWaves : 0);
     const dim3 grid(nb, T);
     if (a.bits == 2) {
         if (act_bf16) launch_kernel(k_route<1, true, 2>, grid, dim3(kBlock), 0, s, a);
@@ -851,7 +914,7 @@ hipError_t launch_topk(const RouteArgs& a, int T, hipStream_t s) {
 }
 
 hipError_t launch_prep(const RouteArgs& a, int T, int act_bf16, hipStream_t s) {
-    const dim3 grid((a.H / 64 + kWaves - 1) / kWaves, T);
+    const dim3 grid(((a.H / 64 + 3) / 4 + kWaves - 1) / kWaves, T);  // four groups per wave
     if (a.bits == 2) {
         if (act_bf16) launch_kernel(k_prep<1, true, 2>, grid, dim3(kBlock), 0, s, a);
         else launch_kernel(k_prep<2, false, 2>, grid, dim3(kBlock), 0, s, a);
