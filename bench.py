@@ -49,14 +49,14 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12463.48 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
+    # FETCH_SIZE 12426.53 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
     # also runs the router)
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25568087, "moe_kernels.hip", "a77a2646aa726983"),
-    # 2-bit records: FETCH_SIZE 7057.03 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (14495676, "moe_kernels.hip", "a77a2646aa726983"),
-    # FETCH_SIZE 1833801.68 KiB x 2.0 + WRITE_SIZE 5753.57 KiB x 1.0 per launch (mean over
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25492407, "moe_kernels.hip", "f04d88d3dba192e2"),
+    # 2-bit records: FETCH_SIZE 7026.67 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (14433501, "moe_kernels.hip", "f04d88d3dba192e2"),
+    # FETCH_SIZE 1833636.30 KiB x 2.0 + WRITE_SIZE 5752.74 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761517496, "moe_prefill.hip", "44cc6cfd0e4a0fe1"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761177948, "moe_prefill.hip", "abea37c5c198022b"),
 }
 
 
