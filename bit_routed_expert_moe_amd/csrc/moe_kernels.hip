@@ -246,19 +246,21 @@ __device__ __forceinline__ int topk_select_v(const float (&lg0)[Q], int E, int k
             before += __builtin_popcountll(eqm);
             pos0 += __builtin_popcountll(tm);
         }
+        if (lane >= k && lane < kMaxTopK) sm.key[lane] = 0u;  // below every selected key
     }
     __syncthreads();
-    // entry j (lane j < k): its rank among the k entries (held in id order)
+    // entry j (lane j < k): its rank among the k entries (held in id order):
+    // the entries ahead of it are those with a larger (key, -position), one
+    // 64-bit compare each; the zero keys past k are behind every entry
     uint32_t keys[kMaxTopK];
 #pragma unroll
     for (int i = 0; i < kMaxTopK; ++i) keys[i] = sm.key[i];
     const int mine = min(lane, kMaxTopK - 1);
-    const uint32_t mu = sm.key[mine];
     const int my_id = sm.id[mine];
+    const uint64_t mc = ((uint64_t)sm.key[mine] << 32) | (uint32_t)(kMaxTopK - 1 - mine);
     int rank = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i)
-        rank += (i < k && (keys[i] > mu || (keys[i] == mu && i < lane))) ? 1 : 0;
+    for (int i = 0; i < kMaxTopK; ++i) rank += (((uint64_t)keys[i] << 32) | (uint32_t)(kMaxTopK - 1 - i)) > mc ? 1 : 0;
     const bool valid = lane < k;
     if (ids_out && threadIdx.x < 64) {
         const float v = valid ? sm.val[mine] : 0.0f;
