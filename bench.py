@@ -49,11 +49,11 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12426.53 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
+    # FETCH_SIZE 12422.49 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
     # also runs the router)
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25492407, "moe_kernels.hip", "f04d88d3dba192e2"),
-    # 2-bit records: FETCH_SIZE 7026.67 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (14433501, "moe_kernels.hip", "f04d88d3dba192e2"),
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25484150, "moe_kernels.hip", "beb75e1d22d1bead"),
+    # 2-bit records: FETCH_SIZE 7019.34 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch
+    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (14418497, "moe_kernels.hip", "beb75e1d22d1bead"),
     # FETCH_SIZE 1833636.30 KiB x 2.0 + WRITE_SIZE 5752.74 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
     ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761177948, "moe_prefill.hip", "abea37c5c198022b"),
