@@ -26,6 +26,7 @@ hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_route_tiles(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, int n_blocks, uint32_t* sink, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -89,7 +90,7 @@ thread_local std::string g_last_error;
 
 // ---- per-launch event timing (moe_profile_*) ----
 enum { K_ROUTE = 0, K_PREP = 1, K_GATE_UP = 2, K_DOWN = 3, K_COMBINE = 4, K_TOPK = 5,
-       K_PF_PREP = 6, K_PF_GROUP = 7, K_PF_GATE_UP = 8, K_PF_DOWN = 9 };
+       K_PF_PREP = 6, K_PF_GROUP = 7, K_PF_GATE_UP = 8, K_PF_DOWN = 9, K_STREAM = 10 };
 struct ProfRec {
     int kid;
     hipEvent_t a, b;
@@ -775,9 +776,20 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
                              int64_t x_stride, int32_t T, int32_t* ids, float* w, float* y,
                              int64_t y_stride, void* workspace, void* stream) {
     if (!layers || n_layers <= 0) return fail(MOE_ERR_ARG, "no layers");
+    if (T <= 0) return fail(MOE_ERR_ARG, "n_tokens out of range");
+    // every layer's ids/w rows sit at l * T * top_k and its x at l * x_stride
+    // elements of one activation dtype: the layers must agree on both, and
+    // each layer's [T][H] block must fit in its stride
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer* L = layers[l];
         if (!L) return fail(MOE_ERR_ARG, "null layer handle in stack");
+        if (L->d.top_k != layers[0]->d.top_k || L->d.act_dtype != layers[0]->d.act_dtype)
+            return fail(MOE_ERR_SHAPE, "stack layers must share top_k and act_dtype");
+        if ((int64_t)T * L->d.hidden > x_stride || (int64_t)T * L->d.hidden > y_stride)
+            return fail(MOE_ERR_SHAPE, "x_stride and y_stride must hold n_tokens * hidden elements");
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer* L = layers[l];
         const size_t esz = L->d.act_dtype == MOE_BF16 ? 2 : 4;
         const void* xl = (const uint8_t*)x + (size_t)l * x_stride * esz;
         moe_status st = moe_layer_forward(layers[l], xl, T, ids + (size_t)l * T * L->d.top_k,
@@ -900,6 +912,16 @@ moe_status moe_poll_device_error(moe_layer_t L, void* workspace, void* stream) {
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "device error poll");
     return host ? fail(MOE_ERR_DEVICE, "a kernel saw an expert id outside [0, n_experts)") : MOE_OK;
+}
+
+moe_status moe_stream_read(const void* src, size_t bytes, int32_t n_blocks, uint32_t* sink, void* stream) {
+    if (!src || !sink) return fail(MOE_ERR_ARG, "null src or sink");
+    if (bytes == 0 || bytes % 16) return fail(MOE_ERR_ARG, "bytes must be a positive multiple of 16");
+    if (n_blocks < 1 || n_blocks > (1 << 20)) return fail(MOE_ERR_ARG, "n_blocks must be in 1..2^20");
+    if (!aligned(src, 16) || !aligned(sink, 4)) return fail(MOE_ERR_ALIGN, "src needs 16-byte alignment");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = timed(K_STREAM, s, [&] { return launch_stream_read(src, bytes, n_blocks, sink, s); });
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "stream read launch");
 }
 
 moe_status moe_profile_start(int32_t capacity) {

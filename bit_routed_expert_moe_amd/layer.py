@@ -26,11 +26,12 @@ EXPORTS = ["moe_expert_record_bytes", "moe_expert_record_bytes_bits", "moe_layer
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
            "moe_cache_prefetch", "moe_cache_prefetch_ids", "moe_cache_prefetch_stats",
-           "moe_poll_device_error",
+           "moe_poll_device_error", "moe_stream_read",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
            "moe_status_str", "moe_last_error"]
 KERNEL_NAMES = {0: "route", 1: "prep", 2: "gate_up", 3: "down_combine", 4: "combine", 5: "topk",
-                6: "grouped_prep", 7: "grouping", 8: "grouped_gate_up", 9: "grouped_down"}
+                6: "grouped_prep", 7: "grouping", 8: "grouped_gate_up", 9: "grouped_down",
+                10: "stream_read"}
 
 
 class MoeError(RuntimeError):
@@ -77,6 +78,7 @@ def lib() -> C.CDLL:
         L.moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
         L.moe_stack_forward.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, i64, vp, vp]
         L.moe_poll_device_error.argtypes = [vp, vp, vp]
+        L.moe_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
         L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
         L.moe_cache_pin.argtypes = [vp, C.POINTER(C.c_int32), i32, vp]
         L.moe_cache_prefetch.argtypes = [vp, vp, i32, vp, C.POINTER(C.c_int32), vp]
@@ -90,7 +92,7 @@ def lib() -> C.CDLL:
         L.moe_profile_read.restype = i32
         for f in ["moe_layer_create", "moe_layer_destroy", "moe_route_topk", "moe_expert_ffn",
                   "moe_combine", "moe_layer_forward", "moe_stack_forward",
-                  "moe_poll_device_error", "moe_profile_start", "moe_profile_stop",
+                  "moe_poll_device_error", "moe_stream_read", "moe_profile_start", "moe_profile_stop",
                   "moe_cache_stats", "moe_cache_pin", "moe_cache_prefetch", "moe_cache_prefetch_ids",
                   "moe_cache_prefetch_stats"]:
             getattr(L, f).restype = i32
@@ -281,6 +283,11 @@ def stack_forward(layers: list[Layer], x: torch.Tensor, ws: torch.Tensor, out=No
     """x [L][T][H] -> (ids [L][T][k], w [L][T][k], y [L][T][H]); layer l reads x[l]."""
     L, T, H = x.shape
     k = layers[0].top_k
+    if len(layers) != L:
+        raise ValueError(f"x holds {L} layers' inputs for {len(layers)} layers")
+    for lay in layers:
+        if lay.hidden != H or lay.top_k != k or lay.act != layers[0].act:
+            raise ValueError("stack layers must share hidden, top_k and activation dtype")
     if out is None:
         ids = torch.empty(L, T, k, dtype=torch.int32, device="cuda")
         w = torch.empty(L, T, k, dtype=torch.float32, device="cuda")
@@ -293,6 +300,15 @@ def stack_forward(layers: list[Layer], x: torch.Tensor, ws: torch.Tensor, out=No
                                    _dev(y, "y", torch.float32), T * H, _dev(ws, "workspace"),
                                    _stream()))
     return ids, w, y
+
+
+def stream_read(buf: torch.Tensor, offset: int, nbytes: int, n_blocks: int, sink: torch.Tensor) -> None:
+    """Plain streaming read of nbytes of the uint8 CUDA tensor buf from byte
+    offset (moe_stream_read): the measured HBM reference."""
+    if offset < 0 or offset + nbytes > buf.numel() * buf.element_size():
+        raise ValueError("read past the end of buf")
+    _check(lib().moe_stream_read(_dev(buf, "buf") + offset, nbytes, n_blocks,
+                                 _dev(sink, "sink", torch.int32), _stream()))
 
 
 class KernelTimer:

@@ -210,7 +210,13 @@ moe_status moe_layer_forward(moe_layer_t layer, const void* x, int32_t n_tokens,
 /* n_layers layers one after another on one stream, layer l reading x_l and
  * writing y_l (strides in elements: x_stride for x, y_stride for y, k-strided
  * ids/w per layer), each layer ordered after the previous one's output.  The
- * workspace must be sized for the largest layer.  Errors as moe_layer_forward. */
+ * layers must share top_k and act_dtype (their ids/w rows sit at l*T*top_k and
+ * their x at l*x_stride elements of one dtype), and x_stride and y_stride must
+ * each hold n_tokens*hidden elements of every layer (else MOE_ERR_SHAPE, checked
+ * before anything is enqueued).  The workspace must be sized for the largest
+ * layer.  The decode engines on the pages run their layers in this order, one
+ * token at a time (TurboFieldfare article, "Proses pembuatan token").  Errors as
+ * moe_layer_forward, plus SHAPE. */
 moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const void* x,
                              int64_t x_stride, int32_t n_tokens, int32_t* ids, float* w,
                              float* y, int64_t y_stride, void* workspace, void* stream);
@@ -287,6 +293,18 @@ moe_status moe_cache_prefetch_stats(moe_layer_t layer, uint64_t* issued, uint64_
  * MOE_ERR_DEVICE otherwise. */
 moe_status moe_poll_device_error(moe_layer_t layer, void* workspace, void* stream);
 
+/* Measurement reference (not part of the layer): reads `bytes` bytes of device
+ * memory at `src` (16-byte aligned, bytes a positive multiple of 16) with the
+ * 16-byte nontemporal loads the expert kernels use, `n_blocks` workgroups of
+ * 256 threads each reading one contiguous slice, and no arithmetic beyond an
+ * XOR of the loaded words.  Its rate is what this chip's HBM delivers to a
+ * plain read-only stream of that size, the achievable figure the expert
+ * kernels' rates are set against.  sink: device, one 32-bit word, written only
+ * when the XOR equals a fixed value the data practically never produce (so the
+ * loads cannot be removed).  Kernel id 10 in the profile records.  Enqueued on
+ * `stream`.  Errors: ARG, ALIGN, HIP. */
+moe_status moe_stream_read(const void* src, size_t bytes, int32_t n_blocks, uint32_t* sink, void* stream);
+
 /* Measurement support.  While profiling is on, the library dispatches the
  * first kernel of each launch step with hipExtLaunchKernelGGL carrying a
  * start/stop hipEvent pair, so the pair holds that dispatch's own start and
@@ -295,7 +313,7 @@ moe_status moe_poll_device_error(moe_layer_t layer, void* workspace, void* strea
  * per recorded launch, the kernel id (0 router, 1 activation prep, 2 gate/up,
  * 3 down with in-place combine, 4 combine, 5 top-k; for calls of 4 or more
  * tokens: 6 activation prep, 7 grouping by expert, 8 grouped gate/up, 9 grouped
- * down) and the elapsed milliseconds;
+ * down; 10 moe_stream_read) and the elapsed milliseconds;
  * it returns the number of records (or a negative status) and clears them.
  * Profiling state is process-wide and not thread-safe; do not profile inside
  * stream capture.  Errors: ARG, HIP, NOMEM. */

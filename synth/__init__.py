@@ -254,6 +254,19 @@ class ZipfRealiser:
         d = self.Q @ sla.solve_triangular(self.R.T, resid, lower=True)
         return (z + d)[None, :]
 
+    def activations_batch(self, steps, attempt: int = 0) -> np.ndarray:
+        """activations(step, attempt)[0] for every step, as one [S][H] array
+        (the same draws; the least-squares step runs on all of them at once, so
+        values may differ from the one-step form in the last bits)."""
+        import scipy.linalg as sla
+        steps = list(steps)
+        t = np.stack([self.target(s, attempt) for s in steps])
+        z = np.stack([normal(key(self.seed, self.layer, KIND_Z1, s, attempt),
+                             key(self.seed, self.layer, KIND_Z2, s, attempt), self.H) for s in steps])
+        resid = t - z @ self.W.T
+        d = sla.solve_triangular(self.R.T, resid.T, lower=True)
+        return z + (self.Q @ d).T
+
 
 # ---------------------------------------------------------------------------
 # workloads (shapes and recipes of the pages' configurations)

@@ -21,6 +21,16 @@ def rel_err(y, y_ref) -> float:
     return float(np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-30))
 
 
+def elem_err(y, y_ref, floor: float = 1e-3) -> float:
+    """Element-wise relative error with a floor: max_i |y_i - y_ref_i| /
+    max(|y_ref_i|, floor * max |y_ref|) (reported beside rel_err; near-zero
+    outputs would otherwise dominate)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    den = np.maximum(np.abs(y_ref), floor * max(np.max(np.abs(y_ref)), 1e-30))
+    return float(np.max(np.abs(y - y_ref) / den))
+
+
 def gap_ok(logits: np.ndarray, k: int, gap: float = GAP) -> bool:
     s = np.sort(logits)[::-1][:k + 1]
     return bool(np.all(-np.diff(s) > gap))
@@ -93,6 +103,25 @@ class DeviceLayer:
         ys = (orc.expert_ffn(self.H, self.Is, self.record(synth.SHARED_INDEX), xd, bits=self.bits)
               if self.Is else None)
         return ids, w, orc.combine(w, yr, ys), yr, ys
+
+
+def zipf_tokens(dl, orc, zipf_s: float, steps, max_attempts: int = 50):
+    """Activations for dl's layer whose router response aims at Zipf(zipf_s)
+    Gumbel-top-k targets (synth.ZipfRealiser), one per step, redrawn until the
+    oracle's top-(k+1) logits are separated by more than GAP.  [(raw, float64)]."""
+    Wd = dl.rq.astype(np.float64) * dl.rs.view(np.float16).astype(np.float64)[:, None]
+    zr = synth.ZipfRealiser(Wd, zipf_s, dl.seed, dl.layer)
+    out = []
+    for step in steps:
+        for a in range(max_attempts):
+            xq = synth.quantize_act(zr.activations(step, a)[0], dl.act)
+            xd = orc.act_to_f64(dl.act, xq)
+            if gap_ok(orc.router_logits(dl.rq, dl.rs, xd), dl.k):
+                break
+        else:
+            raise RuntimeError("no well-separated token found")
+        out.append((xq, xd))
+    return out
 
 
 def to_dev(xq: np.ndarray, act: str, dev="cuda") -> torch.Tensor:

@@ -111,3 +111,12 @@ def test_null_handles():
     assert lib.moe_workspace_bytes(None, 1) == 0
     assert lib.moe_layer_forward(None, None, 1, None, None, None, None, None) == -1
     assert lib.moe_stack_forward(None, 0, None, 0, 1, None, None, None, 0, None, None) == -1
+
+
+def test_stream_read_rejects_bad_arguments_on_the_host():
+    lib = L.lib()
+    assert lib.moe_stream_read(None, 16, 1, 0x20000, None) == -1
+    assert lib.moe_stream_read(0x10000, 0, 1, 0x20000, None) == -1
+    assert lib.moe_stream_read(0x10000, 24, 1, 0x20000, None) == -1   # not whole 16-byte vectors
+    assert lib.moe_stream_read(0x10000, 16, 0, 0x20000, None) == -1
+    assert lib.moe_stream_read(0x10008, 16, 1, 0x20000, None) == -3

@@ -15,7 +15,7 @@ import torch
 
 import synth
 import synth.gpu
-from _gpu_helpers import W_TOL, Y_TOL, DeviceLayer, rel_err, to_dev
+from _gpu_helpers import W_TOL, Y_TOL, DeviceLayer, elem_err, rel_err, to_dev
 from _packer import DenseExpert
 
 pytestmark = pytest.mark.gpu
@@ -34,13 +34,15 @@ def _gpu():
 
 
 def check_tokens(dl, orc, xs_q, xs_d, ids, w, y, tag):
-    worst_y, worst_w = 0.0, 0.0
+    worst_y, worst_w, worst_e = 0.0, 0.0, 0.0
     for t in range(len(xs_d)):
         rid, rw, ry, _, _ = dl.oracle(orc, xs_d[t])
         assert ids[t].tolist() == rid.tolist(), f"{tag} token {t}: ids {ids[t]} vs {rid}"
         worst_w = max(worst_w, float(np.max(np.abs(w[t] - rw))))
         worst_y = max(worst_y, rel_err(y[t], ry))
-    say(f"{tag}: {len(xs_d)} tokens, max |w err| {worst_w:.2e}, max rel y err {worst_y:.2e}")
+        worst_e = max(worst_e, elem_err(y[t], ry))
+    say(f"{tag}: {len(xs_d)} tokens, max |w err| {worst_w:.2e}, max rel y err {worst_y:.2e}, "
+        f"element-wise (floor 1e-3 max|y|) {worst_e:.2e}")
     assert worst_w <= W_TOL and worst_y <= Y_TOL
 
 
@@ -101,21 +103,32 @@ def test_api_calls_match_fused_forward_bitwise(orc):
     assert torch.equal(yb.cpu(), ref), "bf16 output is not the nearest-even rounding"
 
 
-@pytest.mark.parametrize("H,E,I,k,Is,act", [
+SHAPES = [
     (192, 7, 64, 3, 0, "bf16"),        # fewer input groups than waves, no shared expert
     (320, 64, 192, 8, 320, "bf16"),    # ragged splits everywhere
     (64, 1, 64, 1, 64, "f32"),         # minimum sizes, a single expert
     (1024, 1024, 128, 16, 0, "bf16"),  # most experts, largest k
     (8192, 16, 64, 2, 128, "bf16"),    # largest hidden
     (2816, 128, 704, 8, 2112, "f32"),  # Gemma-scale shapes with fp32 activations
-])
-def test_shapes(orc, H, E, I, k, Is, act):
+    (4160, 32, 1152, 8, 640, "bf16"),  # 4-wave gate/up with a ragged last wave; 5 down groups per wave
+    (2048, 96, 2048, 8, 2048, "f32"),  # intermediate 2048 (8 down groups per wave), fp32
+    (8192, 64, 4096, 4, 0, "bf16"),    # largest hidden and intermediate: 32 gate/up and 16 down groups per wave
+]
+
+
+@pytest.mark.parametrize("T", [1, 3, 6])
+@pytest.mark.parametrize("H,E,I,k,Is,act", SHAPES)
+def test_shapes(orc, H, E, I, k, Is, act, T):
+    """Each shape through one call of T tokens: T = 1 and 3 take the per-token
+    (decode) kernels, T = 6 the grouped path.  ids bit-exact, gates within
+    1e-6, y within 2e-3 of the oracle on every token."""
     dl = DeviceLayer(0xB17E0200 + H + E, 1, H, E, I, k, Is, act)
-    toks = [dl.natural_token(orc, s) for s in range(6)]
+    toks = [dl.natural_token(orc, s) for s in range(T)]
     xq = np.stack([t[0] for t in toks])
     ids, w, y = dl.layer_obj.forward(to_dev(xq, act))
+    path = "grouped" if T >= 4 else "per-token"
     check_tokens(dl, orc, xq, [t[1] for t in toks], ids.cpu().numpy(), w.cpu().numpy(),
-                 y.cpu().numpy(), f"H{H} E{E} I{I} k{k} S{Is} {act}")
+                 y.cpu().numpy(), f"H{H} E{E} I{I} k{k} S{Is} {act} T={T} ({path})")
 
 
 def test_dense_swiglu_special_case():
@@ -205,11 +218,14 @@ def test_integer_activations_give_exact_logits():
         assert np.max(np.abs(w.cpu().numpy()[0] - wref)) <= W_TOL
 
 
-def test_rerun_is_bitwise_identical(orc):
+@pytest.mark.parametrize("T", [1, 3, 4])
+def test_rerun_is_bitwise_identical(orc, T):
+    """Two calls on one workspace and one on a fresh workspace give the same
+    bits: T = 1 and 3 on the per-token path, T = 4 on the grouped path."""
     dl = DeviceLayer(0xB17E0300, 0, 2816, 128, 704, 8, 2112, "bf16")
-    toks = [dl.natural_token(orc, s) for s in range(4)]
+    toks = [dl.natural_token(orc, s) for s in range(T)]
     x = to_dev(np.stack([t[0] for t in toks]), "bf16")
-    ws = dl.layer_obj.workspace(4)
+    ws = dl.layer_obj.workspace(T)
     r1 = dl.layer_obj.forward(x, ws)
     r2 = dl.layer_obj.forward(x, ws)
     r3 = dl.layer_obj.forward(x)  # fresh workspace

@@ -171,3 +171,47 @@ def test_cache_rejects_unpinned_pool_and_batches():
     with pytest.raises(MoeError) as ei:
         dl.layer_obj.cache_pin([0])  # no slot cache
     assert ei.value.status == -7
+
+
+def test_offload_workload_shapes_full_size(orc):
+    """The out-of-core workload at its stated shapes: hidden 2816, 256 experts of
+    intermediate 704, shared 2112, 16 LFU slots per layer filled from a pinned
+    host pool of all 256 records, Zipf(1.1) routing.  Two layers, 64 decode
+    steps each (layer 0 then layer 1 per step, one workspace per twin): every
+    step's ids, gates and y equal the resident layer's bit for bit, the ids
+    equal the oracle's, every 8th step's y is within 2e-3 of the oracle, and
+    each layer's hits and misses equal the CPU LFU simulation."""
+    from _gpu_helpers import W_TOL, Y_TOL, rel_err, zipf_tokens
+    wl = synth.WORKLOADS["offload_h2816_e256_l40_lfu16"]
+    NL, S = 2, 64
+    dls = [DeviceLayer(wl.seed, l, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
+           for l in range(NL)]
+    twins = [cached_twin(dl, wl.n_slots) for dl in dls]
+    toks = [zipf_tokens(dl, orc, wl.zipf_s, range(S)) for dl in dls]
+    ws_r, ws_c = dls[0].layer_obj.workspace(1), twins[0][0].workspace(1)
+    oracle_ids = [[] for _ in range(NL)]
+    worst_y = 0.0
+    for step in range(S):
+        for l, dl in enumerate(dls):
+            xq, xd = toks[l][step]
+            x = to_dev(xq[None], wl.act)
+            r = dl.layer_obj.forward(x, ws_r)
+            c = twins[l][0].forward(x, ws_c)
+            for a_, b_ in zip(r, c):
+                assert torch.equal(a_, b_), f"layer {l} step {step}: cached result differs from resident"
+            if step % 8 == 0:
+                rid, rw, ry, _, _ = dl.oracle(orc, xd)
+                assert np.max(np.abs(r[1].cpu().numpy()[0] - rw)) <= W_TOL
+                worst_y = max(worst_y, rel_err(r[2].cpu().numpy()[0], ry))
+            else:
+                rid = orc.route(dl.rq, dl.rs, xd, wl.top_k)[0]
+            assert r[0].cpu().numpy()[0].tolist() == rid.tolist(), f"layer {l} step {step}"
+            oracle_ids[l].append(rid)
+    for l in range(NL):
+        hits, misses = twins[l][0].cache_stats()
+        sim = cache_simulation(oracle_ids[l], wl.n_slots, wl.n_experts, "lfu")
+        assert (hits, misses) == sim[:2], f"layer {l}"
+        print(f"offload shapes, layer {l}: {S} steps, hits {hits} misses {misses} "
+              f"hit rate {hits / (hits + misses):.3f}", flush=True)
+    print(f"offload shapes: max rel y err on sampled steps {worst_y:.2e}", flush=True)
+    assert worst_y <= Y_TOL
