@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -83,6 +84,14 @@ struct moe_layer {
 namespace moe {
 LaunchStamp* g_stamp = nullptr;  // see launch_kernel
 }  // namespace moe
+
+// Scratch of moe_layer_forward_noalloc: the workspace of one call, in a
+// static device array (one copy per GPU, held until the process ends).  Host
+// code never uses the array's name as an address: each device's copy is
+// located once with hipGetSymbolAddress and that pointer is passed to the
+// kernels.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -798,6 +807,66 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
         if (st != MOE_OK) return st;
     }
     return MOE_OK;
+}
+
+namespace {
+// Per-device address of `scratch` and whether its counters still need the
+// one clear of their first use (or a clear after a failed call).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_dirty[kMaxDevices] = {};
+
+__global__ void k_clear_words(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// The current device's scratch address (looked up on its first use there).
+moe_status scratch_for_current_device(uint8_t** out, int* dev_out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_STATE, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = (uint8_t*)ptr;
+        g_scratch_dirty[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    *dev_out = dev;
+    return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_layer_forward_noalloc(moe_layer_t L, const void* x, int32_t T, int32_t* ids, float* w,
+                                     float* y, void* stream) {
+    if (!L) return fail(MOE_ERR_ARG, "null layer handle");
+    if (T <= 0 || T > (1 << 20)) return fail(MOE_ERR_ARG, "n_tokens out of range");
+    const size_t need = ws_layout(L, T).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_SHAPE, "this call needs " + std::to_string(need) + " bytes of scratch; the "
+                                   "allocation-free entry holds " + std::to_string(kScratchBytes));
+    uint8_t* ws = nullptr;
+    int dev = -1;
+    moe_status st = scratch_for_current_device(&ws, &dev);
+    if (st != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (g_scratch_dirty[dev]) {
+        // counters, logit words and the error word must start at zero: they
+        // are the scratch's first bytes, below the offsets that depend on T
+        const size_t words = ws_layout(L, 1).pred_ids / 4;
+        hipLaunchKernelGGL(k_clear_words, dim3(64), dim3(256), 0, s, (uint32_t*)ws, words);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+        g_scratch_dirty[dev] = false;
+    }
+    st = moe_layer_forward(L, x, T, ids, w, y, ws, stream);
+    if (st == MOE_ERR_HIP) g_scratch_dirty[dev] = true;  // a partial call may leave counters set
+    return st;
 }
 
 moe_status moe_cache_stats(moe_layer_t L, uint64_t* hits, uint64_t* misses) {

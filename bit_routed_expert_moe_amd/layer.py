@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIG
 
 EXPORTS = ["moe_expert_record_bytes", "moe_expert_record_bytes_bits", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
+           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
            "moe_cache_prefetch", "moe_cache_prefetch_ids", "moe_cache_prefetch_stats",
            "moe_poll_device_error", "moe_stream_read",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
@@ -76,6 +76,7 @@ def lib() -> C.CDLL:
         L.moe_expert_ffn.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.moe_combine.argtypes = [vp, vp, vp, i32, vp, i32, vp]
         L.moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
+        L.moe_layer_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.moe_stack_forward.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, i64, vp, vp]
         L.moe_poll_device_error.argtypes = [vp, vp, vp]
         L.moe_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
@@ -91,7 +92,7 @@ def lib() -> C.CDLL:
         L.moe_profile_read.argtypes = [vp, vp, i32]
         L.moe_profile_read.restype = i32
         for f in ["moe_layer_create", "moe_layer_destroy", "moe_route_topk", "moe_expert_ffn",
-                  "moe_combine", "moe_layer_forward", "moe_stack_forward",
+                  "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_stack_forward",
                   "moe_poll_device_error", "moe_stream_read", "moe_profile_start", "moe_profile_stop",
                   "moe_cache_stats", "moe_cache_pin", "moe_cache_prefetch", "moe_cache_prefetch_ids",
                   "moe_cache_prefetch_stats"]:
@@ -241,6 +242,16 @@ class Layer:
         _check(lib().moe_layer_forward(self.handle, self._x(x), T, _dev(ids, "ids", torch.int32),
                                        _dev(w, "w", torch.float32), _dev(y, "y", torch.float32),
                                        _dev(ws, "workspace"), _stream()))
+        return ids, w, y
+
+    def forward_noalloc(self, x: torch.Tensor, out):
+        """forward() with the library's static scratch as the workspace
+        (moe_layer_forward_noalloc): out = (ids, w, y) preallocated by the caller."""
+        T = x.shape[0]
+        ids, w, y = out
+        _check(lib().moe_layer_forward_noalloc(self.handle, self._x(x), T, _dev(ids, "ids", torch.int32),
+                                               _dev(w, "w", torch.float32), _dev(y, "y", torch.float32),
+                                               _stream()))
         return ids, w, y
 
     def cache_stats(self):

@@ -207,6 +207,23 @@ moe_status moe_combine(moe_layer_t layer, const float* expert_out, const float* 
 moe_status moe_layer_forward(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
                              float* w, float* y, void* workspace, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: the same kernels and results (bit for bit), with the workspace
+ * taken from a static device array of the library (8 MiB, one copy per GPU,
+ * held until the process ends) instead of a caller's buffer.  Calls no
+ * hipMalloc, hipFree or other allocating routine.  A call whose workspace
+ * (moe_workspace_bytes(layer, n_tokens)) exceeds 8 MiB returns MOE_ERR_SHAPE
+ * before anything is enqueued; every per-token call (n_tokens <= 3) at any
+ * shape moe_layer_create accepts fits.  The first call on a device (and the
+ * first after a call that returned MOE_ERR_HIP) enqueues a small clear
+ * kernel for the array's counters before the layer; every call returns them
+ * to zero.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and must not be issued.
+ * Errors: ARG, SHAPE, ALIGN, HIP. */
+moe_status moe_layer_forward_noalloc(moe_layer_t layer, const void* x, int32_t n_tokens, int32_t* ids,
+                                     float* w, float* y, void* stream);
+
 /* n_layers layers one after another on one stream, layer l reading x_l and
  * writing y_l (strides in elements: x_stride for x, y_stride for y, k-strided
  * ids/w per layer), each layer ordered after the previous one's output.  The
