@@ -12,7 +12,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_layer.so")
+# MOE_LAYER_LIB names another build of the same library (the sanitizer tests
+# load one with instrumented host code); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("MOE_LAYER_LIB") or os.path.join(HERE, "libmoe_layer.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK = 0
