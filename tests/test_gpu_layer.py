@@ -79,11 +79,20 @@ def test_tiny_layer_many_tokens(orc):
                  y2.cpu().numpy(), "tiny T=2 (decode path)")
 
 
-def test_api_calls_match_fused_forward_bitwise(orc):
+@pytest.mark.parametrize("H,E,I,k,Is,T", [
+    (512, 40, 192, 6, 320, 24),     # grouped path
+    (512, 40, 192, 6, 320, 1),      # per-token: separate kernels vs the one-launch FFN (routing inside)
+    (512, 40, 192, 6, 320, 3),
+    (4608, 72, 1024, 8, 1024, 1),   # per-token above hidden 4096 (router launch, then the FFN launch)
+    (4608, 72, 1024, 8, 1024, 3),
+])
+def test_api_calls_match_fused_forward_bitwise(orc, H, E, I, k, Is, T):
     """route -> expert_ffn -> combine gives exactly the fused forward's result,
-    and each per-expert output matches the oracle's expert."""
-    dl = DeviceLayer(0xB17E0101, 0, 512, 40, 192, 6, 320, "bf16")
-    toks = [dl.natural_token(orc, s) for s in range(24)]
+    and each per-expert output matches the oracle's expert.  On the per-token
+    path the API calls run the gate/up and down kernels as two launches and
+    the forward runs them as one."""
+    dl = DeviceLayer(0xB17E0101, 0, H, E, I, k, Is, "bf16")
+    toks = [dl.natural_token(orc, s) for s in range(T)]
     x = to_dev(np.stack([t[0] for t in toks]), "bf16")
     ws = dl.layer_obj.workspace(x.shape[0])
     ids_f, w_f, y_f = dl.layer_obj.forward(x, ws)
