@@ -127,8 +127,8 @@ struct FfnArgs {
     int gis;                 // input groups per shared down item
     int gpw_dn;              // input groups per wave in the down kernel
     int bits;                // weight code width: 4 or 2
-    size_t sb_off;           // start of a routed record's scale/bias region
-    size_t sb_off_shared;    // the same for the shared record
+    size_t d_off;            // start of a routed record's down segments
+    size_t d_off_shared;     // the same for the shared record
 };
 
 constexpr int kTileRows = 16;         // rows (tokens) per MFMA tile in the prefill path
@@ -157,7 +157,7 @@ struct PrefillArgs {
     const int8_t* rq;        // router [E][H] (k_route_tiles)
     const uint16_t* rs;      // router row scales [E] fp16
     float* logits;           // [T][E] out (k_route_tiles)
-    size_t sb_off, sb_off_shared;  // scale/bias region of a routed / the shared record
+    size_t d_off, d_off_shared;  // down segments of a routed / the shared record
     int H, E, I, Is, k, T, P, Imax, tile_cap, xparts, bits;
 };
 

@@ -570,12 +570,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     } else {
         rec = a.shared;
     }
-    // a 32-row block is 48*H bytes of nibbles (a 64-input group = two 16-byte
-    // chunks per tile row) or 24*H bytes of 2-bit codes (one chunk per group)
+    // the block's H/64 segments, one per 64-input group: NW 1 KB chunks of
+    // codes (16 bytes per tile row: 32 nibbles, or 64 2-bit codes) and then
+    // the 64 rows' (scale, bias) pairs, 4 bytes per row
     constexpr int NW = BITS == 4 ? 2 : 1;
-    const uint8_t* tile = rec + (size_t)(BITS == 4 ? 48 : 24) * H * b + (size_t)lane * 16;
-    const uint8_t* sbt = rec + (routed ? a.sb_off : a.sb_off_shared) + (size_t)12 * H * (b >> 1) +
-                         (size_t)4 * H * (b & 1) + (size_t)lane * 4;
+    constexpr int SEG = NW * 1024 + 256;
+    const uint8_t* tile = rec + (size_t)SEG * NG * b + (size_t)lane * 16;
+    const uint8_t* sbt = rec + (size_t)SEG * NG * b + NW * 1024 + (size_t)lane * 4;
     const int g0 = wave * a.gpw_gu;
     const int g1 = min(NG, g0 + a.gpw_gu);
 
@@ -590,8 +591,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     for (int q = 0; q < D; ++q) {
         const int g = min(g0 + q, NG - 1);
 #pragma unroll
-        for (int c = 0; c < NW; ++c) W[q][c] = ldg_nt((const u32x4*)(tile + (size_t)(NW * g + c) * 1024));
-        SB[q] = ldg_nt((const uint32_t*)(sbt + (size_t)g * 256));
+        for (int c = 0; c < NW; ++c) W[q][c] = ldg_nt((const u32x4*)(tile + (size_t)g * SEG + c * 1024));
+        SB[q] = ldg_nt((const uint32_t*)(sbt + (size_t)g * SEG));
         __builtin_amdgcn_sched_barrier(0);
     }
     // 4. activations to LDS (waits only for the loads issued before the weights)
@@ -643,8 +644,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
         if (q + D < MAXG) {  // refill the slot just consumed
             const int gn = min(g0 + q + D, NG - 1);
 #pragma unroll
-            for (int c = 0; c < NW; ++c) W[slot][c] = ldg_nt((const u32x4*)(tile + (size_t)(NW * gn + c) * 1024));
-            SB[slot] = ldg_nt((const uint32_t*)(sbt + (size_t)gn * 256));
+            for (int c = 0; c < NW; ++c) W[slot][c] = ldg_nt((const u32x4*)(tile + (size_t)gn * SEG + c * 1024));
+            SB[slot] = ldg_nt((const uint32_t*)(sbt + (size_t)gn * SEG));
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -696,12 +697,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
 // k_down: grid (n_otiles * n_items, T).  Lane = output row of a 64-row tile;
 // waves split the item's input groups (64 inputs of I = two h blocks).
 // ---------------------------------------------------------------------------
-template <int BITS> struct DownRow { typedef u32x4 T; };  // 32 nibbles of one row
-template <> struct DownRow<2> { typedef u32x2 T; };        // 32 2-bit codes
-
 template <int MAXG, int BITS>
 __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
-    typedef typename DownRow<BITS>::T RowT;
     extern __shared__ uint32_t smem[];
     const int H = a.H;
     const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -730,11 +727,15 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     const int o = ot * 64 + lane;
     const int g0 = ga + wave * a.gpw_dn;
     const int g1 = min(gb, g0 + a.gpw_dn);
-    // D block of 32 inputs of I: 16 (nibbles) or 8 (2-bit) bytes per output row,
-    // after the 32-row block's gate/up tile; blocks 48*H or 24*H bytes apart
-    const size_t blk = (size_t)(BITS == 4 ? 48 : 24) * H;
-    const uint8_t* dblk = rec + (size_t)(BITS == 4 ? 32 : 16) * H + (size_t)o * sizeof(RowT);
-    const uint8_t* dsb = rec + (item < a.k ? a.sb_off : a.sb_off_shared) + (size_t)8 * H + (size_t)o * 4;
+    // the output tile's down segments, one per 64-input group of I: the codes
+    // (two 1 KB chunks of 32 nibbles per row, or one of 64 2-bit codes per
+    // row), then the 64 rows' (scale, bias) pairs
+    constexpr int NW = BITS == 4 ? 2 : 1;
+    constexpr int SEG = NW * 1024 + 256;
+    const int ngi = (item < a.k ? a.I : a.Is) / 64;
+    const uint8_t* dseg = rec + (item < a.k ? a.d_off : a.d_off_shared) + (size_t)SEG * ngi * ot;
+    const uint8_t* dcodes = dseg + (size_t)lane * 16;
+    const uint8_t* dsb = dseg + NW * 1024 + (size_t)lane * 4;
 
     // h of (t, j), blocks [2ga, 2gb): loaded before the weights
     const int nb = 2 * (gb - ga);
@@ -761,14 +762,14 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     // a ring of DD groups in flight per wave (every group at once when a wave
     // has at most kDnRing groups)
     constexpr int DD = MAXG > kDnRing ? kDnRing : MAXG;
-    RowT W[2 * DD];
+    u32x4 W[DD][NW];
     uint32_t SB[DD];
 #pragma unroll
     for (int q = 0; q < DD; ++q) {
         const int g = min(g0 + q, gb - 1);  // past this wave's range: re-read a valid group
-        W[2 * q] = ldg_nt((const RowT*)(dblk + blk * (2 * g)));
-        W[2 * q + 1] = ldg_nt((const RowT*)(dblk + blk * (2 * g + 1)));
-        SB[q] = ldg_nt((const uint32_t*)(dsb + (size_t)12 * H * g));
+#pragma unroll
+        for (int c = 0; c < NW; ++c) W[q][c] = ldg_nt((const u32x4*)(dcodes + (size_t)g * SEG + c * 1024));
+        SB[q] = ldg_nt((const uint32_t*)(dsb + (size_t)g * SEG));
         __builtin_amdgcn_sched_barrier(0);  // keep issue order = consumption order
     }
 #pragma unroll
@@ -793,22 +794,25 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int lb = 2 * (g - ga) + half;  // local h block
-                const RowT wv = W[2 * slot + half];
                 const uint32_t* hc = sp + (size_t)lb * 16 * kHParts;
                 float a0 = 0.0f, a1 = 0.0f;
                 if constexpr (BITS == 4) {
+                    const u32x4 wv = W[slot][half];  // 32 nibbles: inputs 32 half .. of the group
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
+                        const uint32_t wm = wv[m];
 #pragma unroll
                         for (int p = 0; p < kHParts; ++p)
-                            dot_nib8(wv[m], hc + (m * kHParts + p) * 4, a0, a1);
+                            dot_nib8(wm, hc + (m * kHParts + p) * 4, a0, a1);
                     }
                 } else {
+                    const u32x4 wv = W[slot][0];  // 64 codes: dwords 2 half, 2 half + 1 hold this half
 #pragma unroll
                     for (int m = 0; m < 2; ++m) {
+                        const uint32_t wm = wv[2 * half + m];
 #pragma unroll
                         for (int p = 0; p < kHParts; ++p)
-                            dot_crumb16(wv[m], hc + (m * kHParts + p) * 8, a0, a1);
+                            dot_crumb16(wm, hc + (m * kHParts + p) * 8, a0, a1);
                     }
                 }
                 part = fmaf((a0 + a1) - sK[lb], sI[lb], part);
@@ -819,9 +823,9 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
         }
         if (q + DD < MAXG) {  // refill the slot just consumed
             const int gn = min(g0 + q + DD, gb - 1);
-            W[2 * slot] = ldg_nt((const RowT*)(dblk + blk * (2 * gn)));
-            W[2 * slot + 1] = ldg_nt((const RowT*)(dblk + blk * (2 * gn + 1)));
-            SB[slot] = ldg_nt((const uint32_t*)(dsb + (size_t)12 * H * gn));
+#pragma unroll
+            for (int c = 0; c < NW; ++c) W[slot][c] = ldg_nt((const u32x4*)(dcodes + (size_t)gn * SEG + c * 1024));
+            SB[slot] = ldg_nt((const uint32_t*)(dsb + (size_t)gn * SEG));
         }
         __builtin_amdgcn_sched_barrier(0);
     }

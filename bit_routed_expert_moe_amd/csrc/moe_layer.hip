@@ -65,8 +65,8 @@ struct moe_layer {
     size_t rec_bytes;
     size_t shared_rec_bytes;
     int bits;             // code width of the expert records: 4 or 2
-    size_t sb_off;        // scale/bias region of a routed record
-    size_t sb_off_shared; // ... and of the shared record
+    size_t d_off;         // down segments of a routed record (after its gate/up segments)
+    size_t d_off_shared;  // ... and of the shared record
     int NG;        // H / 64
     int blk_r;     // I / 32
     int blk_s;     // Is / 32
@@ -260,8 +260,8 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.shared = L->w.shared;
     a.rec_bytes = L->rec_bytes;
     a.bits = L->bits;
-    a.sb_off = L->sb_off;
-    a.sb_off_shared = L->sb_off_shared;
+    a.d_off = L->d_off;
+    a.d_off_shared = L->d_off_shared;
     if (L->cache.n_slots) {
         a.slots = L->w.slots;
         a.slot_ids = (const int32_t*)(ws + o.slot_ids);
@@ -312,8 +312,8 @@ PrefillArgs prefill_args(const moe_layer* L, const void* x, const int32_t* ids, 
     a.x16 = (uint16_t*)(ws + o.x16);
     a.x16b = (uint16_t*)(ws + o.x16b);
     a.bits = L->bits;
-    a.sb_off = L->sb_off;
-    a.sb_off_shared = L->sb_off_shared;
+    a.d_off = L->d_off;
+    a.d_off_shared = L->d_off_shared;
     a.xsum = (float*)(ws + o.pxsum);
     a.xinv = (float*)(ws + o.pxinv);
     a.pair_tok = (int32_t*)(ws + o.pair_tok);
@@ -627,8 +627,11 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     L->bits = d.bits == 2 ? 2 : 4;
     L->rec_bytes = moe_expert_record_bytes_bits(d.hidden, d.inter, L->bits);
     L->shared_rec_bytes = d.shared_inter ? moe_expert_record_bytes_bits(d.hidden, d.shared_inter, L->bits) : 0;
-    L->sb_off = (size_t)d.hidden * d.inter * L->bits * 3 / 8;  // G, U and D codes first
-    L->sb_off_shared = (size_t)d.hidden * d.shared_inter * L->bits * 3 / 8;
+    // gate/up segments first: (I/32) blocks x (H/64) groups, each segment the
+    // group's codes (64 rows x 64 inputs) and its 64 (scale, bias) pairs
+    const size_t seg = (size_t)64 * 64 * L->bits / 8 + 256;
+    L->d_off = (size_t)(d.inter / 32) * (d.hidden / 64) * seg;
+    L->d_off_shared = (size_t)(d.shared_inter / 32) * (d.hidden / 64) * seg;
     L->NG = d.hidden / 64;
     L->blk_r = d.inter / 32;
     L->blk_s = d.shared_inter / 32;

@@ -134,10 +134,6 @@ __device__ __forceinline__ uint32_t bload(__amdgpu_buffer_rsrc_t r, int voff, in
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
 }
 template <int AUX = 0>
-__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
-}
-template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
 }
@@ -510,14 +506,15 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
         // per-lane offsets (bytes): row 16*kq + n of each GU tile (codes and
         // scale/bias pair; one 16-byte load covers a 1 KB chunk of a tile per
         // wave), and the lane's activations; the rest of each address is
-        // uniform and goes in the scalar offset.  A 64-input group is two
-        // chunks of nibbles or one chunk of 2-bit codes.
+        // uniform and goes in the scalar offset.  A 64-input group's segment
+        // is two chunks of nibbles or one chunk of 2-bit codes, then the 64
+        // rows' (scale, bias) pairs.
         constexpr int NC = BITS == 4 ? 2 : 1;
-        const int blk = (BITS == 4 ? 48 : 24) * H;  // bytes per 32-row block
-        const int sbo = (int)(shared ? a.sb_off_shared : a.sb_off);
+        constexpr int SEG = NC * 1024 + 256;
+        const int tb = SEG * NG;  // bytes of a 32-row block's segments
         const int rl = 16 * kq + n;
-        const int wo[2] = {blk * (2 * gi) + rl * 16, blk * (2 * gi + 1) + rl * 16};
-        const int so[2] = {sbo + 12 * H * gi + rl * 4, sbo + 12 * H * gi + 4 * H + rl * 4};
+        const int wo[2] = {tb * (2 * gi) + rl * 16, tb * (2 * gi + 1) + rl * 16};
+        const int so[2] = {tb * (2 * gi) + NC * 1024 + rl * 4, tb * (2 * gi + 1) + NC * 1024 + rl * 4};
         const int xo = (max(s_tok[n], 0) * H + 8 * kq) * 2;
         const int xpart = a.T * H * 2;
         const Unpack up;
@@ -537,9 +534,9 @@ __global__ __launch_bounds__(kBlock) void k_gu_grouped(PrefillArgs a) {
             for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
-                    R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], live ? 1024 * NC * jg + 1024 * c : kPastEnd);
+                    R.W[t2][c] = bload4<kAuxNT>(rw, wo[t2], live ? SEG * jg + 1024 * c : kPastEnd);
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) R.SB[t2] = bload(rw, so[t2], live ? 256 * jg : kPastEnd);
+            for (int t2 = 0; t2 < 2; ++t2) R.SB[t2] = bload(rw, so[t2], live ? SEG * jg : kPastEnd);
         };
         auto compute = [&](const Regs& R, int jg) {
             const f32x4 xs = *(const f32x4*)&sX[jg * kTileRows + 4 * kq];
@@ -666,14 +663,16 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     const uint8_t* rec = shared ? a.shared : a.experts + (size_t)tl.x * a.rec_bytes;
     const __amdgpu_buffer_rsrc_t rw = rsrc(rec, shared ? a.rec_bytes_shared : a.rec_bytes);
     const __amdgpu_buffer_rsrc_t rh = rsrc(a.h16, (size_t)(a.P + a.T) * a.Imax * 2);
-    // lane row o0 + 64*hh + 16*kq + n: one 16-byte load covers 64 rows of a
-    // down chunk of nibbles (two 8-byte loads, of the group's two 32-input
-    // blocks, for 2-bit codes), one dword load their scale/bias pairs
-    constexpr int RB = BITS == 4 ? 16 : 8;       // bytes per row per 32-input block
-    const int blk = (BITS == 4 ? 48 : 24) * H;  // bytes per 32-row block of the record
-    const int rl = o0 + 16 * kq + n;
-    const int wo = (BITS == 4 ? 32 : 16) * H + rl * RB;
-    const int so = (int)(shared ? a.sb_off_shared : a.sb_off) + 8 * H + rl * 4;
+    // lane row o0 + 64*hh + 16*kq + n, row 16*kq + n of output tile
+    // o0/64 + hh: one 16-byte load covers 64 rows of a 1 KB chunk of a down
+    // segment (32 nibbles per row, or the group's 64 2-bit codes), one dword
+    // load their scale/bias pairs
+    constexpr int NC = BITS == 4 ? 2 : 1;
+    constexpr int SEG = NC * 1024 + 256;
+    const int ts = SEG * NGe;  // bytes of an output tile's segments
+    const int dof = (int)(shared ? a.d_off_shared : a.d_off) + ts * (o0 / 64);
+    const int wo = dof + (16 * kq + n) * 16;
+    const int so = dof + NC * 1024 + (16 * kq + n) * 4;
     const int ho = (max(s_row[n], 0) * a.Imax + 8 * kq) * 2;
     const Unpack up;
     f32x4 acc[kNtDn];
@@ -681,7 +680,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
     for (int nt = 0; nt < kNtDn; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
     struct Regs {
         u32x4 A[2];
-        u32x4 W[2][2];  // [half][chunk] (2-bit: the two blocks' 8 bytes in W[half][0])
+        u32x4 W[2][2];  // [output tile][chunk] (2-bit: the group's 16 bytes in W[tile][0])
         uint32_t SB[2];
     };
     auto load = [&](Regs& R, int jg) {  // jg >= NGe: a refill past the end
@@ -691,16 +690,10 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(PrefillArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const bool live = jg < NGe && (hh == 0 || hi_ok);
-            if (BITS == 4) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    R.W[hh][c] = bload4<kAuxNT>(rw, wo, live ? blk * (2 * jg + c) + 1024 * hh : kPastEnd);
-            } else {
-                const u32x2 b0 = bload2<kAuxNT>(rw, wo, live ? blk * (2 * jg) + 512 * hh : kPastEnd);
-                const u32x2 b1 = bload2<kAuxNT>(rw, wo, live ? blk * (2 * jg + 1) + 512 * hh : kPastEnd);
-                R.W[hh][0] = u32x4{b0[0], b0[1], b1[0], b1[1]};
-            }
-            R.SB[hh] = bload(rw, so, live ? 12 * H * jg + 256 * hh : kPastEnd);
+            for (int c = 0; c < NC; ++c)
+                R.W[hh][c] = bload4<kAuxNT>(rw, wo, live ? ts * hh + SEG * jg + 1024 * c : kPastEnd);
+            R.SB[hh] = bload(rw, so, live ? ts * hh + SEG * jg : kPastEnd);
         }
     };
     auto compute = [&](const Regs& R, int jg) {

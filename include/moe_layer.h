@@ -36,32 +36,31 @@
  * Packed expert record (hidden H, intermediate I; H and I multiples of 64).
  * Matrices G (gate) and U (up) are [I][H] with input dim H; D (down) is [H][I]
  * with input dim I.  Inputs are quantised in groups of 64 consecutive inputs:
- * W = scale * q + bias, q in 0..15.  Within a 16-byte run of 32 inputs, input
- * 2m is the low nibble of byte m and input 2m+1 the high nibble.
- *   nibble region (3*H*I/2 bytes): I/32 blocks of 48*H bytes; block b covers
- *   rows i in [32b, 32b+32):
- *     +0     GU tile: for chunk c < H/32, for tile row r < 64: 16 bytes holding
- *            inputs [32c, 32c+32) of G row 32b+r (r < 32) or U row 32b+r-32
- *     +32*H  D block: for output row o < H: 16 bytes = D[o][32b .. 32b+32)
- *   scale/bias region (at 3*H*I/2; I/64 slabs of 12*H bytes); slab g covers
- *   rows/inputs i in [64g, 64g+64):
- *     +0     (scale, bias) fp16 pairs of GU tile 2g, [group h < H/64][row r < 64]
- *     +4*H   the same for GU tile 2g+1
- *     +8*H   (scale, bias) of D[o][64g .. 64g+64) for o < H
+ * W = scale * q + bias, q in 0..15, one fp16 (scale, bias) pair per row and
+ * group.  The record is a sequence of 3*H*I/4096 segments of 2304 bytes; a
+ * segment covers one tile of 64 rows x 64 inputs:
+ *     +0     codes: [half c < 2][row r < 64][16 bytes], the 16 bytes holding
+ *            inputs [32c, 32c+32) of the tile's row r, input 2m of those 32
+ *            in the low nibble of byte m and 2m+1 in its high nibble
+ *     +2048  (scale, bias) fp16 pairs of the 64 rows, in row order
+ *   gate/up segments first: segment b*(H/64) + g (b < I/32, g < H/64) holds
+ *     inputs [64g, 64g+64) of tile rows r < 32 = G row 32b+r and r >= 32 =
+ *     U row 32b+r-32
+ *   down segments next: segment (I/32)*(H/64) + t*(I/64) + g (t < H/64,
+ *     g < I/64) holds inputs [64g, 64g+64) of D rows 64t+r
  *   Record size: 27*H*I/16 bytes (0.5625 bytes per weight).  A layer's routed
  *   records lie back to back: record e at experts + e * moe_expert_record_bytes.
- * 2-bit records (desc.bits = 2): W = scale * q + bias, q in 0..3, the same
- * groups and the same scale/bias slabs; a 16-byte run holds 64 inputs, input
- * 4m+j in bits [2j, 2j+2) of byte m.  The 4-bit format with half the code
- * bytes (Colibri README, "What's implemented", names packed int2 among its CPU
- * quantisation kernels; the layout here is our own).
- *   code region (3*H*I/4 bytes): I/32 blocks of 24*H bytes:
- *     +0     GU tile: for chunk c < H/64, for tile row r < 64: 16 bytes holding
- *            inputs [64c, 64c+64) of G row 32b+r (r < 32) or U row 32b+r-32
- *     +16*H  D block: for output row o < H: 8 bytes = D[o][32b .. 32b+32)
- *   scale/bias region at 3*H*I/4, laid out as above.
- *   Record size: 15*H*I/16 bytes (0.3125 bytes per weight);
- *   moe_expert_record_bytes_bits gives either size.
+ *   Keeping each group's pairs beside its codes makes every 64-input step of
+ *   a weight stream one contiguous 2.25 KB read (the gate, up and down
+ *   matrices of an expert stored next to each other: Inferno README, "Model",
+ *   ExpertPack).
+ * 2-bit records (desc.bits = 2): W = scale * q + bias, q in 0..3; segments of
+ * 1280 bytes: codes [row r < 64][16 bytes] holding the tile's 64 inputs of row
+ * r, input 4m+j in bits [2j, 2j+2) of byte m, then the 64 pairs at +1024.
+ * (Colibri README, "What's implemented", names packed int2 among its CPU
+ * quantisation kernels; the layout here is our own.)  Record size:
+ * 15*H*I/16 bytes (0.3125 bytes per weight); moe_expert_record_bytes_bits
+ * gives either size.
  * Router: rows q[E][H] int8, row-major, and one fp16 scale per row;
  *   logit_e = scale_e * sum_h q[e][h] * x_h.
  */

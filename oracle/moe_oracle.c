@@ -33,32 +33,23 @@
  * tests/test_oracle_pins.py except where it says "parity unpinned".
  *
  * Packed expert record (hidden H, intermediate I, both multiples of 64).
- * G and U are [I][H] (input dim H), D is [H][I] (input dim I).  Within a
- * 16-byte run of 32 inputs, input 2m is the low nibble of byte m and input
- * 2m+1 its high nibble.
+ * G and U are [I][H] (input dim H), D is [H][I] (input dim I).  A weight is
+ * W = scale * q + bias, q the code (0..15 for 4-bit records, 0..3 for 2-bit),
+ * with one fp16 (scale, bias) pair per row and per group of 64 inputs.
  *
- *   nibble region, 3*H*I/2 bytes, I/32 blocks of 48*H bytes; block b holds
- *   rows i in [32b, 32b+32):
- *     +0      GU tile: for chunk c < H/32, for tile row r < 64: 16 bytes =
- *             inputs [32c, 32c+32) of G row 32b+r (r < 32) or U row
- *             32b+r-32 (r >= 32)
- *     +32*H   D block: for output row o < H: 16 bytes = D[o][32b .. 32b+32)
- *   scale/bias region at 3*H*I/2, I/64 slabs of 12*H bytes; slab g covers
- *   i in [64g, 64g+64):
- *     +0      (scale, bias) fp16 pairs of GU tile 2g:   [group h < H/64][row r < 64]
- *     +4*H    (scale, bias) fp16 pairs of GU tile 2g+1: same order
- *     +8*H    (scale, bias) fp16 pairs of D[o][64g .. 64g+64) for o < H
- *   A weight is  W = scale * q + bias,  q the nibble in 0..15.
- *
- * The 2-bit variant (our own format: the pages name 2-bit models but define
- * no 2-bit container) keeps the structure with 64 inputs per 16-byte run,
- * input 4m+j in bits [2j, 2j+2) of byte m, q in 0..3:
- *   code region, 3*H*I/4 bytes, I/32 blocks of 24*H bytes; block b holds
- *   rows i in [32b, 32b+32):
- *     +0      GU tile: for chunk c < H/64, for tile row r < 64: 16 bytes =
- *             inputs [64c, 64c+64) of G row 32b+r (r < 32) or U row 32b+r-32
- *     +16*H   D block: for output row o < H: 8 bytes = D[o][32b .. 32b+32)
- *   scale/bias region at 3*H*I/4, laid out as for 4 bits.
+ * The record is a sequence of 3*H*I/4096 segments.  A segment covers one tile
+ * of 64 rows x 64 inputs: its codes (2048 bytes at 4 bits, 1024 at 2 bits),
+ * then 256 bytes of (scale, bias) pairs, one per row r < 64, in row order.
+ *   gate/up segments first: segment b*(H/64) + g, for b < I/32, g < H/64:
+ *     tile row r < 32 is G row 32b+r, r >= 32 is U row 32b+r-32; inputs
+ *     [64g, 64g+64) of H
+ *   down segments next: segment (I/32)*(H/64) + t*(I/64) + g, for t < H/64,
+ *     g < I/64: tile row r is D row 64t+r; inputs [64g, 64g+64) of I
+ * Codes of a segment, 4-bit: [half c < 2][row r < 64][16 bytes], the 16 bytes
+ * holding inputs [64g+32c, 64g+32c+32) of row r, input 2m of those 32 in the
+ * low nibble of byte m and 2m+1 in its high nibble.  2-bit (our own format:
+ * the pages name 2-bit models but define no 2-bit container): [row r < 64][16
+ * bytes] holding inputs [64g, 64g+64), input 4m+j in bits [2j, 2j+2) of byte m.
  */
 #include <math.h>
 #include <stddef.h>
@@ -128,20 +119,33 @@ static int nibble_at(const uint8_t *rec, size_t byte_off, int elem)
     return (elem & 1) ? (byte >> 4) : (byte & 0x0F);
 }
 
-static size_t sb_region(int H, int I) { return (size_t)3 * H * I / 2; }
+/* bytes of a segment's codes, and of a whole segment (codes + 64 pairs) */
+static size_t seg_codes(int bits) { return bits == 2 ? 1024 : 2048; }
+static size_t seg_bytes(int bits) { return seg_codes(bits) + 256; }
+
+/* start of gate/up segment (b, g) and of down segment (t, g) */
+static size_t gu_segment(int bits, int H, int b, int g)
+{
+    return ((size_t)b * (H / 64) + g) * seg_bytes(bits);
+}
+
+static size_t d_segment(int bits, int H, int I, int t, int g)
+{
+    return ((size_t)(I / 32) * (H / 64) + (size_t)t * (I / 64) + g) * seg_bytes(bits);
+}
 
 /* quantised value of gate (which = 0) or up (which = 1) at row i, input k */
 static int q_gate_up(const uint8_t *rec, int H, int which, int i, int k)
 {
-    int b = i / 32, r = i % 32 + 32 * which, c = k / 32, e = k % 32;
-    size_t off = (size_t)48 * H * b + (size_t)c * 1024 + (size_t)r * 16 + e / 2;
+    int b = i / 32, r = i % 32 + 32 * which, g = k / 64, c = (k % 64) / 32, e = k % 32;
+    size_t off = gu_segment(4, H, b, g) + (size_t)c * 1024 + (size_t)r * 16 + e / 2;
     return nibble_at(rec, off, e);
 }
 
-static int q_down(const uint8_t *rec, int H, int o, int i)
+static int q_down(const uint8_t *rec, int H, int I, int o, int i)
 {
-    int b = i / 32, e = i % 32;
-    size_t off = (size_t)48 * H * b + (size_t)32 * H + (size_t)o * 16 + e / 2;
+    int t = o / 64, r = o % 64, g = i / 64, c = (i % 64) / 32, e = i % 32;
+    size_t off = d_segment(4, H, I, t, g) + (size_t)c * 1024 + (size_t)r * 16 + e / 2;
     return nibble_at(rec, off, e);
 }
 
@@ -153,15 +157,15 @@ static int crumb_at(const uint8_t *rec, size_t byte_off, int elem)
 
 static int q_gate_up2(const uint8_t *rec, int H, int which, int i, int k)
 {
-    int b = i / 32, r = i % 32 + 32 * which, c = k / 64, e = k % 64;
-    size_t off = (size_t)24 * H * b + (size_t)c * 1024 + (size_t)r * 16 + e / 4;
+    int b = i / 32, r = i % 32 + 32 * which, g = k / 64, e = k % 64;
+    size_t off = gu_segment(2, H, b, g) + (size_t)r * 16 + e / 4;
     return crumb_at(rec, off, e);
 }
 
-static int q_down2(const uint8_t *rec, int H, int o, int i)
+static int q_down2(const uint8_t *rec, int H, int I, int o, int i)
 {
-    int b = i / 32, e = i % 32;
-    size_t off = (size_t)24 * H * b + (size_t)16 * H + (size_t)o * 8 + e / 4;
+    int t = o / 64, r = o % 64, g = i / 64, e = i % 64;
+    size_t off = d_segment(2, H, I, t, g) + (size_t)r * 16 + e / 4;
     return crumb_at(rec, off, e);
 }
 
@@ -171,9 +175,9 @@ static int q_gu(int bits, const uint8_t *rec, int H, int which, int i, int k)
     return bits == 2 ? q_gate_up2(rec, H, which, i, k) : q_gate_up(rec, H, which, i, k);
 }
 
-static int q_d(int bits, const uint8_t *rec, int H, int o, int i)
+static int q_d(int bits, const uint8_t *rec, int H, int I, int o, int i)
 {
-    return bits == 2 ? q_down2(rec, H, o, i) : q_down(rec, H, o, i);
+    return bits == 2 ? q_down2(rec, H, I, o, i) : q_down(rec, H, I, o, i);
 }
 
 static void sb_read(const uint8_t *rec, size_t off, double *s, double *bias)
@@ -186,27 +190,24 @@ static void sb_read(const uint8_t *rec, size_t off, double *s, double *bias)
 }
 
 /* scale/bias of gate (which = 0) or up (which = 1) row i, input group h */
-static void sb_gate_up(const uint8_t *rec, size_t sb0, int H, int which, int i, int h,
+static void sb_gate_up(int bits, const uint8_t *rec, int H, int which, int i, int h,
                        double *s, double *bias)
 {
-    int g = i / 64, tile = (i / 32) % 2, r = i % 32 + 32 * which;
-    size_t off = sb0 + (size_t)12 * H * g + (size_t)4 * H * tile
-               + (size_t)h * 256 + (size_t)r * 4;
+    int b = i / 32, r = i % 32 + 32 * which;
+    size_t off = gu_segment(bits, H, b, h) + seg_codes(bits) + (size_t)r * 4;
     sb_read(rec, off, s, bias);
 }
 
-static void sb_down(const uint8_t *rec, size_t sb0, int H, int o, int g, double *s, double *bias)
+/* scale/bias of down row o, input group g */
+static void sb_down(int bits, const uint8_t *rec, int H, int I, int o, int g, double *s, double *bias)
 {
-    size_t off = sb0 + (size_t)12 * H * g + (size_t)8 * H + (size_t)o * 4;
+    size_t off = d_segment(bits, H, I, o / 64, g) + seg_codes(bits) + (size_t)(o % 64) * 4;
     sb_read(rec, off, s, bias);
 }
-
-/* start of the scale/bias region: after 3*H*I*bits/8 code bytes */
-static size_t sb_start(int bits, int H, int I) { return bits == 2 ? sb_region(H, I) / 2 : sb_region(H, I); }
 
 size_t oracle_record_bytes_bits(int bits, int H, int I)
 {
-    return sb_start(bits, H, I) + (size_t)(I / 64) * 12 * H;
+    return (size_t)3 * (H / 64) * (I / 64) * seg_bytes(bits);
 }
 
 size_t oracle_record_bytes(int H, int I) { return oracle_record_bytes_bits(4, H, I); }
@@ -218,18 +219,17 @@ void oracle_dequant_record_bits(int bits, int H, int I, const uint8_t *rec, doub
                                 double *D)
 {
     double s, bias;
-    const size_t sb0 = sb_start(bits, H, I);
     for (int i = 0; i < I; ++i)
         for (int k = 0; k < H; ++k) {
-            sb_gate_up(rec, sb0, H, 0, i, k / 64, &s, &bias);
+            sb_gate_up(bits, rec, H, 0, i, k / 64, &s, &bias);
             G[(size_t)i * H + k] = s * q_gu(bits, rec, H, 0, i, k) + bias;
-            sb_gate_up(rec, sb0, H, 1, i, k / 64, &s, &bias);
+            sb_gate_up(bits, rec, H, 1, i, k / 64, &s, &bias);
             U[(size_t)i * H + k] = s * q_gu(bits, rec, H, 1, i, k) + bias;
         }
     for (int o = 0; o < H; ++o)
         for (int i = 0; i < I; ++i) {
-            sb_down(rec, sb0, H, o, i / 64, &s, &bias);
-            D[(size_t)o * I + i] = s * q_d(bits, rec, H, o, i) + bias;
+            sb_down(bits, rec, H, I, o, i / 64, &s, &bias);
+            D[(size_t)o * I + i] = s * q_d(bits, rec, H, I, o, i) + bias;
         }
 }
 
@@ -331,13 +331,12 @@ void oracle_expert_ffn_bits(int bits, int H, int I, const uint8_t *rec, const do
                             double *y, double *g_out, double *u_out, double *h_out)
 {
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
-    const size_t sb0 = sb_start(bits, H, I);
     #pragma omp parallel for schedule(static)
     for (int i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0, sg, bg, su, bu;
         for (int grp = 0; grp < H / 64; ++grp) {
-            sb_gate_up(rec, sb0, H, 0, i, grp, &sg, &bg);
-            sb_gate_up(rec, sb0, H, 1, i, grp, &su, &bu);
+            sb_gate_up(bits, rec, H, 0, i, grp, &sg, &bg);
+            sb_gate_up(bits, rec, H, 1, i, grp, &su, &bu);
             for (int k = 64 * grp; k < 64 * grp + 64; ++k) {
                 g += (sg * q_gu(bits, rec, H, 0, i, k) + bg) * x[k];
                 u += (su * q_gu(bits, rec, H, 1, i, k) + bu) * x[k];
@@ -352,9 +351,9 @@ void oracle_expert_ffn_bits(int bits, int H, int I, const uint8_t *rec, const do
     for (int o = 0; o < H; ++o) {
         double acc = 0.0, s, bias;
         for (int grp = 0; grp < I / 64; ++grp) {
-            sb_down(rec, sb0, H, o, grp, &s, &bias);
+            sb_down(bits, rec, H, I, o, grp, &s, &bias);
             for (int i = 64 * grp; i < 64 * grp + 64; ++i)
-                acc += (s * q_d(bits, rec, H, o, i) + bias) * h[i];
+                acc += (s * q_d(bits, rec, H, I, o, i) + bias) * h[i];
         }
         y[o] = acc;
     }

@@ -21,7 +21,7 @@ Stream keys: ``key(seed, layer, kind, index[, attempt])`` folds each part p as
 Value recipes (every float goes double -> float32 -> target type, each step
 round-to-nearest-even; the double arithmetic is one multiply then one add, no
 fused multiply-add):
-  nibble bytes     little-endian bytes of out_i: byte p = byte (p & 7) of out_{p >> 3}
+  code bytes       little-endian bytes of out_i: byte p = byte (p & 7) of out_{p >> 3}
   scale s          fp16(fp32(1e-3 + 9e-3 * U))          U = (out >> 11) * 2^-53
   bias  b          fp16(fp32(-8e-3 * U))
   router int8      ((out >> 32) mod 255) - 127
@@ -111,13 +111,22 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# expert records: a nibble region followed by a region of (scale, bias) fp16
-# pairs.  The generator only needs these two region sizes; which group a pair
-# belongs to is the layout's business, not the generator's.
+# expert records: a sequence of equal segments, each SEGMENT_CODE_BYTES of
+# weight codes followed by 256 bytes (64 pairs) of (scale, bias) fp16 pairs.
+# The code stream fills the code parts in order and the pair stream the pair
+# parts; which weights a code or a pair belongs to is the layout's business,
+# not the generator's.
 # ---------------------------------------------------------------------------
+PAIR_PART_BYTES = 256
+
+
+def segment_code_bytes(bits: int = 4) -> int:
+    """Code bytes per segment: 64 rows x 64 inputs of `bits`-wide codes."""
+    return 64 * 64 * bits // 8
+
 
 def nibble_region_bytes(hidden: int, inter: int, bits: int = 4) -> int:
-    """Bytes of the code region (4-bit nibbles, or 2-bit codes)."""
+    """Code bytes of a record (4-bit nibbles, or 2-bit codes), all segments."""
     return 3 * hidden * inter * bits // 8
 
 
@@ -134,15 +143,19 @@ def expert_record(seed: int, layer: int, expert: int, hidden: int, inter: int,
     """One packed expert record (uint8), generated on the CPU."""
     nb = nibble_region_bytes(hidden, inter, bits)
     npairs = sb_pairs(hidden, inter)
-    out = np.empty(nb + 4 * npairs, dtype=np.uint8)
-    out[:nb] = stream(key(seed, layer, KIND_NIBBLE, expert), nb // 8).view(np.uint8)
+    codes = stream(key(seed, layer, KIND_NIBBLE, expert), nb // 8).view(np.uint8)
     s = 1e-3 + 9e-3 * unit_uniform(stream(key(seed, layer, KIND_SCALE, expert), npairs))
     b = -8e-3 * unit_uniform(stream(key(seed, layer, KIND_BIAS, expert), npairs))
     sb = np.empty(2 * npairs, dtype=np.uint16)
     sb[0::2] = to_f16_bits(s)
     sb[1::2] = to_f16_bits(b)
-    out[nb:] = sb.view(np.uint8)
-    return out
+    cb = segment_code_bytes(bits)
+    nseg = nb // cb
+    assert nseg * PAIR_PART_BYTES == 4 * npairs
+    out = np.empty((nseg, cb + PAIR_PART_BYTES), dtype=np.uint8)
+    out[:, :cb] = codes.reshape(nseg, cb)
+    out[:, cb:] = sb.view(np.uint8).reshape(nseg, PAIR_PART_BYTES)
+    return out.reshape(-1)
 
 
 def router(seed: int, layer: int, n_experts: int, hidden: int):

@@ -4,17 +4,16 @@ Written as the inverse of the record layout with array reshapes, independently
 of the oracle's scalar indexing, so that a decoding mistake in either one shows
 up as a mismatch against the dense source matrices.
 
-Layout (hidden H, intermediate I): G, U are [I][H], D is [H][I].
-  nibble region: for each block b of 32 rows i: the GU tile [H/32 chunks][64
-  tile rows (32 G rows, then the same 32 U rows)][16 bytes], then the D block
-  [H output rows][16 bytes of D[o][32b:32b+32]].  Byte m of a 16-byte run holds
-  input 2m in the low nibble and 2m+1 in the high nibble.
-  The 2-bit variant packs 64 inputs per 16-byte run (input 4m+j in bits
-  [2j, 2j+2) of byte m): GU tiles [H/64 chunks][64 rows][16 bytes], D blocks
-  [H rows][8 bytes].
-  scale/bias region: for each slab g of 64 rows i: GU tile 2g pairs
-  [H/64 groups][64 tile rows], GU tile 2g+1 pairs, then D pairs [H] for input
-  group g.  Each pair is (scale fp16, bias fp16).
+Layout (hidden H, intermediate I): G, U are [I][H], D is [H][I].  The record
+is a sequence of segments, one per 64-row x 64-input tile: the tile's codes,
+then its 64 (scale fp16, bias fp16) pairs in row order.
+  gate/up tiles first, [block b of 32 rows of I][input group g of H]: the
+  tile's rows are the 32 G rows of the block, then the same 32 U rows.
+  down tiles next, [64-row tile t of H][input group g of I].
+  Codes of a tile: [runs of 16 bytes][64 rows][16 bytes]: 4-bit records have
+  two runs of 32 inputs (byte m holds input 2m in the low nibble, 2m+1 in the
+  high nibble), 2-bit records one run of 64 inputs (input 4m+j in bits
+  [2j, 2j+2) of byte m).
 """
 from __future__ import annotations
 
@@ -32,30 +31,36 @@ def pack_crumbs(q: np.ndarray) -> np.ndarray:
     return (q[..., 0::4] | (q[..., 1::4] << 2) | (q[..., 2::4] << 4) | (q[..., 3::4] << 6)).astype(np.uint8)
 
 
+def _segments(q: np.ndarray, s_bits: np.ndarray, b_bits: np.ndarray, bits: int) -> np.ndarray:
+    """q [n][64][K] codes of n tile rows-sets (64 rows each), s/b [n][64][K/64]
+    fp16 bits -> [n][K/64][segment bytes] (codes of each 64-input tile, then its
+    pairs)."""
+    n, _, K = q.shape
+    per_run = 128 // bits                                        # inputs per 16-byte run
+    pack = pack_nibbles if bits == 4 else pack_crumbs
+    t = q.reshape(n, 64, K // 64, 64 // per_run, per_run)        # [n][row][group][run][input]
+    t = t.transpose(0, 2, 3, 1, 4)                               # [n][group][run][row][input]
+    codes = pack(t).reshape(n, K // 64, -1)                      # [n][group][runs*64*16]
+    pairs = np.stack([s_bits.transpose(0, 2, 1), b_bits.transpose(0, 2, 1)], axis=-1)  # [n][group][row][2]
+    pairs = np.ascontiguousarray(pairs, dtype=np.uint16).view(np.uint8).reshape(n, K // 64, 256)
+    return np.concatenate([codes, pairs], axis=-1)
+
+
 def pack_record(qG, qU, qD, sG, bG, sU, bU, sD, bD, bits: int = 4) -> np.ndarray:
     """q*: int arrays 0..2^bits-1 (G, U [I][H]; D [H][I]); s*, b*: fp16 bit
-    arrays (G, U [I][H/64]; D [H][I/64]).  bits 4: 32 inputs per 16-byte run;
-    bits 2: 64.  Returns the record as uint8."""
+    arrays (G, U [I][H/64]; D [H][I/64]).  Returns the record as uint8."""
     I, H = qG.shape
     assert qU.shape == (I, H) and qD.shape == (H, I)
     assert H % 64 == 0 and I % 64 == 0 and bits in (2, 4)
-    per_run = 128 // bits           # inputs per 16-byte run
-    pack = pack_nibbles if bits == 4 else pack_crumbs
-    parts = []
-    for b in range(I // 32):
-        rows = np.concatenate([qG[32 * b:32 * b + 32], qU[32 * b:32 * b + 32]], axis=0)
-        tile = rows.reshape(64, H // per_run, per_run).transpose(1, 0, 2)   # [chunk][row][run]
-        parts.append(pack(tile).reshape(-1))
-        parts.append(pack(qD[:, 32 * b:32 * b + 32]).reshape(-1))           # [o][32 inputs]
-    for g in range(I // 64):
-        for t in (2 * g, 2 * g + 1):
-            s_rows = np.concatenate([sG[32 * t:32 * t + 32], sU[32 * t:32 * t + 32]], axis=0)
-            b_rows = np.concatenate([bG[32 * t:32 * t + 32], bU[32 * t:32 * t + 32]], axis=0)
-            pairs = np.stack([s_rows.T, b_rows.T], axis=-1)               # [group][row][2]
-            parts.append(np.ascontiguousarray(pairs, dtype=np.uint16).reshape(-1).view(np.uint8))
-        pairs = np.stack([sD[:, g], bD[:, g]], axis=-1)                    # [o][2]
-        parts.append(np.ascontiguousarray(pairs, dtype=np.uint16).reshape(-1).view(np.uint8))
-    return np.concatenate(parts)
+    nb = I // 32
+    gu_q = np.concatenate([qG.reshape(nb, 32, H), qU.reshape(nb, 32, H)], axis=1)          # [b][row][H]
+    gu_s = np.concatenate([sG.reshape(nb, 32, H // 64), sU.reshape(nb, 32, H // 64)], axis=1)
+    gu_b = np.concatenate([bG.reshape(nb, 32, H // 64), bU.reshape(nb, 32, H // 64)], axis=1)
+    nt = H // 64
+    d_q = qD.reshape(nt, 64, I)                                                              # [t][row][I]
+    d_s, d_b = sD.reshape(nt, 64, I // 64), bD.reshape(nt, 64, I // 64)
+    return np.concatenate([_segments(gu_q, gu_s, gu_b, bits).reshape(-1),
+                           _segments(d_q, d_s, d_b, bits).reshape(-1)])
 
 
 def dense(q: np.ndarray, s_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:

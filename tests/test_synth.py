@@ -26,18 +26,43 @@ def test_record_regions_and_ranges():
     rec = synth.expert_record(0xB17E0001, 0, 5, H, I)
     assert rec.size == synth.record_bytes(H, I) == 3 * H * I * 9 // 16
     nb = synth.nibble_region_bytes(H, I)
-    nib = np.concatenate([rec[:nb] & 15, rec[:nb] >> 4])
+    cb = synth.segment_code_bytes(4)
+    segs = rec.reshape(-1, cb + synth.PAIR_PART_BYTES)
+    assert segs.shape[0] * cb == nb
+    codes = segs[:, :cb].reshape(-1)
+    nib = np.concatenate([codes & 15, codes >> 4])
     counts = np.bincount(nib, minlength=16)
     exp = nib.size / 16
     chi2 = float(((counts - exp) ** 2 / exp).sum())
     assert chi2 < 50, chi2  # 15 dof
-    sb = rec[nb:].view(np.uint16).view(np.float16).astype(np.float64)
+    sb = np.ascontiguousarray(segs[:, cb:]).reshape(-1).view(np.uint16).view(np.float16).astype(np.float64)
     s, b = sb[0::2], sb[1::2]
     assert s.min() >= float(np.float16(1e-3)) and s.max() <= float(np.float16(1e-2))
     assert b.min() >= float(np.float16(-8e-3)) and b.max() <= 0.0
     # biases that land in the fp16 subnormal range: about 6.1e-5 / 8e-3 of them
     frac = np.mean(np.abs(b) < 2.0 ** -14)
     assert 0.003 < frac < 0.013, frac
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_record_segments_hold_the_two_streams_in_order(bits):
+    """The code stream fills each segment's code part in order and the pair
+    stream its pair part: re-reading the parts in segment order gives the two
+    counter streams back (code bytes are the little-endian bytes of the
+    stream's words)."""
+    H, I, seed, layer, e = 128, 64, 11, 2, 3
+    rec = synth.expert_record(seed, layer, e, H, I, bits)
+    cb = synth.segment_code_bytes(bits)
+    assert cb == 2048 // (4 // bits)
+    segs = rec.reshape(-1, cb + 256)
+    assert segs.shape[0] == 3 * H * I // 4096
+    nb = synth.nibble_region_bytes(H, I, bits)
+    words = synth.stream(synth.key(seed, layer, synth.KIND_NIBBLE, e), nb // 8)
+    assert np.array_equal(segs[:, :cb].reshape(-1), words.view(np.uint8))
+    pairs = np.ascontiguousarray(segs[:, cb:]).reshape(-1).view(np.uint16)
+    npairs = synth.sb_pairs(H, I)
+    s = 1e-3 + 9e-3 * synth.unit_uniform(synth.stream(synth.key(seed, layer, synth.KIND_SCALE, e), npairs))
+    assert np.array_equal(pairs[0::2], synth.to_f16_bits(s))
 
 
 def test_records_differ_per_expert_and_layer():
