@@ -142,9 +142,15 @@ size_t moe_expert_record_bytes(int32_t hidden, int32_t inter);
  * 27*hidden*inter/16 or 15*hidden*inter/16; 0 for a bad shape or width. */
 size_t moe_expert_record_bytes_bits(int32_t hidden, int32_t inter, int32_t bits);
 
-/* Validates desc and weights and builds a handle.  The handle borrows the
- * weight pointers (they must outlive it) and owns only host metadata.
- * Launches nothing.  Errors: ARG, SHAPE, ALIGN, STATE, NOMEM. */
+/* Validates desc and weights and builds a handle for one MoE layer: its
+ * router, its routed experts' packed records and the shared expert's record
+ * (the per-layer expert set the engines on the pages keep: Inferno README,
+ * "Model" and "Memory Strategy"; TurboFieldfare article, "Arsitektur
+ * eksekusi yang mengurangi memori").  Fails at creation on any inconsistent
+ * shape or pointer rather than falling back to another path later (Colibri
+ * analysis report, section 6).  The handle borrows the weight pointers (they
+ * must outlive it) and owns only host metadata.  Launches nothing.
+ * Errors: ARG, SHAPE, ALIGN, STATE, NOMEM. */
 moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w,
                             moe_layer_t* out);
 moe_status moe_layer_destroy(moe_layer_t layer);
@@ -158,7 +164,11 @@ moe_status moe_layer_destroy(moe_layer_t layer);
  * must not share a workspace. */
 size_t moe_workspace_bytes(moe_layer_t layer, int32_t n_tokens);
 
-/* Router + exact top-k + gates for n_tokens tokens.
+/* Router + exact top-k + gates for n_tokens tokens: the 8-bit router on the
+ * token's activations (TurboFieldfare article, "Arsitektur eksekusi ...": the
+ * router is 8-bit; "Proses pembuatan token": it runs first, on resident
+ * weights) and the exact top-k (Inferno README, "Current Scope": exact top-8,
+ * no approximate routing), gates renormalised over the selection.
  *   x   device [T][H] in desc.act_dtype
  *   ids device [T][k] int32 out: selected experts, by logit descending, ties to
  *       the lower id
@@ -179,7 +189,11 @@ moe_status moe_route_topk(moe_layer_t layer, const void* x, int32_t n_tokens, in
  * bit for bit; within each path a token's result does not depend on the other
  * tokens of its call. */
 
-/* Per-expert SwiGLU outputs for the given selection.
+/* Per-expert SwiGLU outputs for the given selection: each selected expert's
+ * gate, up and down matrices dequantised on use from the affine group-64
+ * record (TurboFieldfare article, "Arsitektur eksekusi ...": MLX affine 4-bit
+ * group 64; Colibri README, "What's implemented": dequantisation on use),
+ * h = silu(G x) * (U x), y_e = D h, and the shared expert's the same way.
  *   ids        device [T][k] int32 (values outside [0, E) set the device error
  *              flag, see moe_poll_device_error, and make that slot's output NaN)
  *   expert_out device [T][k+1][H] fp32 out: row j < k is D_e silu(G_e x)*(U_e x)
@@ -188,8 +202,10 @@ moe_status moe_route_topk(moe_layer_t layer, const void* x, int32_t n_tokens, in
 moe_status moe_expert_ffn(moe_layer_t layer, const void* x, int32_t n_tokens,
                           const int32_t* ids, void* workspace, float* expert_out, void* stream);
 
-/* y[t] = sum_{j<k} w[t][j] * expert_out[t][j] + expert_out[t][k], summed in
- * that order.  y device [T][H] of y_dtype (MOE_F32 or MOE_BF16, round to
+/* The combine: y[t] = sum_{j<k} w[t][j] * expert_out[t][j] + expert_out[t][k]
+ * (routed outputs weighted by their gates, the shared expert's added with
+ * weight 1: TurboFieldfare article, "Proses pembuatan token", shared and
+ * routed outputs combined after the expert reads), summed in that order.  y device [T][H] of y_dtype (MOE_F32 or MOE_BF16, round to
  * nearest even).  Errors: ARG, ALIGN, HIP. */
 moe_status moe_combine(moe_layer_t layer, const float* expert_out, const float* w,
                        int32_t n_tokens, void* y, int32_t y_dtype, void* stream);
