@@ -141,3 +141,30 @@ def test_lookahead_hint_is_a_seeded_noisy_preview():
         assert abs(h[t].std() / x[t].std() - 1.0) < 0.05
     z = synth.lookahead_hint(5, 2, 3, x, 0.0)
     assert abs(np.corrcoef(x[0], z[0])[0, 1]) < 0.05
+
+
+def test_zipf_routing_histogram_matches_the_marginals(orc):
+    """GLM-scale decode routing (Zipf(1.1) over 256 experts, layer 0): the
+    oracle's selections over the first 2048 seeded steps, counted per
+    popularity rank, equal the stored dump (tests/golden/zipf_glm_layer0.json,
+    written by tests/golden/make_zipf_histogram.py) and follow the
+    Gumbel-top-8 inclusion probabilities: chi^2 per bin near 1 with every
+    rank's count within 4.5 standard deviations (binomial per rank)."""
+    import json
+    import os
+    import sys
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    sys.path.insert(0, here)
+    import make_zipf_histogram as mz
+    with open(os.path.join(here, "zipf_glm_layer0.json")) as f:
+        gold = json.load(f)
+    counts = np.array(mz.realised_rank_counts(orc, gold["steps"]))
+    assert counts.tolist() == gold["counts_by_rank"]
+    p = np.array(gold["expected_inclusion_by_rank"])
+    assert abs(p.sum() - 8.0) < 1e-4 and np.all(np.diff(p) < 0.002)  # 8 picks (stored to 6 digits); falls with rank
+    n = gold["steps"]
+    assert counts.sum() == 8 * n
+    z2 = (counts - n * p) ** 2 / (n * p * (1 - p))
+    chi2_per_bin = float(z2.sum() / p.size)
+    print(f"zipf histogram: chi2 per bin {chi2_per_bin:.3f}, max |z| {np.sqrt(z2.max()):.2f}")
+    assert 0.75 < chi2_per_bin < 1.35 and float(np.sqrt(z2.max())) < 4.5
