@@ -24,15 +24,6 @@ constexpr int kRouteSpinLimit = 1 << 14;
 // 2 % less per decode step at hidden 2816; at hidden 6144 the separate router
 // launch is 16 % faster).
 constexpr int kFusedMaxHidden = kGuSmallHMax;
-// The gate/up units read the logit words no earlier than this many ticks of
-// the 100 MHz device clock after they start: about the router units' span at
-// these sizes.  Reading the words before the router units have stored them
-// delays the hand-off by about 1.5 us (measured at hidden 2816: first read
-// from the start +4.6 % per step, after 1.6 us +1.6 %, after 1.9 us -3 %,
-// after 2.2 us -4 %, after 2.6 us -2 %, against a first read after the
-// workgroup's own share of the activation preparation).  It only sets when
-// the reads begin; what they read is unchanged.
-constexpr int kLogitPollDelayTicks = 220;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxHidden = 8192;
@@ -96,6 +87,8 @@ struct FfnArgs {
     uint32_t* flog;          // [T][E] logits stored bit-inverted, 0 = not yet written;
                              // k_down returns the words to 0 when set
     int spin_limit;          // polls before computing the logits locally (< 0: none)
+    int logit_delay;         // ticks of the 100 MHz device clock after its start before a
+                             // gate/up unit first reads the logit words (logit_delay_ticks)
     const float* bias;       // [E] selection bias (sigmoid gate) or nullptr
     float rscale;            // sigmoid gate: routed scaling factor
     int gate;                // 0 softmax, 1 sigmoid

@@ -551,7 +551,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
             float lv[Q] = {};
             if (wave == 0) {
                 // first read no earlier than the router units' span (bounded wait)
-                while (wall_clock64() - t_launch < (uint64_t)kLogitPollDelayTicks) __builtin_amdgcn_s_sleep(1);
+                while (wall_clock64() - t_launch < (uint64_t)a.logit_delay) __builtin_amdgcn_s_sleep(1);
                 fused_logits<Q, XP == 1>(a, t, lv);
             }
             e = topk_select_v<Q>(lv, a.E, a.k, j, s_topk, ids_out, w_out, GateFn{a.gate, a.bias, a.rscale});

@@ -395,6 +395,21 @@ hipError_t decode_finish(const FfnArgs& fa, int T, hipStream_t s) {
     return timed(K_DOWN, s, [&] { return launch_down(fa, T, s); });
 }
 
+// Routing inside the gate/up launch: when the gate/up units first read the
+// router units' logit words, in ticks of the 100 MHz device clock after they
+// start.  Reading the words before the router units have stored them delays
+// the hand-off by about 1 us (a re-read waits behind the weight streams that
+// have started meanwhile), and each tick past the router units' span is lost,
+// so the first read waits for about that span: 1.5 us plus 0.25 us per round
+// of 16-byte router loads per lane (hidden / 1024).  The router units run in
+// parallel, one row per wave, so the expert count hardly matters.  Measured
+// best delays: hidden 256 (32 experts) 160 ticks, 2816 (128) 220, 4096 (256
+// and 1024) 220-300; the rule gives 175, 225 and 250.
+int logit_delay_ticks(const moe_layer_desc& d) {
+    const int rounds = (d.hidden + 1023) / 1024;
+    return 150 + 25 * rounds;
+}
+
 moe_status check_call(const moe_layer* L, const void* x, int32_t T, const void* ws) {
     if (!L) return fail(MOE_ERR_ARG, "null layer handle");
     if (!x) return fail(MOE_ERR_ARG, "null activations");
@@ -778,6 +793,7 @@ moe_status moe_layer_forward(moe_layer_t L, const void* x, int32_t T, int32_t* i
         fa.rs = L->w.router_scale;
         fa.flog = (uint32_t*)(ws + o.flog);
         fa.spin_limit = L->spin_limit;
+        fa.logit_delay = logit_delay_ticks(L->d);
     }
     if ((e = decode_units(L, fa, T, 0, fa.n_units, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
     if ((e = decode_finish(fa, T, s)) != hipSuccess) return hip_fail(e, "down launch");
