@@ -54,14 +54,14 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 12422.49 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
+    # FETCH_SIZE 62484.99 KiB x 2.0 + WRITE_SIZE 90.06 KiB x 1.0 per launch
+    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128056478, "moe_kernels.hip", "dc3f5cbd064599bb"),
+    # FETCH_SIZE 12343.17 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
     # also runs the router)
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25484150, "moe_kernels.hip", "beb75e1d22d1bead"),
-    # 2-bit records: FETCH_SIZE 7019.34 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch
-    ("gemma_a4b_h2816_e128_l30/bits2", "k_gate_up"): (14418497, "moe_kernels.hip", "beb75e1d22d1bead"),
-    # FETCH_SIZE 1833636.30 KiB x 2.0 + WRITE_SIZE 5752.74 KiB x 1.0 per launch (mean over
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25320709, "moe_kernels.hip", "dc3f5cbd064599bb"),
+    # FETCH_SIZE 1833398.48 KiB x 2.0 + WRITE_SIZE 5756.57 KiB x 1.0 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761177948, "moe_prefill.hip", "abea37c5c198022b"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3760548011, "moe_prefill.hip", "974d53b7d0163dd0"),
 }
 
 

@@ -14,7 +14,7 @@ from _gpu_helpers import DeviceLayer, to_dev
 
 pytestmark = pytest.mark.gpu
 
-ARG, ALIGN = -1, -3
+ARG, SHAPE, ALIGN = -1, -2, -3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,3 +58,35 @@ def test_compute_calls_reject_bad_arguments(orc):
         assert torch.equal(a_, b_)
     want = dl.oracle(orc, xd)[0].tolist()
     assert got[0].cpu().numpy().tolist() == [want, want]
+
+
+def test_stack_rejects_layers_that_would_overlap():
+    """moe_stack_forward places layer l's ids/w at l*T*top_k and its x at
+    l*x_stride elements of one dtype: layers of different top_k or activation
+    dtype, and strides shorter than a layer's [T][H] block, are refused on the
+    host (MOE_ERR_SHAPE) before anything is enqueued; the binding refuses
+    them too."""
+    import ctypes as C
+    from bit_routed_expert_moe_amd import layer as L, stack_forward
+    lib = L.lib()
+    a = DeviceLayer(0xE1105100, 0, 256, 16, 128, 8, 0, "bf16")
+    b = DeviceLayer(0xE1105101, 1, 256, 16, 128, 4, 0, "bf16")  # another top_k
+    c = DeviceLayer(0xE1105102, 2, 256, 16, 128, 8, 0, "f32")   # another activation dtype
+    ws = a.layer_obj.workspace(1)
+    x = torch.zeros(2, 1, 256, dtype=torch.bfloat16, device="cuda")
+    ids = torch.full((2, 1, 8), -5, dtype=torch.int32, device="cuda")
+    w = torch.zeros(2, 1, 8, dtype=torch.float32, device="cuda")
+    y = torch.zeros(2, 1, 256, dtype=torch.float32, device="cuda")
+    p = lambda t: t.data_ptr()
+
+    def stack(l0, l1, xs=256, ys=256):
+        arr = (C.c_void_p * 2)(l0.layer_obj.handle.value, l1.layer_obj.handle.value)
+        return lib.moe_stack_forward(arr, 2, p(x), xs, 1, p(ids), p(w), p(y), ys, p(ws), None)
+
+    assert stack(a, b) == SHAPE and stack(a, c) == SHAPE
+    assert stack(a, a, xs=128) == SHAPE and stack(a, a, ys=255) == SHAPE
+    torch.cuda.synchronize()
+    assert torch.all(ids == -5)  # nothing ran
+    assert stack(a, a) == 0      # the same stack with full strides runs
+    with pytest.raises(ValueError):
+        stack_forward([a.layer_obj, b.layer_obj], x, ws)
