@@ -3,7 +3,8 @@
 
 The resident forward computes the router logits in leading workgroups of the
 gate/up launch; the gate/up workgroups read them as they land and, after a
-bounded number of polls, compute them locally instead.  A layer created with
+bounded number of polls, compute them locally instead (above hidden 4096 a
+separate router launch runs first, and the limit changes nothing).  A layer created with
 MOE_ROUTE_SPIN_LIMIT=-1 always computes them locally and one created with 0
 polls once: both must give the default layer's ids, gates and outputs bit for
 bit, and the oracle's selection.  The logit words go back to zero after every
@@ -47,6 +48,9 @@ CASES = [
     (2816, 128, 704, 8, 2112, 1, "bf16", "softmax", 4),  # Gemma-scale shapes
     (768, 256, 128, 8, 128, 2, "bf16", "sigmoid", 4),   # sigmoid gate with bias, 4 key slots
     (5120, 200, 128, 8, 128, 1, "bf16", "softmax", 4),  # hidden > 4096: separate router launch
+    (5120, 200, 128, 8, 128, 1, "bf16", "softmax", 2),  # the same with 2-bit records
+    (4608, 72, 128, 8, 128, 2, "f32", "softmax", 4),    # hidden > 4096, fp32 activations, 2 tokens
+    (8192, 16, 64, 2, 128, 1, "bf16", "softmax", 4),    # largest hidden, few experts
     (1024, 1024, 64, 16, 0, 1, "f32", "softmax", 2),   # most experts, largest k, 2-bit
     (192, 7, 64, 3, 0, 2, "bf16", "softmax", 2),       # fewer experts than waves
 ]
