@@ -40,7 +40,11 @@ constexpr int kDepthLargeH = 2;  // the same for 4-bit records with 4-wave workg
                                  // above 4096): 2.5 % per layer at hidden 6144 (2-bit groups,
                                  // half the bytes, keep 3)
 constexpr int kMaxSharedItems = 8;  // down work items of the shared expert
-constexpr int kDnRing = 2;          // k_down: groups in flight per wave (A/B: 2 beats 4 and all-at-once)
+// k_down: groups in flight per wave.  2 beats 4 and all-at-once; above hidden
+// 4096 (864 down workgroups at hidden 6144) 4-bit records keep only 1 in
+// flight: 3 % less down time there, while at hidden 2816 one in flight is
+// 10 % slower.
+constexpr int kDnRing = 2;
 constexpr int kMaxItems = kMaxTopK + kMaxSharedItems;
 
 // Prepared activations of one vector of length n (n multiple of 64):

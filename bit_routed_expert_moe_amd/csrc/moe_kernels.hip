@@ -697,7 +697,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
 // k_down: grid (n_otiles * n_items, T).  Lane = output row of a 64-row tile;
 // waves split the item's input groups (64 inputs of I = two h blocks).
 // ---------------------------------------------------------------------------
-template <int MAXG, int BITS>
+template <int MAXG, int BITS, int RING>
 __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     extern __shared__ uint32_t smem[];
     const int H = a.H;
@@ -760,8 +760,8 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // a ring of DD groups in flight per wave (every group at once when a wave
-    // has at most kDnRing groups)
-    constexpr int DD = MAXG > kDnRing ? kDnRing : MAXG;
+    // has at most RING groups)
+    constexpr int DD = MAXG > RING ? RING : MAXG;
     u32x4 W[DD][NW];
     uint32_t SB[DD];
 #pragma unroll
@@ -973,9 +973,13 @@ hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {
     const int nb = 2 * max(a.gi, a.gis);  // blocks staged per item (upper bound)
     const size_t sh = ((size_t)nb * (16 * kHParts + 3) + kWaves * 64) * 4;
     const int m = a.gpw_dn;
-#define MOE_DN(MG)                                                             \
-    (a.bits == 2 ? launch_kernel(k_down<MG, 2>, grid, dim3(kBlock), sh, s, a)  \
-                 : launch_kernel(k_down<MG, 4>, grid, dim3(kBlock), sh, s, a))
+    // one group in flight per wave for 4-bit records above hidden 4096 (the
+    // largest down grids), else kDnRing
+    const bool ring1 = a.bits == 4 && a.H > kGuSmallHMax;
+#define MOE_DN(MG)                                                                                   \
+    (a.bits == 2 ? launch_kernel(k_down<MG, 2, kDnRing>, grid, dim3(kBlock), sh, s, a)              \
+                 : (ring1 ? launch_kernel(k_down<MG, 4, 1>, grid, dim3(kBlock), sh, s, a)           \
+                          : launch_kernel(k_down<MG, 4, kDnRing>, grid, dim3(kBlock), sh, s, a)))
     if (m <= 2) MOE_DN(2);
     else if (m <= 4) MOE_DN(4);
     else if (m <= 8) MOE_DN(8);
