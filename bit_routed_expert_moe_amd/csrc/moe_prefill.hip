@@ -8,8 +8,9 @@
 //   k_route_tiles   router logits as 16-token x 16-expert MFMA tiles over the
 //                   prepared activations and the int8 rows turned exactly into
 //                   fp16 (k_topk then selects).
-//   k_group         one workgroup: (token, slot) pairs sorted by expert
-//                   (stable), and a tile list of at most 16 rows per tile;
+//   k_group         one workgroup: (token, slot) pairs grouped by expert
+//                   (in any order within an expert: no row of a tile
+//                   depends on another), and a tile list of at most 16 rows;
 //                   the shared expert adds tiles of 16 consecutive tokens.
 //   k_gu_grouped    per (tile, 128 rows of I): wave = one 64-row group of I
 //                   (gate and up: 8 MFMA N-tiles of 16) over one half of H;
@@ -245,14 +246,20 @@ __global__ __launch_bounds__(kBlock) void k_prep_tokens(PrefillArgs a) {
 
 // ---------------------------------------------------------------------------
 // k_route_tiles: router logits of many tokens.  Grid (ceil(E/16), ceil(T/16)),
-// 256 threads; the workgroup computes a 16-token x 16-expert tile, wave w over
-// the 32-input chunks [w*C/4, (w+1)*C/4), the four partial sums added in a
-// fixed order.  A = the prepared fp16 activations (slot order, odd inputs / 16,
+// 64*NW threads; the workgroup computes a 16-token x 16-expert tile, wave w
+// over the 64-input units [w*U/NW, (w+1)*U/NW), the NW partial sums added in
+// wave order.  A = the prepared fp16 activations (slot order, odd inputs / 16,
 // token scale 2^e); B = the int8 router bytes turned into fp16 in the same slot
 // order with odd inputs x16: byte b + 128 in the mantissa of 1024.0 (or of
 // 16384.0, where one mantissa step is 16) minus 1152 (or 18432) is b (or 16 b)
 // exactly.  Products are exact in fp32; logit = sum * 2^-e * scale.
+// Within a 64-input unit, lane quarter kq owns inputs [16 kq, 16 kq + 16): one
+// 16-byte router load and two 16-byte activation loads per lane, the unit's two
+// MFMA steps taking the first and the second 8 of them.  (A lane owning 8
+// inputs of each 32-input step instead touches twice the cache lines per load
+// and measured no faster with 4, 8 or 16 waves.)
 // ---------------------------------------------------------------------------
+
 __device__ __forceinline__ half8 router_b(uint32_t lo4, uint32_t hi4) {
     const uint32_t u0 = lo4 ^ 0x80808080u, u1 = hi4 ^ 0x80808080u;  // bytes b + 128
     // inputs (0,4) (1,5) (2,6) (3,7) into the low bytes of two halves
@@ -271,45 +278,49 @@ __device__ __forceinline__ half8 router_b(uint32_t lo4, uint32_t hi4) {
     return o;
 }
 
-template <int XP>
-__global__ __launch_bounds__(kBlock) void k_route_tiles(PrefillArgs a) {
-    __shared__ float red[kWaves][kTileRows][kTileRows + 1];
-    const int H = a.H, nch = H / 32;
+template <int XP, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k_route_tiles(PrefillArgs a) {
+    __shared__ float red[NW][kTileRows][kTileRows + 1];
+    const int H = a.H, nu = H / 64;
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int n = lane & 15, kq = lane >> 4;
     const int e0 = blockIdx.x * kTileRows, t0 = blockIdx.y * kTileRows;
-    const int c0 = wave * nch / kWaves, c1 = (wave + 1) * nch / kWaves;
+    const int u0 = wave * nu / NW, u1 = (wave + 1) * nu / NW;
     const __amdgpu_buffer_rsrc_t rx = rsrc(a.x16, (size_t)XP * a.T * H * 2);
     const __amdgpu_buffer_rsrc_t rr = rsrc(a.rq, (size_t)a.E * H);
     const int xpart = a.T * H * 2;
-    const int xo = (min(t0 + n, a.T - 1) * H + 8 * kq) * 2;  // rows past T compute on token T-1; discarded
-    const int ro = min(e0 + n, a.E - 1) * H + 8 * kq;
-    constexpr int D = 8;  // chunks in flight per wave
-    u32x4 A[D][XP];
-    uint32_t B[D][2];
-    auto load = [&](int q, int c) {
-        const int cc = min(c, c1 - 1);
+    const int xo = (min(t0 + n, a.T - 1) * H + 16 * kq) * 2;  // rows past T compute on token T-1; discarded
+    const int ro = min(e0 + n, a.E - 1) * H + 16 * kq;
+    u32x4 A[D][XP][2];
+    u32x4 B[D];
+    auto load = [&](int q, int u) {
+        const int uc = min(u, u1 - 1);
 #pragma unroll
-        for (int p = 0; p < XP; ++p) A[q][p] = bload4(rx, xo, p * xpart + 64 * cc);
-        B[q][0] = bload(rr, ro, 32 * cc);
-        B[q][1] = bload(rr, ro + 4, 32 * cc);
+        for (int p = 0; p < XP; ++p) {
+            A[q][p][0] = bload4(rx, xo, p * xpart + 128 * uc);
+            A[q][p][1] = bload4(rx, xo, p * xpart + 128 * uc + 16);
+        }
+        B[q] = bload4(rr, ro, 64 * uc);
     };
     f32x4 acc = {0, 0, 0, 0};
-    if (c1 > c0) {
+    if (u1 > u0) {
 #pragma unroll
         for (int q = 0; q < D; ++q) {
-            load(q, c0 + q);
+            load(q, u0 + q);
             __builtin_amdgcn_sched_barrier(0);
         }
-        for (int cb = c0; cb < c1; cb += D) {
+        for (int ub = u0; ub < u1; ub += D) {
 #pragma unroll
             for (int q = 0; q < D; ++q) {
-                if (cb + q < c1) {
-                    const half8 b = router_b(B[q][0], B[q][1]);
+                if (ub + q < u1) {
 #pragma unroll
-                    for (int p = 0; p < XP; ++p) acc = mfma(A[q][p], b, acc);
+                    for (int j = 0; j < 2; ++j) {
+                        const half8 b = router_b(B[q][2 * j], B[q][2 * j + 1]);
+#pragma unroll
+                        for (int p = 0; p < XP; ++p) acc = mfma(A[q][p][j], b, acc);
+                    }
                 }
-                load(q, cb + q + D);
+                load(q, ub + q + D);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -317,10 +328,13 @@ __global__ __launch_bounds__(kBlock) void k_route_tiles(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][n] = acc[r];
     __syncthreads();
+    if (threadIdx.x >= kTileRows * kTileRows) return;
     const int m = threadIdx.x >> 4, ei = threadIdx.x & 15;  // token m, expert ei of the tile
     const int t = t0 + m, e = e0 + ei;
     if (t < a.T && e < a.E) {
-        const float v = ((red[0][m][ei] + red[1][m][ei]) + red[2][m][ei]) + red[3][m][ei];
+        float v = red[0][m][ei];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][m][ei];
         a.logits[(size_t)t * a.E + e] = v * a.xinv[t] * (float)__builtin_bit_cast(_Float16, a.rs[e]);
     }
 }
@@ -337,7 +351,6 @@ __global__ __launch_bounds__(kBlock) void k_group(PrefillArgs a) {
     __shared__ int offs[kMaxExperts + 1];       // exclusive prefix sums of hist
     __shared__ int tile_base[kMaxExperts + 1];  // exclusive prefix sums of the tile counts
     __shared__ int running[kMaxExperts];
-    __shared__ int chunk_e[kBlock];
     __shared__ int scan[2][kBlock];
     const int E = a.E, P = a.T * a.k, tid = threadIdx.x;
     for (int e = tid; e < E; e += kBlock) {
@@ -404,32 +417,21 @@ __global__ __launch_bounds__(kBlock) void k_group(PrefillArgs a) {
         tile_base[E] = scan[1][tid];
     }
     __syncthreads();
-    // stable scatter, kBlock pairs at a time
+    // scatter: each pair takes the next free position of its expert.  The
+    // order of an expert's pairs does not change any result (every row of a
+    // grouped tile is computed on its own, and written to its own (token,
+    // slot)), so the positions come from an LDS atomic per pair.
     for (int base = 0; base < P; base += kBlock * R) {
         int v[R];
         load_ids(base, v);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const int p0 = base + kBlock * i;
-            if (p0 >= P) break;  // uniform
-            const int p = p0 + tid;
-            int e = -1;
-            if (p < P) {
-                e = v[i];
-                e = (e < 0 || e >= E) ? 0 : e;
-            }
-            chunk_e[tid] = e;
-            __syncthreads();
-            if (p < P) {
-                int rank = 0;
-                for (int q = 0; q < tid; ++q) rank += chunk_e[q] == e;
-                const int pos = offs[e] + running[e] + rank;
-                a.pair_tok[pos] = p / a.k;
-                a.pair_slot[pos] = p % a.k;
-            }
-            __syncthreads();
-            if (p < P) atomicAdd(&running[e], 1);
-            __syncthreads();
+            const int p = base + tid + kBlock * i;
+            if (p >= P) continue;
+            const int e = (v[i] < 0 || v[i] >= E) ? 0 : v[i];
+            const int pos = offs[e] + atomicAdd(&running[e], 1);
+            a.pair_tok[pos] = p / a.k;
+            a.pair_slot[pos] = p % a.k;
         }
     }
     // tiles
@@ -781,10 +783,11 @@ hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s
 
 hipError_t launch_route_tiles(const PrefillArgs& a, hipStream_t s) {
     const dim3 grid((a.E + kTileRows - 1) / kTileRows, (a.T + kTileRows - 1) / kTileRows);
+    constexpr int NW = 4, D = 4;  // waves per tile, 64-input units in flight per wave
     if (a.xparts == 1)
-        launch_kernel(k_route_tiles<1>, grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_route_tiles<1, NW, D>, grid, dim3(64 * NW), 0, s, a);
     else
-        launch_kernel(k_route_tiles<2>, grid, dim3(kBlock), 0, s, a);
+        launch_kernel(k_route_tiles<2, NW, D>, grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
