@@ -10,8 +10,9 @@ SwiGLU, the shared expert and the weighted combine, layer after layer on one
 stream (layer l+1 starts after layer l's output is written).  Inputs are
 synthetic and seeded (synth/): random 4-bit records filled on the GPU, int8
 routers, N(0,1) bf16 activations, a distinct input for each of the workload's
-decode steps.  Timed: exactly --steps steps, replayed as hipGraphs of
---graph-chunk steps, bracketed by synchronisations.
+decode steps.  Timed: exactly --steps steps, replayed as hipGraphs of up to
+--graph-chunk steps (the largest divisor of --steps not above it), bracketed
+by synchronisations.
 
 Printed (stdout, one JSON line): decode tokens/s per MoE layer (value), the
 whole-stack tokens/s, achieved HBM GB/s on algorithmic bytes (router + 8
@@ -54,14 +55,14 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 62484.99 KiB x 2.0 + WRITE_SIZE 90.06 KiB x 1.0 per launch
-    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128056478, "moe_kernels.hip", "dc3f5cbd064599bb"),
-    # FETCH_SIZE 12343.17 KiB x 2.0 + WRITE_SIZE 41.88 KiB x 1.0 per launch (the launch
+    # FETCH_SIZE 62482.97 KiB x 2.00 + WRITE_SIZE 90.06 KiB x 1.00 per launch
+    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128052320, "moe_kernels.hip", "afda35b37cbc3f01"),
+    # FETCH_SIZE 12339.69 KiB x 2.00 + WRITE_SIZE 41.88 KiB x 1.00 per launch (the launch
     # also runs the router)
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25320709, "moe_kernels.hip", "dc3f5cbd064599bb"),
-    # FETCH_SIZE 1833398.48 KiB x 2.0 + WRITE_SIZE 5756.57 KiB x 1.0 per launch (mean over
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25313575, "moe_kernels.hip", "afda35b37cbc3f01"),
+    # FETCH_SIZE 1833444.62 KiB x 2.00 + WRITE_SIZE 5756.59 KiB x 1.00 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3760548011, "moe_prefill.hip", "974d53b7d0163dd0"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3760641615, "moe_prefill.hip", "d4b7c0729970de19"),
 }
 
 
@@ -83,6 +84,29 @@ def traffic_for(workload, kernel, bits=4):
 
 
 METRIC = "decode tokens/s per MoE layer + achieved HBM GB/s vs peak (batch 1, top-8)"
+
+
+def chunk_len(K: int, cap: int) -> int:
+    """Steps per graph: the largest divisor of K not above cap, so that exactly K
+    steps are replayed in whole graphs."""
+    return max(d for d in range(1, max(1, min(K, cap)) + 1) if K % d == 0)
+
+
+def graph_units(run_step, S: int, G: int, n: int):
+    """n replay callables; the i-th runs steps (i*G + j) mod S, j < G, captured
+    as one hipGraph (graphs over the same steps are shared)."""
+    import torch
+    made, units = {}, []
+    for i in range(n):
+        c0 = (i * G) % S
+        if c0 not in made:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(G):
+                    run_step((c0 + j) % S)
+            made[c0] = g.replay
+        units.append(made[c0])
+    return units
 
 
 def log(*a):
@@ -532,27 +556,20 @@ def run_prefill(args, wl):
         run_step(s)
     torch.cuda.synchronize()
     K, W = args.steps, args.warmup
-    G = 1 if args.no_graph else math.gcd(args.graph_chunk, math.gcd(K, S))
-    units = []
-    if args.no_graph:
-        units = [(lambda s=s: run_step(s)) for s in range(S)]
-    else:
-        for c0 in range(0, S, G):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for s in range(c0, c0 + G):
-                    run_step(s)
-            units.append(g.replay)
-    n_units = len(units)
-    for i in range((W + G - 1) // G):
-        units[i % n_units]()
-    torch.cuda.synchronize()
+    G = 1 if args.no_graph else chunk_len(K, args.graph_chunk)
     start = (W + G - 1) // G
+    if args.no_graph:
+        units = [(lambda s=s: run_step(s)) for s in range(start + K)]
+    else:
+        units = graph_units(run_step, S, G, start + K // G)
+    for i in range(start):
+        units[i]()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for i in range(K // G):
-        units[(start + i) % n_units]()
+        units[start + i]()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -659,7 +676,8 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="glm_h6144_e256_l40_zipf")
-    ap.add_argument("--graph-chunk", type=int, default=16)
+    ap.add_argument("--graph-chunk", type=int, default=32,
+                    help="most steps per hipGraph (the largest divisor of --steps not above it)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of hipGraphs")
     ap.add_argument("--profile-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -756,29 +774,22 @@ def main():
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    G = 1 if args.no_graph else math.gcd(args.graph_chunk, math.gcd(K, S))
-    units = []  # callables, each running G consecutive steps
-    if args.no_graph:
-        units = [(lambda s=s: run_step(s)) for s in range(S)]
+    G = 1 if args.no_graph else chunk_len(K, args.graph_chunk)
+    start = (W + G - 1) // G
+    if args.no_graph:  # callables, each running G consecutive steps
+        units = [(lambda s=s: run_step(s % S)) for s in range(start + K)]
     else:
-        for c0 in range(0, S, G):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for s in range(c0, c0 + G):
-                    run_step(s)
-            units.append(g.replay)
-    n_units = len(units)
-    for i in range((W + G - 1) // G):
-        units[i % n_units]()
+        units = graph_units(run_step, S, G, start + K // G)
+    for i in range(start):
+        units[i]()
     torch.cuda.synchronize()
 
-    start = (W + G - 1) // G
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K // G + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(K // G):
-        units[(start + i) % n_units]()
+        units[start + i]()
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

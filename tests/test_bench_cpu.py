@@ -65,3 +65,12 @@ def test_launch_bytes_cover_the_token_layer(bits):
     assert bench.launch_bytes(wl, bits, 3, True)["gate_up"] == 3 * fused["gate_up"]
     if bits == 4:
         assert fused["gate_up"] == 24_893_696 and sep["route"] == 360_704
+
+
+def test_graph_chunks_divide_the_timed_steps():
+    assert bench.chunk_len(20, 32) == 20 and bench.chunk_len(64, 32) == 32
+    assert bench.chunk_len(256, 32) == 32 and bench.chunk_len(37, 32) == 1
+    assert bench.chunk_len(48, 16) == 16 and bench.chunk_len(1, 32) == 1
+    for K in range(1, 100):
+        G = bench.chunk_len(K, 32)
+        assert K % G == 0 and G <= 32
