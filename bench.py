@@ -799,6 +799,7 @@ def main():
     log(f"timed {K} steps in {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), graphs of {G} steps")
 
     tl_bytes = token_layer_bytes(wl, bits)
+    sel_bytes = wl.top_k * record_bytes(H, I, bits)
     step_bytes = L * T * tl_bytes
     layer_tok_s = L * T / (ms_per_step * 1e-3)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -852,6 +853,10 @@ def main():
         "stack_tok_s": round(T / (ms_per_step * 1e-3), 2),
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
         "alg_bytes_per_token_layer": tl_bytes,
+        # the selected records alone (no router, no shared record)
+        "selected_bytes_per_token_layer": sel_bytes,
+        "hbm_gbps_selected_only": round(L * T * sel_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_ms_percentiles_over": f"{K // G} timed graph replays of {G} steps (per-step means)",
         "step_ms_p50": round(float(np.percentile(per_step, 50)), 5),
         "step_ms_p95": round(float(np.percentile(per_step, 95)), 5),
         "step_ms_p99": round(float(np.percentile(per_step, 99)), 5),

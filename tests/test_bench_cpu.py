@@ -74,3 +74,11 @@ def test_graph_chunks_divide_the_timed_steps():
     for K in range(1, 100):
         G = bench.chunk_len(K, 32)
         assert K % G == 0 and G <= 32
+
+
+def test_selected_record_bytes_at_glm_scale():
+    # the eight selected records alone, the second byte column of the decode line
+    from bit_routed_expert_moe_amd import record_bytes
+    wl = synth.WORKLOADS["glm_h6144_e256_l40_zipf"]
+    assert wl.top_k * record_bytes(wl.hidden, wl.inter, 4) == 169_869_312
+    assert bench.token_layer_bytes(wl, 4) == 192_676_352
