@@ -5,8 +5,8 @@
   through moe_stack_forward exactly as bench.py times it.
 * GLM-scale decode: hidden 6144, 256 experts of intermediate 2048, top-8, shared
   2048 (5.5 GB per layer), activations drawn so the choice follows Zipf(1.1):
-  4 layers x 8 steps through moe_stack_forward (per-token path), and one call
-  of 4 tokens (grouped path).
+  4 layers x 8 steps through moe_stack_forward (per-token path), all 40 layers
+  x 2 steps as bench.py holds them, and one call of 4 tokens (grouped path).
 * GLM-scale 128-token prefill chunk (grouped path), 4-bit and 2-bit records.
 The oracle regenerates the records it selects on the CPU from the seeded
 generator; nothing the GPU computed is given to it.
@@ -90,6 +90,47 @@ def test_glm_stack_decode_per_token(orc):
             assert np.max(np.abs(w[t] - rw)) <= W_TOL
             assert rel_err(y[t], ry) <= Y_TOL, f"T={T} token {t}: {rel_err(y[t], ry):.2e}"
         print(f"glm decode layer, T={T}: ok", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_glm_stack_all_40_layers(orc):
+    """The GLM-scale stack exactly as bench.py holds it: all 40 layers (218 GB
+    of records in HBM), Zipf(1.1) activations, 2 decode steps of one token
+    through moe_stack_forward.  ids bit-exact and gates within 1e-6 on every
+    layer of both steps; y within 2e-3 of the oracle on layers 0, 13, 26 and
+    39 of the first step (the oracle regenerates each selected record)."""
+    import gc
+    wl = synth.WORKLOADS["glm_h6144_e256_l40_zipf"]
+    NL, S = wl.n_layers, 2
+    gc.collect()
+    torch.cuda.empty_cache()  # room for 218 GB next to what earlier tests left cached
+    layers = [DeviceLayer(wl.seed, l, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
+              for l in range(NL)]
+    print(f"glm stack: {NL} layers filled", flush=True)
+    try:
+        toks = [zipf_tokens(dl, orc, wl.zipf_s, range(S)) for dl in layers]
+        ws = layers[0].layer_obj.workspace(1)
+        worst_w = worst_y = 0.0
+        for step in range(S):
+            x = to_dev(np.stack([toks[l][step][0] for l in range(NL)])[:, None, :], wl.act)
+            ids, w, y = stack_forward([dl.layer_obj for dl in layers], x, ws)
+            ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+            for l, dl in enumerate(layers):
+                xd = toks[l][step][1]
+                if step == 0 and l in (0, 13, 26, 39):
+                    rid, rw, ry, _, _ = dl.oracle(orc, xd)
+                    worst_y = max(worst_y, rel_err(y[l, 0], ry))
+                else:
+                    rid, rw, _ = orc.route(dl.rq, dl.rs, xd, wl.top_k)
+                assert ids[l, 0].tolist() == rid.tolist(), f"step {step} layer {l}"
+                worst_w = max(worst_w, float(np.max(np.abs(w[l, 0] - rw))))
+        print(f"glm stack, all {NL} layers: {S} steps, max |w err| {worst_w:.2e}, "
+              f"max rel y err (sampled layers) {worst_y:.2e}", flush=True)
+        assert worst_w <= W_TOL and worst_y <= Y_TOL
+    finally:
+        del layers
+        gc.collect()
+        torch.cuda.empty_cache()
 
 
 def test_glm_layer_zipf_grouped_path(orc):
