@@ -30,23 +30,31 @@ def _gpu():
 
 
 def test_gemma_stack_full_size(orc):
+    """All 30 layers, 16 decode steps through moe_stack_forward: ids bit-exact
+    and gates within 1e-6 on every token-layer, y within 2e-3 of the oracle on
+    every layer of the first 2 steps (the oracle regenerates each selected
+    record)."""
     wl = synth.WORKLOADS["gemma_a4b_h2816_e128_l30"]
-    L, H = wl.n_layers, wl.hidden
+    L, H, S = wl.n_layers, wl.hidden, 16
     layers = [DeviceLayer(wl.seed, l, H, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
               for l in range(L)]
     ws = layers[0].layer_obj.workspace(1)
     worst_y = worst_w = 0.0
-    for step in range(2):
+    for step in range(S):
         toks = [dl.natural_token(orc, step) for dl in layers]
         x = to_dev(np.stack([t[0] for t in toks])[:, None, :], wl.act)  # [L][1][H]
         ids, w, y = stack_forward([dl.layer_obj for dl in layers], x, ws)
         ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
         for l, dl in enumerate(layers):
-            rid, rw, ry, _, _ = dl.oracle(orc, toks[l][1])
+            if step < 2:
+                rid, rw, ry, _, _ = dl.oracle(orc, toks[l][1])
+                worst_y = max(worst_y, rel_err(y[l, 0], ry))
+            else:
+                rid, rw, _ = orc.route(dl.rq, dl.rs, toks[l][1], wl.top_k)
             assert ids[l, 0].tolist() == rid.tolist(), f"step {step} layer {l}"
             worst_w = max(worst_w, float(np.max(np.abs(w[l, 0] - rw))))
-            worst_y = max(worst_y, rel_err(y[l, 0], ry))
-    print(f"gemma stack: 2 steps x {L} layers, max |w err| {worst_w:.2e}, max rel y err {worst_y:.2e}")
+    print(f"gemma stack: {S} steps x {L} layers, max |w err| {worst_w:.2e}, "
+          f"max rel y err (first 2 steps) {worst_y:.2e}")
     assert worst_w <= W_TOL and worst_y <= Y_TOL
 
 
