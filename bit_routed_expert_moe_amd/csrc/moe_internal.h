@@ -30,6 +30,11 @@ constexpr int kMaxHidden = 8192;
 constexpr int kHParts = 1;         // fp16 parts used for the intermediate h
 constexpr int kMaxDownGroups = 64; // input groups (of I) per down work item
 constexpr int kMaxGateUpGroupsPerWave = 32;
+// Shared 32-row blocks split into this many slices of H (4-wave units only):
+// the shared expert's gate/up then runs on every CU while the routed units
+// select, instead of as a third unit on a quarter of the CUs
+constexpr int kSharedSplit = 4;
+constexpr int kPieceMaxGroups = 8;  // input groups per wave in a shared piece, at most
 constexpr int kCounterStride = 64;  // arrival counters 256 bytes apart (own cache lines)
 // Weight groups in flight per wave in k_gate_up.  Shallow on purpose: with one
 // wave per SIMD and every wave's loads queued at once, deeper rings delay each
@@ -107,14 +112,17 @@ struct FfnArgs {
     float* hHs;              // [T][k+1][blk_max]
     float* hinv;             // [T][k+1][blk_max]
     float* dpart;            // [T][n_otiles][n_items][64]
-    int n_units;             // k*blk_r + blk_s
-    uint32_t* dctr;          // [T][n_otiles][kCounterStride]
+    int n_units;             // k*blk_r + sh_split*blk_s
+    uint32_t* dctr;          // [T][n_otiles][kCounterStride] (k_gate_up: [T][blk_s] piece counts)
+    float* shp;              // [T][blk_s][sh_split][64] gate/up sums of the shared pieces
+    int sh_split;            // pieces per shared 32-row block (each a slice of H), or 1
+    int gpw_sh;              // input groups per wave in a shared piece
     float* y;                // [T][H] fused output (or nullptr)
     float* eo;               // [T][k+1][H] per-expert outputs (or nullptr)
     uint32_t* err;           // device error word
     int H, I, Is, E, k;
     int blk_r;               // I/32  (gate/up units per routed expert)
-    int blk_s;               // Is/32 (gate/up units of the shared expert)
+    int blk_s;               // Is/32 (32-row blocks of the shared expert; sh_split units each)
     int blk_max;             // max(blk_r, blk_s)
     int gpw_gu;              // input groups per wave in the gate/up kernel
     int gu_waves;            // waves per gate/up workgroup

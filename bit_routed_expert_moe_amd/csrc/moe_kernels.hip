@@ -28,11 +28,14 @@
 // contiguous record bytes.  Small inputs (activations, logits) are loaded
 // before the weights so that the weights can be consumed in arrival order.
 // Sums across waves and workgroups are done in a fixed order: reruns are
-// bit-identical.  The two hand-offs inside a kernel (k_down's last arrival,
-// k_gate_up's router units to its gate/up units) use agent-scope coherent
-// stores and loads (plus an arrival counter in k_down), so no L2 write-back
-// or invalidate is needed.
+// bit-identical.  The hand-offs inside a kernel (k_down's last arrival,
+// k_gate_up's router units to its gate/up units, the last shared piece of a
+// block in k_gate_up) use agent-scope coherent stores and loads (plus an
+// arrival counter in k_down and for the pieces), so no L2 write-back or
+// invalidate is needed.
 #include "moe_device.h"
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -466,8 +469,12 @@ __global__ __launch_bounds__(kBlock) void k_prep(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_gate_up: grid (k*blk_r + blk_s, T).  Lane = row of the 64-row GU tile
-// (rows 0..31 gate, 32..63 up); waves split the H/64 input groups.
+// k_gate_up: grid (k*blk_r + sh_split*blk_s, T).  Lane = row of the 64-row GU
+// tile (rows 0..31 gate, 32..63 up); waves split the H/64 input groups.  With
+// 4-wave units each shared 32-row block is sh_split units, one slice of H
+// each: the slices' gate/up sums meet in the last slice to arrive, which
+// computes h.  (A unit per shared block was a third unit on a quarter of the
+// CUs, and a CU streams at most about 25 GB/s: those CUs finished last.)
 // ---------------------------------------------------------------------------
 template <int XP, int MAXG, int Q, int BITS, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
@@ -507,7 +514,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     const bool fused = route_units > 0;
     const bool routed = u < a.k * a.blk_r;
     const int j = routed ? u / a.blk_r : a.k;
-    const int b = routed ? u - j * a.blk_r : u - a.k * a.blk_r;
+    // a shared unit is one slice (piece) of H of a 32-row block when sh_split > 1
+    const int S = routed ? 1 : a.sh_split;
+    const int vs = u - a.k * a.blk_r;
+    const int b = routed ? u - j * a.blk_r : vs / S;
+    const int piece = routed ? 0 : vs - b * S;
 
     // 1. the prepared activations of token t: into registers first, or with
     // fused routing prepared here, straight into LDS (the same arithmetic as
@@ -577,8 +588,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     constexpr int SEG = NW * 1024 + 256;
     const uint8_t* tile = rec + (size_t)SEG * NG * b + (size_t)lane * 16;
     const uint8_t* sbt = rec + (size_t)SEG * NG * b + NW * 1024 + (size_t)lane * 4;
-    const int g0 = wave * a.gpw_gu;
-    const int g1 = min(NG, g0 + a.gpw_gu);
+    int g0, g1;
+    if (S == 1) {
+        g0 = wave * a.gpw_gu;
+        g1 = min(NG, g0 + a.gpw_gu);
+    } else {  // this piece's slice of the input groups, split over the waves
+        const int r1 = (piece + 1) * NG / S;
+        g0 = piece * NG / S + wave * a.gpw_sh;
+        g1 = min(r1, g0 + a.gpw_sh);
+    }
+    const int glast = max(g1 - 1, 0);  // clamp of the loads past this wave's groups (re-reads)
 
     // 3. weight stream: a ring of kDepth groups in flight per wave.  Loads are
     // unconditional (clamped to a valid group) and kept in program order, so
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     uint32_t SB[D];
 #pragma unroll
     for (int q = 0; q < D; ++q) {
-        const int g = min(g0 + q, NG - 1);
+        const int g = min(g0 + q, glast);
 #pragma unroll
         for (int c = 0; c < NW; ++c) W[q][c] = ldg_nt((const u32x4*)(tile + (size_t)g * SEG + c * 1024));
         SB[q] = ldg_nt((const uint32_t*)(sbt + (size_t)g * SEG));
@@ -610,60 +629,96 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
     }
     __syncthreads();
 
-    // 5. dequantised dot products, group by group as the weights arrive
+    // 5. dequantised dot products, group by group as the weights arrive (a
+    // shared piece's waves hold at most kPieceMaxGroups groups: its own
+    // unrolled copy, so that every copy's waits stay exact)
     float rs = 0.0f, rb = 0.0f;
+    auto stream = [&](auto mg) {
+        constexpr int MG = decltype(mg)::value;
 #pragma unroll
-    for (int q = 0; q < MAXG; ++q) {
-        const int slot = q % D;
-        const int g = g0 + q;
-        if (g < g1) {
-            float a0 = 0.0f, a1 = 0.0f;
-            if constexpr (BITS == 4) {
+        for (int q = 0; q < MG; ++q) {
+            const int slot = q % D;
+            const int g = g0 + q;
+            if (g < g1) {
+                float a0 = 0.0f, a1 = 0.0f;
+                if constexpr (BITS == 4) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const u32x4 wv = W[slot][half];
-                    const uint32_t* xc = xp + (size_t)(2 * g + half) * 16 * XP;
+                    for (int half = 0; half < 2; ++half) {
+                        const u32x4 wv = W[slot][half];
+                        const uint32_t* xc = xp + (size_t)(2 * g + half) * 16 * XP;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                            for (int p = 0; p < XP; ++p) dot_nib8(wv[m], xc + (m * XP + p) * 4, a0, a1);
+                        }
+                    }
+                } else {
+                    const u32x4 wv = W[slot][0];
+                    const uint32_t* xc = xp + (size_t)g * 32 * XP;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                        for (int p = 0; p < XP; ++p) dot_nib8(wv[m], xc + (m * XP + p) * 4, a0, a1);
+                        for (int p = 0; p < XP; ++p) dot_crumb16(wv[m], xc + (m * XP + p) * 8, a0, a1);
                     }
                 }
-            } else {
-                const u32x4 wv = W[slot][0];
-                const uint32_t* xc = xp + (size_t)g * 32 * XP;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int p = 0; p < XP; ++p) dot_crumb16(wv[m], xc + (m * XP + p) * 8, a0, a1);
-                }
+                rs = fmaf(f16lo(SB[slot]) * sI[g], (a0 + a1) - sK[g], rs);
+                rb = fmaf(f16hi(SB[slot]), sX[g], rb);
             }
-            rs = fmaf(f16lo(SB[slot]) * sI[g], (a0 + a1) - sK[g], rs);
-            rb = fmaf(f16hi(SB[slot]), sX[g], rb);
-        }
-        if (q + D < MAXG) {  // refill the slot just consumed
-            const int gn = min(g0 + q + D, NG - 1);
+            if (q + D < MG) {  // refill the slot just consumed
+                const int gn = min(g0 + q + D, glast);
 #pragma unroll
-            for (int c = 0; c < NW; ++c) W[slot][c] = ldg_nt((const u32x4*)(tile + (size_t)gn * SEG + c * 1024));
-            SB[slot] = ldg_nt((const uint32_t*)(sbt + (size_t)gn * SEG));
+                for (int c = 0; c < NW; ++c) W[slot][c] = ldg_nt((const u32x4*)(tile + (size_t)gn * SEG + c * 1024));
+                SB[slot] = ldg_nt((const uint32_t*)(sbt + (size_t)gn * SEG));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (WAVES == kGuWavesLargeH && S > 1)  // pieces only with 4-wave units
+        stream(std::integral_constant<int, (kPieceMaxGroups < MAXG ? kPieceMaxGroups : MAXG)>{});
+    else
+        stream(std::integral_constant<int, MAXG>{});
     red[wave * 64 + lane] = rs + rb;
     __syncthreads();
     if (wave != 0) return;
 
-    // 6. wave 0: gate/up sums in wave order, h = silu(g) * u, then h prepared
-    float h = 0.0f;
-    if (lane < 32) {
-        float g = 0.0f, uu = 0.0f;
+    // 6. wave 0: gate/up sums in wave order (of a shared block split into
+    // pieces: each piece's sums, then in the last piece to arrive their sums
+    // in piece order), h = silu(g) * u, then h prepared
+    float gsum = 0.0f, usum = 0.0f;
+    if (WAVES != kGuWavesLargeH || S == 1) {
+        if (lane < 32) {
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            g += red[w * 64 + lane];
-            uu += red[w * 64 + 32 + lane];
+            for (int w = 0; w < WAVES; ++w) {
+                gsum += red[w * 64 + lane];
+                usum += red[w * 64 + 32 + lane];
+            }
         }
-        h = bad ? __builtin_nanf("") : g / (1.0f + expf(-g)) * uu;
+    } else {
+        float pv = 0.0f;  // lane < 32: gate row lane, else up row lane - 32
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) pv += red[w * 64 + lane];
+        float* P = a.shp + ((size_t)t * a.blk_s + b) * S * 64;
+        __hip_atomic_store(P + piece * 64 + lane, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);  // the coherent store above has completed
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        uint32_t* ctr = a.dctr + ((size_t)t * a.blk_s + b) * kCounterStride;
+        uint32_t prev = 0;
+        if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0, 64);
+        if (prev != (uint32_t)S - 1) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        for (int q = 0; q < S; ++q) {
+            const float gq = __hip_atomic_load(P + q * 64 + (lane & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float uq = __hip_atomic_load(P + q * 64 + 32 + (lane & 31), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            gsum += gq;
+            usum += uq;
+        }
+        if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    float h = 0.0f;
+    if (lane < 32) h = bad ? __builtin_nanf("") : gsum / (1.0f + expf(-gsum)) * usum;
     if (bad && lane == 0) atomicOr(a.err, 1u);
     const float mx = wave_max(lane < 32 ? fabsf(h) : 0.0f);
     const int e = act_exponent(mx);

@@ -77,6 +77,8 @@ struct moe_layer {
     int n_items;   // down items per output tile
     int n_otiles;  // H / 64
     int gpw_gu, gpw_dn;
+    int sh_split;  // pieces per shared 32-row block (kSharedSplit or 1)
+    int gpw_sh;    // input groups per wave in a shared piece
     int gu_waves;  // waves per gate/up workgroup
     int spin_limit; // fused routing: polls of the logit words before computing them locally
 };
@@ -137,7 +139,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
     size_t err, flog, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
-        x16, x16b, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, total;
+        x16, x16b, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, shp, total;
     int tile_cap;
 };
 
@@ -183,6 +185,7 @@ WsLayout ws_layout(const moe_layer* L, int T) {
         o.hHs = take(nslot * 4);
         o.hinv = take(nslot * 4);
         o.dpart = take((size_t)T * L->n_otiles * L->n_items * 64 * 4);
+        o.shp = take((size_t)T * L->blk_s * L->sh_split * 64 * 4);
     } else {  // grouped path, one chunk of at most grouped_chunk(L) tokens at a time
         const size_t Tg = (size_t)std::min(T, grouped_chunk(L));
         const size_t P = Tg * k;
@@ -277,7 +280,10 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.hHs = (float*)(ws + o.hHs);
     a.hinv = (float*)(ws + o.hinv);
     a.dpart = (float*)(ws + o.dpart);
-    a.n_units = L->d.top_k * L->blk_r + L->blk_s;
+    a.n_units = L->d.top_k * L->blk_r + L->sh_split * L->blk_s;
+    a.shp = (float*)(ws + o.shp);
+    a.sh_split = L->sh_split;
+    a.gpw_sh = L->gpw_sh;
     a.dctr = (uint32_t*)(ws + o.dctr);
     a.y = y;
     a.eo = eo;
@@ -502,7 +508,7 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
     if (e != hipSuccess) return hip_fail(e, "slot table copy");
     const int routed_units = k * L->blk_r;
     // shared expert first, overlapping the copies
-    if ((e = decode_units(L, fa, 1, routed_units, L->blk_s, s)) != hipSuccess)
+    if ((e = decode_units(L, fa, 1, routed_units, L->sh_split * L->blk_s, s)) != hipSuccess)
         return hip_fail(e, "gate/up launch");
     if (copies || c.side_pending) {  // this call's copies and any earlier prefetch copies
         if ((e = hipEventRecord(c.ev_copies, c.side)) != hipSuccess ||
@@ -666,6 +672,15 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         if (end != sl && *end == '\0' && v >= -1 && v <= kRouteSpinLimit) L->spin_limit = (int)v;
     }
     L->gpw_gu = (L->NG + L->gu_waves - 1) / L->gu_waves;
+    // the shared blocks in slices of H where the units have 4 waves; the piece
+    // counts reuse the down stage's arrival counters ([T][n_otiles] of them)
+    {
+        const int per_wave = ((L->NG + kSharedSplit - 1) / kSharedSplit + L->gu_waves - 1) / L->gu_waves;
+        const bool split = L->gu_waves == kGuWavesLargeH && L->blk_s > 0 && L->blk_s <= kMaxHidden / 64 &&
+                           per_wave <= kPieceMaxGroups;
+        L->sh_split = split ? kSharedSplit : 1;
+        L->gpw_sh = split ? per_wave : 0;
+    }
     if (L->gpw_gu > kMaxGateUpGroupsPerWave || std::max(L->gi, L->gis) > kMaxDownGroups) {
         delete L;
         return fail(MOE_ERR_SHAPE, "shape exceeds the kernels' per-wave register tiles");

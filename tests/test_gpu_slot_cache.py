@@ -216,3 +216,27 @@ def test_offload_workload_shapes_full_size(orc):
               f"hit rate {hits / (hits + misses):.3f}", flush=True)
     print(f"offload shapes: max rel y err on sampled steps {worst_y:.2e}", flush=True)
     assert worst_y <= Y_TOL
+
+
+def test_cached_layer_large_hidden_matches_resident(orc):
+    """Hidden 4608 (4-wave gate/up units, the shared expert's blocks in slices
+    of H): the slot-cached layer launches the shared units and the routed
+    units separately, the resident layer in one launch; every step's ids,
+    gates and y agree bit for bit, and y is within 2e-3 of the oracle."""
+    from _gpu_helpers import Y_TOL, rel_err
+    H, E, I, k, Is, n_slots = 4608, 24, 128, 4, 256, 8
+    dl = DeviceLayer(0xB17E0530, 0, H, E, I, k, Is, "bf16")
+    cached, _, _ = cached_twin(dl, n_slots)
+    ws_r, ws_c = dl.layer_obj.workspace(1), cached.workspace(1)
+    worst = 0.0
+    for step in range(12):
+        xq, xd = dl.natural_token(orc, step)
+        x = to_dev(xq[None], "bf16")
+        r = dl.layer_obj.forward(x, ws_r)
+        c = cached.forward(x, ws_c)
+        for a_, b_ in zip(r, c):
+            assert torch.equal(a_, b_), f"step {step}: cached result differs from resident"
+        rid, rw, ry, _, _ = dl.oracle(orc, xd)
+        assert r[0].cpu().numpy()[0].tolist() == rid.tolist()
+        worst = max(worst, rel_err(r[2].cpu().numpy()[0], ry))
+    assert worst <= Y_TOL, worst
