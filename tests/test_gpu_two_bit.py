@@ -6,9 +6,10 @@ bit-exact, gates within 1e-6, outputs within the usual 2e-3 relative per token.
 Calls of 4 or more tokens take the grouped (MFMA) path, where a token's
 result does not depend on the rest of its batch.  The three-call API agrees
 with the fused forward bit for bit, a slot-cached 2-bit layer agrees with the
-resident one, and the Gemma-scale stack (30 layers, the shape and the call the
-benchmark times) is checked on two decode steps of every layer.  More grouped
-shapes run 2-bit records in the prefill tests.
+resident one, the Gemma-scale stack (30 layers, the shape and the call the
+benchmark times) is checked on two decode steps of every layer, and so is
+GLM-scale decode on two layers.  More grouped shapes run 2-bit records in the
+prefill tests.
 """
 import numpy as np
 import pytest
@@ -139,3 +140,27 @@ def test_two_bit_gemma_stack_full_size(orc):
     print(f"2-bit gemma stack: 2 steps x {L} layers, max |w err| {worst_w:.2e}, "
           f"max rel y err {worst_y:.2e}", flush=True)
     assert worst_w <= W_TOL and worst_y <= Y_TOL
+
+
+def test_two_bit_glm_decode(orc):
+    """GLM-scale decode with 2-bit records (the bench's --bits 2 line): hidden
+    6144 (4-wave gate/up units, the shared expert in quarters of H), 256
+    experts of intermediate 2048, shared 2048, Zipf(1.1) activations; 2 layers
+    x 4 steps of one token through moe_stack_forward, then a 3-token call on
+    one layer (still the per-token path)."""
+    from _gpu_helpers import zipf_tokens
+    from bit_routed_expert_moe_amd import stack_forward
+    wl = synth.WORKLOADS["glm_h6144_e256_l40_zipf"]
+    NL, S = 2, 4
+    layers = [DeviceLayer(wl.seed, l, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act,
+                          bits=2) for l in range(NL)]
+    toks = [zipf_tokens(dl, orc, wl.zipf_s, range(S)) for dl in layers]
+    ws = layers[0].layer_obj.workspace(1)
+    for step in range(S):
+        x = to_dev(np.stack([toks[l][step][0] for l in range(NL)])[:, None, :], wl.act)
+        ids, w, y = stack_forward([dl.layer_obj for dl in layers], x, ws)
+        for l, dl in enumerate(layers):
+            check(dl, orc, [toks[l][step]], ids[l], w[l], y[l], f"2-bit glm decode step {step} layer {l}")
+    dl = layers[0]
+    ids, w, y = dl.layer_obj.forward(to_dev(np.stack([t[0] for t in toks[0][:3]]), wl.act))
+    check(dl, orc, toks[0][:3], ids, w, y, "2-bit glm decode, 3 tokens")
