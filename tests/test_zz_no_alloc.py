@@ -1,7 +1,7 @@
 """moe_layer_forward_noalloc (the workspace in the library's static device
 array) against moe_layer_forward with a caller's workspace, through the C ABI
 (needs a GPU): ids, gates and outputs bit-identical, on two calls in a row
-with the second smaller, on two layers of different shapes; a call whose
+with the second smaller, on three layers of different shapes; a call whose
 workspace would exceed the array is refused before any launch."""
 import numpy as np
 import pytest
@@ -28,7 +28,9 @@ def _outs(T, k, H):
 def test_noalloc_forward_matches_workspace_forward(orc):
     big = DeviceLayer(0xA110C001, 0, 2816, 128, 704, 8, 2112, "bf16")   # Gemma-scale shapes
     small = DeviceLayer(0xA110C002, 0, 512, 40, 192, 6, 320, "f32")
-    for dl, T1, T2 in ((big, 3, 1), (small, 2, 1), (big, 1, 1)):
+    # above hidden 4096: the router launch, and the shared expert in quarters of H
+    wide = DeviceLayer(0xA110C004, 0, 6144, 64, 512, 8, 512, "bf16")
+    for dl, T1, T2 in ((big, 3, 1), (small, 2, 1), (wide, 3, 2), (big, 1, 1)):
         toks = [dl.natural_token(orc, s) for s in range(T1)]
         xq = np.stack([t[0] for t in toks])
         for T in (T1, T2):  # two calls in a row, the second not larger
