@@ -80,7 +80,7 @@ struct FfnArgs {
     const uint8_t* shared;   // shared record or nullptr
     size_t rec_bytes;
     const uint8_t* slots;    // slot cache: n_slots records (nullptr = resident pool)
-    const int32_t* slot_ids; // [T][k] slot holding each selected expert (with slots)
+    int32_t slot_of[kMaxTopK];  // with slots (one token per call): the slot of each selected expert
     int unit_offset;         // k_gate_up: first unit of this launch (split launches)
     const int32_t* ids;      // [T][k] selection (read by k_down; by k_gate_up unless logits)
     const float* w;          // [T][k] gate weights (fused combine only)
@@ -164,6 +164,18 @@ struct PrefillArgs {
     float* logits;           // [T][E] out (k_route_tiles)
     size_t d_off, d_off_shared;  // down segments of a routed / the shared record
     int H, E, I, Is, k, T, P, Imax, tile_cap, xparts, bits;
+};
+
+constexpr int kFetchBlocksPerRecord = 64;  // k_fetch workgroups per record
+// Missed experts' records copied by a kernel from the pinned host pool (read
+// over PCIe through its device mapping) into their HBM slots.
+struct FetchArgs {
+    const uint8_t* src;          // host pool, device-mapped address
+    uint8_t* dst;                // slots
+    size_t rec_bytes;            // a multiple of 16
+    int n;                       // records to copy (<= kMaxTopK)
+    int32_t src_rec[kMaxTopK];   // expert index in the pool
+    int32_t dst_slot[kMaxTopK];  // slot index
 };
 
 struct CombineArgs {

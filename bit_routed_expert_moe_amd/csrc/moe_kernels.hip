@@ -576,7 +576,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gate_up(FfnArgs a) {
             bad = true;
             e = 0;
         }
-        rec = a.slots ? a.slots + (size_t)a.slot_ids[(size_t)t * a.k + j] * a.rec_bytes
+        rec = a.slots ? a.slots + (size_t)a.slot_of[j] * a.rec_bytes
                       : a.experts + (size_t)e * a.rec_bytes;
     } else {
         rec = a.shared;
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs a) {
         j = item;
         int e = a.ids[(size_t)t * a.k + j];
         if (e < 0 || e >= a.E) e = 0;  // h of this slot is NaN already
-        rec = a.slots ? a.slots + (size_t)a.slot_ids[(size_t)t * a.k + j] * a.rec_bytes
+        rec = a.slots ? a.slots + (size_t)a.slot_of[j] * a.rec_bytes
                       : a.experts + (size_t)e * a.rec_bytes;
         ga = 0;
         gb = a.I / 64;
@@ -947,6 +947,25 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
 
 __global__ void k_clear_word(uint32_t* p) { *p = 0u; }
 
+// k_fetch: grid (blocks per record, n).  Each workgroup copies an interleaved
+// share of one record's 16-byte vectors, four loads in flight per thread
+// (the loads cross PCIe, so many must be outstanding).
+__global__ __launch_bounds__(kBlock) void k_fetch(FetchArgs f) {
+    const int r = blockIdx.y;
+    const u32x4* src = (const u32x4*)(f.src + (size_t)f.src_rec[r] * f.rec_bytes);
+    u32x4* dst = (u32x4*)(f.dst + (size_t)f.dst_slot[r] * f.rec_bytes);
+    const size_t nv = f.rec_bytes / 16, stride = (size_t)gridDim.x * kBlock;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nv; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * stride < nv) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * stride < nv) dst[i + u * stride] = v[u];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (called from moe_layer.hip)
 // ---------------------------------------------------------------------------
@@ -1046,6 +1065,12 @@ hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     const dim3 grid((a.H + kBlock - 1) / kBlock, a.T);
     launch_kernel(k_combine, grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fetch(const FetchArgs& f, hipStream_t s) {
+    if (f.n <= 0) return hipSuccess;
+    launch_kernel(k_fetch, dim3(kFetchBlocksPerRecord, f.n), dim3(kBlock), 0, s, f);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ hipError_t launch_gate_up(const FfnArgs& a, int T, int xparts, int n_units, hipS
 hipError_t launch_down(const FfnArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* p, hipStream_t s);
+hipError_t launch_fetch(const FetchArgs& f, hipStream_t s);
 hipError_t launch_prefill_prep(const PrefillArgs& a, int act_bf16, hipStream_t s);
 hipError_t launch_prefill_group(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_route_tiles(const PrefillArgs& a, hipStream_t s);
@@ -81,6 +82,9 @@ struct moe_layer {
     int gpw_sh;    // input groups per wave in a shared piece
     int gu_waves;  // waves per gate/up workgroup
     int spin_limit; // fused routing: polls of the logit words before computing them locally
+    // the host pool as the device addresses it (null: not mapped; misses are
+    // then copied on the side stream)
+    const uint8_t* host_pool_dev = nullptr;
 };
 
 namespace moe {
@@ -138,7 +142,7 @@ moe_status hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t err, flog, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart, slot_ids,
+    size_t err, flog, dctr, pred_ids, pred_w, xpairs, xK, xX, xinv, logits, hpairs, hK, hHs, hinv, dpart,
         x16, x16b, pxsum, pxinv, pair_tok, pair_slot, tiles, n_tiles, h16, phsum, phinv, eo, shp, total;
     int tile_cap;
 };
@@ -173,7 +177,6 @@ WsLayout ws_layout(const moe_layer* L, int T) {
     o.pred_ids = take((size_t)L->d.top_k * 4);  // moe_cache_prefetch's selection
     o.pred_w = take((size_t)L->d.top_k * 4);
     o.logits = take((size_t)T * L->d.n_experts * 4);
-    o.slot_ids = take((size_t)T * k * 4);
     if (T < kPrefillMinTokens) {  // per-token (decode) path
         o.xpairs = take((size_t)T * (H / 2) * L->xparts * 4);
         o.xK = take((size_t)T * L->NG * 4);
@@ -267,7 +270,6 @@ FfnArgs ffn_args(const moe_layer* L, const int32_t* ids, const float* w, uint8_t
     a.d_off_shared = L->d_off_shared;
     if (L->cache.n_slots) {
         a.slots = L->w.slots;
-        a.slot_ids = (const int32_t*)(ws + o.slot_ids);
     }
     a.ids = ids;
     a.w = w;
@@ -470,6 +472,14 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
             return fail(MOE_ERR_ARG, "selected expert id out of range");
     }
     bool copies = false;
+    // misses copied by a kernel on `s` when the pool is device-mapped and no
+    // prefetch copies are pending on the side stream (else on the side stream,
+    // behind them: no wait between the streams before the copies)
+    const bool fetch_kernel = L->host_pool_dev && !c.side_pending;
+    FetchArgs fetch{};
+    fetch.src = L->host_pool_dev;
+    fetch.dst = L->w.slots;
+    fetch.rec_bytes = L->rec_bytes;
     for (int j = 0; j < k; ++j) {
         const int ex = c.h_ids[j];
         c.count[ex] += 1;
@@ -491,21 +501,27 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
             c.expert_in[slot] = ex;
             c.slot_of[ex] = slot;
             c.prefetched[slot] = 0;
-            if (!copies) {  // the side stream must not overwrite a slot still being read
-                if ((e = hipStreamWaitEvent(c.side, c.ev_ids, 0)) != hipSuccess)
-                    return hip_fail(e, "side stream wait");
-                copies = true;
+            if (fetch_kernel) {
+                fetch.src_rec[fetch.n] = ex;
+                fetch.dst_slot[fetch.n] = slot;
+                ++fetch.n;
+            } else {
+                if (!copies) {  // the side stream must not overwrite a slot still being read
+                    if ((e = hipStreamWaitEvent(c.side, c.ev_ids, 0)) != hipSuccess)
+                        return hip_fail(e, "side stream wait");
+                    copies = true;
+                }
+                e = hipMemcpyAsync(L->w.slots + (size_t)slot * L->rec_bytes,
+                                   L->w.host_pool + (size_t)ex * L->rec_bytes, L->rec_bytes,
+                                   hipMemcpyHostToDevice, c.side);
+                if (e != hipSuccess) return hip_fail(e, "expert copy into its slot");
             }
-            e = hipMemcpyAsync(L->w.slots + (size_t)slot * L->rec_bytes,
-                               L->w.host_pool + (size_t)ex * L->rec_bytes, L->rec_bytes,
-                               hipMemcpyHostToDevice, c.side);
-            if (e != hipSuccess) return hip_fail(e, "expert copy into its slot");
         }
         c.last_use[slot] = c.tick;
         c.h_slots[j] = slot;
     }
-    e = hipMemcpyAsync(ws + o.slot_ids, c.h_slots, sizeof(int32_t) * k, hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "slot table copy");
+    for (int j = 0; j < k; ++j) fa.slot_of[j] = c.h_slots[j];  // by value: no copy to the device
+    if (fetch.n && (e = launch_fetch(fetch, s)) != hipSuccess) return hip_fail(e, "expert fetch launch");
     const int routed_units = k * L->blk_r;
     // shared expert first, overlapping the copies
     if ((e = decode_units(L, fa, 1, routed_units, L->sh_split * L->blk_s, s)) != hipSuccess)
@@ -632,6 +648,7 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
     if (w->slots && (st = check_device_ptr(w->slots, "slots")) != MOE_OK) return st;
     if (w->selection_bias && (st = check_device_ptr(w->selection_bias, "selection_bias")) != MOE_OK)
         return st;
+    const uint8_t* host_pool_dev = nullptr;
     if (w->host_pool) {
         hipPointerAttribute_t attr;
         if (hipPointerGetAttributes(&attr, w->host_pool) != hipSuccess ||
@@ -639,12 +656,14 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
             (void)hipGetLastError();
             return fail(MOE_ERR_NOT_PINNED, "host_pool must be page-locked host memory (hipHostMalloc)");
         }
+        host_pool_dev = (const uint8_t*)attr.devicePointer;
     }
 
     moe_layer* L = new (std::nothrow) moe_layer();
     if (!L) return fail(MOE_ERR_NOMEM, "host allocation failed");
     L->d = d;
     L->w = *w;
+    L->host_pool_dev = host_pool_dev;
     L->bits = d.bits == 2 ? 2 : 4;
     L->rec_bytes = moe_expert_record_bytes_bits(d.hidden, d.inter, L->bits);
     L->shared_rec_bytes = d.shared_inter ? moe_expert_record_bytes_bits(d.hidden, d.shared_inter, L->bits) : 0;

@@ -267,11 +267,12 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
  * then the least recently used, then the lowest slot; MOE_CACHE_LRU (the
  * per-layer LRU of the Colibri README) the least recently used, then the
  * lowest slot.
- * Misses are copied with hipMemcpyAsync from host_pool on a side stream owned
- * by the handle while the shared expert's gate/up runs; the routed kernels
- * wait for the copies.  The handle owns the side stream, two events and two
- * small page-locked staging buffers.  Results are bit-identical to the
- * resident path for the same records.
+ * Misses are copied into their slots by a kernel on the call's stream that
+ * reads host_pool through its device mapping (or, when the pool has none, or
+ * while prefetch copies are pending, with hipMemcpyAsync on a side stream owned
+ * by the handle, which the routed kernels wait for).  The handle owns the side
+ * stream, two events and two small page-locked staging buffers.  Results are
+ * bit-identical to the resident path for the same records.
  * moe_cache_stats returns the hits and misses so far.  Errors: ARG, STATE. */
 moe_status moe_cache_stats(moe_layer_t layer, uint64_t* hits, uint64_t* misses);
 
