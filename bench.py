@@ -55,14 +55,14 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 62764.84 KiB x 2.00 + WRITE_SIZE 161.33 KiB x 1.00 per launch
-    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128702578, "moe_kernels.hip", "51232b733de4698f"),
-    # FETCH_SIZE 12340.25 KiB x 2.00 + WRITE_SIZE 41.88 KiB x 1.00 per launch (the launch
+    # FETCH_SIZE 62898.75 KiB x 2.00 + WRITE_SIZE 161.00 KiB x 1.00 per launch
+    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128976569, "moe_kernels.hip", "bc062b8896313720"),
+    # FETCH_SIZE 12344.18 KiB x 2.00 + WRITE_SIZE 41.88 KiB x 1.00 per launch (the launch
     # also runs the router)
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25314727, "moe_kernels.hip", "51232b733de4698f"),
-    # FETCH_SIZE 1833656.03 KiB x 2.00 + WRITE_SIZE 5756.59 KiB x 1.00 per launch (mean over
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25322792, "moe_kernels.hip", "bc062b8896313720"),
+    # FETCH_SIZE 1833708.04 KiB x 2.00 + WRITE_SIZE 5757.18 KiB x 1.00 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761075911, "moe_prefill.hip", "e80ed9639065bbdb"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761185715, "moe_prefill.hip", "7e251e45206dc978"),
 }
 
 
