@@ -47,6 +47,7 @@ struct SlotCache {
     std::vector<uint64_t> last_use;   // [n_slots]
     std::vector<char> pinned;         // [n_slots]
     std::vector<char> prefetched;     // [n_slots]: entered by a prefetch, not yet selected
+    std::vector<char> side_writing;   // [n_slots]: a copy into the slot may be pending on `side`
     int policy = MOE_CACHE_LFU;
     uint64_t tick = 0, hits = 0, misses = 0;
     uint64_t prefetch_issued = 0, prefetch_used = 0;
@@ -453,18 +454,25 @@ int victim_slot(const SlotCache& c, const int32_t* keep, int n) {
 }
 
 // Routed + shared FFN of one decode token through the slot cache.  ids are on
-// the device (written earlier on `s`).  The host reads them, updates the LFU,
-// copies the missing records into their slots on the side stream, runs the
-// shared expert's gate/up meanwhile, then the routed gate/up and the down
-// kernel once the copies have landed.
+// the device (written earlier on `s`).  They are copied to pinned host memory,
+// and the shared expert's gate/up units are queued before the host waits for
+// them: those need no selection, so they run meanwhile.  The host then
+// updates the policy's state, has the missing records copied into their slots
+// (k_fetch on `s`, or copies on the side stream behind pending prefetches),
+// and queues the routed gate/up and the down kernel behind the copies.
+// ev_ids marks the point after every earlier reader of the slots: copies on
+// the side stream wait for it.
 moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayout& o,
                       uint8_t* ws, hipStream_t s) {
     SlotCache& c = L->cache;
     const int k = L->d.top_k;
+    const int routed_units = k * L->blk_r;
     hipError_t e = hipMemcpyAsync(c.h_ids, ids, sizeof(int32_t) * k, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipEventRecord(c.ev_ids, s);
-    if (e == hipSuccess) e = hipEventSynchronize(c.ev_ids);
     if (e != hipSuccess) return hip_fail(e, "reading the selected experts");
+    if ((e = decode_units(L, fa, 1, routed_units, L->sh_split * L->blk_s, s)) != hipSuccess)
+        return hip_fail(e, "gate/up launch");
+    if ((e = hipEventSynchronize(c.ev_ids)) != hipSuccess) return hip_fail(e, "reading the selected experts");
     ++c.tick;
     for (int j = 0; j < k; ++j) {
         const int ex = c.h_ids[j];
@@ -472,10 +480,10 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
             return fail(MOE_ERR_ARG, "selected expert id out of range");
     }
     bool copies = false;
-    // misses copied by a kernel on `s` when the pool is device-mapped and no
-    // prefetch copies are pending on the side stream (else on the side stream,
-    // behind them: no wait between the streams before the copies)
-    const bool fetch_kernel = L->host_pool_dev && !c.side_pending;
+    // misses copied by a kernel on `s` when the pool is device-mapped, except
+    // into a slot that a pending side-stream copy may still be writing (a
+    // prefetched expert evicted before use): that miss goes to the side
+    // stream, behind the copy
     FetchArgs fetch{};
     fetch.src = L->host_pool_dev;
     fetch.dst = L->w.slots;
@@ -501,7 +509,7 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
             c.expert_in[slot] = ex;
             c.slot_of[ex] = slot;
             c.prefetched[slot] = 0;
-            if (fetch_kernel) {
+            if (L->host_pool_dev && !c.side_writing[slot]) {
                 fetch.src_rec[fetch.n] = ex;
                 fetch.dst_slot[fetch.n] = slot;
                 ++fetch.n;
@@ -522,15 +530,12 @@ moe_status cached_ffn(moe_layer* L, const int32_t* ids, FfnArgs fa, const WsLayo
     }
     for (int j = 0; j < k; ++j) fa.slot_of[j] = c.h_slots[j];  // by value: no copy to the device
     if (fetch.n && (e = launch_fetch(fetch, s)) != hipSuccess) return hip_fail(e, "expert fetch launch");
-    const int routed_units = k * L->blk_r;
-    // shared expert first, overlapping the copies
-    if ((e = decode_units(L, fa, 1, routed_units, L->sh_split * L->blk_s, s)) != hipSuccess)
-        return hip_fail(e, "gate/up launch");
     if (copies || c.side_pending) {  // this call's copies and any earlier prefetch copies
         if ((e = hipEventRecord(c.ev_copies, c.side)) != hipSuccess ||
             (e = hipStreamWaitEvent(s, c.ev_copies, 0)) != hipSuccess)
             return hip_fail(e, "copy ordering");
         c.side_pending = false;
+        std::fill(c.side_writing.begin(), c.side_writing.end(), 0);
     }
     if ((e = decode_units(L, fa, 1, 0, routed_units, s)) != hipSuccess)
         return hip_fail(e, "gate/up launch");
@@ -567,12 +572,15 @@ moe_status prefetch_place(moe_layer* L, const int32_t* pred, int n) {
                 return hip_fail(e, "side stream wait");
             waited = true;
         }
+        // DMA copies: they run beside the other layers' kernels without
+        // taking CUs (a copy kernel there slowed those kernels down)
         e = hipMemcpyAsync(L->w.slots + (size_t)slot * L->rec_bytes,
                            L->w.host_pool + (size_t)ex * L->rec_bytes, L->rec_bytes,
                            hipMemcpyHostToDevice, c.side);
         if (e != hipSuccess) return hip_fail(e, "prefetch copy into its slot");
         ++c.prefetch_issued;
         c.side_pending = true;
+        c.side_writing[slot] = 1;
     }
     return MOE_OK;
 }
@@ -713,6 +721,7 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
         c.last_use.assign(d.n_slots, 0);
         c.pinned.assign(d.n_slots, 0);
         c.prefetched.assign(d.n_slots, 0);
+        c.side_writing.assign(d.n_slots, 0);
         c.policy = d.cache_policy;
         hipError_t e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c.ev_ids, hipEventDisableTiming);
@@ -947,6 +956,7 @@ moe_status moe_cache_pin(moe_layer_t L, const int32_t* experts, int32_t n, void*
         if (e == hipSuccess) e = hipStreamWaitEvent(s, c.ev_copies, 0);
         if (e != hipSuccess) return hip_fail(e, "copy ordering");
         c.side_pending = false;
+        std::fill(c.side_writing.begin(), c.side_writing.end(), 0);
     }
     std::fill(c.pinned.begin(), c.pinned.end(), 0);
     ++c.tick;

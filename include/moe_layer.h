@@ -269,8 +269,11 @@ moe_status moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const 
  * lowest slot.
  * Misses are copied into their slots by a kernel on the call's stream that
  * reads host_pool through its device mapping (or, when the pool has none, or
- * while prefetch copies are pending, with hipMemcpyAsync on a side stream owned
- * by the handle, which the routed kernels wait for).  The handle owns the side
+ * into a slot that a pending prefetch copy may still be writing, on a side
+ * stream owned by the handle, behind that copy; the routed kernels wait for
+ * the side stream).  The shared expert's
+ * gate/up is queued before the host waits for the ids, so it runs during that
+ * wait rather than beside the copies.  The handle owns the side
  * stream, two events and two small page-locked staging buffers.  Results are
  * bit-identical to the resident path for the same records.
  * moe_cache_stats returns the hits and misses so far.  Errors: ARG, STATE. */
@@ -299,7 +302,7 @@ moe_status moe_cache_pin(moe_layer_t layer, const int32_t* experts, int32_t n, v
  * predicted ids, and copies every predicted expert that is not resident from
  * host_pool into a free slot, else into the slot the cache policy would evict
  * (never a pinned slot or another predicted expert; with none left the rest
- * are skipped), on the handle's side stream, ordered after the layer's own
+ * are skipped), on the handle's side stream (DMA copies), ordered after the layer's own
  * earlier kernels that read its slots (not after other work on `stream`).
  * The next compute call on the layer waits for those copies
  * before it reads any slot.  Prefetching changes only which experts are
