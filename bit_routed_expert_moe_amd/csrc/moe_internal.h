@@ -166,7 +166,9 @@ struct PrefillArgs {
     int H, E, I, Is, k, T, P, Imax, tile_cap, xparts, bits;
 };
 
-constexpr int kFetchBlocksPerRecord = 64;  // k_fetch workgroups per record
+// k_fetch workgroups per record: 4 to 16 measured alike on the out-of-core
+// stack, 64 and more 7 % slower (too many host reads in flight at once)
+constexpr int kFetchBlocksPerRecord = 8;
 // Missed experts' records copied by a kernel from the pinned host pool (read
 // over PCIe through its device mapping) into their HBM slots.
 struct FetchArgs {

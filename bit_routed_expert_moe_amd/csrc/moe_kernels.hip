@@ -949,7 +949,8 @@ __global__ void k_clear_word(uint32_t* p) { *p = 0u; }
 
 // k_fetch: grid (blocks per record, n).  Each workgroup copies an interleaved
 // share of one record's 16-byte vectors, four loads in flight per thread
-// (the loads cross PCIe, so many must be outstanding).
+// (the loads cross PCIe: enough must be outstanding to cover its latency,
+// and not so many that they slow each other down).
 __global__ __launch_bounds__(kBlock) void k_fetch(FetchArgs f) {
     const int r = blockIdx.y;
     const u32x4* src = (const u32x4*)(f.src + (size_t)f.src_rec[r] * f.rec_bytes);
