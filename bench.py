@@ -55,14 +55,14 @@ PEAK_HBM_GBS = 8000.0
 # of them changes.
 KERNEL_HEADERS = ("moe_device.h", "moe_internal.h")
 TRAFFIC = {
-    # FETCH_SIZE 62898.75 KiB x 2.00 + WRITE_SIZE 161.00 KiB x 1.00 per launch
-    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128976569, "moe_kernels.hip", "bc062b8896313720"),
-    # FETCH_SIZE 12344.18 KiB x 2.00 + WRITE_SIZE 41.88 KiB x 1.00 per launch (the launch
+    # FETCH_SIZE 62870.48 KiB x 2.00 + WRITE_SIZE 160.84 KiB x 1.00 per launch
+    ("glm_h6144_e256_l40_zipf", "k_gate_up"): (128918532, "moe_kernels.hip", "f321826cbb94aa76"),
+    # FETCH_SIZE 12344.51 KiB x 2.00 + WRITE_SIZE 41.88 KiB x 1.00 per launch (the launch
     # also runs the router)
-    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25322792, "moe_kernels.hip", "bc062b8896313720"),
-    # FETCH_SIZE 1833708.04 KiB x 2.00 + WRITE_SIZE 5757.18 KiB x 1.00 per launch (mean over
+    ("gemma_a4b_h2816_e128_l30", "k_gate_up"): (25323475, "moe_kernels.hip", "f321826cbb94aa76"),
+    # FETCH_SIZE 1833452.71 KiB x 2.00 + WRITE_SIZE 5756.12 KiB x 1.00 per launch (mean over
     # the bench's 32 distinct chunks)
-    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3761185715, "moe_prefill.hip", "7e251e45206dc978"),
+    ("glm_prefill_h6144_e256_t128", "k_gu_grouped"): (3760662184, "moe_prefill.hip", "5f90596f37f6cfc7"),
 }
 
 
