@@ -194,3 +194,37 @@ def test_prefetch_argument_errors(orc):
     with pytest.raises(MoeError) as ei:
         dl.layer_obj.prefetch_stats()
     assert ei.value.status == -7
+
+
+def test_prefetched_slot_evicted_before_use(orc):
+    """Wrong predictions of never-selected experts, issued right before a token
+    whose selection misses: the LFU evicts exactly those prefetched slots (count
+    0), so each miss lands in a slot whose prefetch copy may still be running on
+    the side stream.  Such a miss must be copied behind that copy, not beside
+    it: the output stays bit-identical to the resident layer's, every step."""
+    H, E, I, k, Is, n_slots = 512, 48, 192, 8, 256, 12
+    dl = DeviceLayer(0xB17E0730, 0, H, E, I, k, Is, "bf16")
+    cached, _, _ = cached_twin(dl, n_slots, "lfu")
+    model = CacheModel(n_slots, E, "lfu")
+    ws_r, ws_c = dl.layer_obj.workspace(1), cached.workspace(1)
+    evicted_prefetch = 0
+    for step in range(24):
+        xq, xd = dl.natural_token(orc, step)
+        ids = orc.route(dl.rq, dl.rs, xd, k)[0].tolist()
+        if step >= 2:  # the cache is full: predict experts never selected and not about to be
+            pred = [e for e in range(E) if model.uses[e] == 0 and e not in model.where and e not in ids][:k]
+            if pred:
+                cached.cache_prefetch_ids(pred)
+                model.prefetch(pred)
+        before = {q: model.holder[q] for q in range(n_slots) if model.pref[q]}
+        x = to_dev(xq[None], "bf16")
+        r = dl.layer_obj.forward(x, ws_r)
+        c = cached.forward(x, ws_c)
+        for a_, b_ in zip(r, c):
+            assert torch.equal(a_, b_), f"step {step}: cached result differs from resident"
+        model.token(ids)
+        evicted_prefetch += sum(1 for q, e in before.items() if model.holder[q] != e)
+    assert cached.cache_stats() == (model.hits, model.misses)
+    assert cached.prefetch_stats() == (model.issued, model.used)
+    assert evicted_prefetch >= 8, f"only {evicted_prefetch} prefetched slots were evicted before use"
+    print(f"prefetched slots evicted before use: {evicted_prefetch}; misses {model.misses}")
