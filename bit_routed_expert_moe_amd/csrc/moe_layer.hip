@@ -931,6 +931,26 @@ moe_status moe_layer_forward_noalloc(moe_layer_t L, const void* x, int32_t T, in
     return st;
 }
 
+moe_status moe_cache_usage(moe_layer_t L, uint64_t* counts) {
+    if (!L || !counts) return fail(MOE_ERR_ARG, "null argument");
+    if (!L->cache.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    std::copy(L->cache.count.begin(), L->cache.count.end(), counts);
+    return MOE_OK;
+}
+
+moe_status moe_cache_pin_hottest(moe_layer_t L, const uint64_t* counts, int32_t n, void* stream) {
+    if (!L) return fail(MOE_ERR_ARG, "null layer handle");
+    const SlotCache& c = L->cache;
+    if (!c.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");
+    if (n < 0 || n > c.n_slots - L->d.top_k) return fail(MOE_ERR_ARG, "n must be in 0..n_slots - top_k");
+    const int E = L->d.n_experts;
+    const uint64_t* u = counts ? counts : c.count.data();
+    std::vector<int32_t> order(E);
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(), [u](int32_t a, int32_t b) { return u[a] > u[b]; });
+    return moe_cache_pin(L, order.data(), n, stream);
+}
+
 moe_status moe_cache_stats(moe_layer_t L, uint64_t* hits, uint64_t* misses) {
     if (!L || !hits || !misses) return fail(MOE_ERR_ARG, "null argument");
     if (!L->cache.n_slots) return fail(MOE_ERR_STATE, "layer has no slot cache");

@@ -27,6 +27,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIG
 EXPORTS = ["moe_expert_record_bytes", "moe_expert_record_bytes_bits", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route_topk", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_layer_forward_noalloc", "moe_stack_forward", "moe_cache_stats", "moe_cache_pin",
+           "moe_cache_usage", "moe_cache_pin_hottest",
            "moe_cache_prefetch", "moe_cache_prefetch_ids", "moe_cache_prefetch_stats",
            "moe_poll_device_error", "moe_stream_read",
            "moe_profile_start", "moe_profile_stop", "moe_profile_read",
@@ -84,6 +85,8 @@ def lib() -> C.CDLL:
         L.moe_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
         L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
         L.moe_cache_pin.argtypes = [vp, C.POINTER(C.c_int32), i32, vp]
+        L.moe_cache_usage.argtypes = [vp, C.POINTER(C.c_uint64)]
+        L.moe_cache_pin_hottest.argtypes = [vp, C.POINTER(C.c_uint64), i32, vp]
         L.moe_cache_prefetch.argtypes = [vp, vp, i32, vp, C.POINTER(C.c_int32), vp]
         L.moe_cache_prefetch_ids.argtypes = [vp, C.POINTER(C.c_int32), i32, vp]
         L.moe_cache_prefetch_stats.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
@@ -96,7 +99,8 @@ def lib() -> C.CDLL:
         for f in ["moe_layer_create", "moe_layer_destroy", "moe_route_topk", "moe_expert_ffn",
                   "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_stack_forward",
                   "moe_poll_device_error", "moe_stream_read", "moe_profile_start", "moe_profile_stop",
-                  "moe_cache_stats", "moe_cache_pin", "moe_cache_prefetch", "moe_cache_prefetch_ids",
+                  "moe_cache_stats", "moe_cache_pin", "moe_cache_usage", "moe_cache_pin_hottest",
+                  "moe_cache_prefetch", "moe_cache_prefetch_ids",
                   "moe_cache_prefetch_stats"]:
             getattr(L, f).restype = i32
         _LIB = L
@@ -265,6 +269,24 @@ class Layer:
         """Pin these expert ids into the slot cache (replacing any pinned set)."""
         ids = (C.c_int32 * max(len(experts), 1))(*[int(e) for e in experts])
         _check(lib().moe_cache_pin(self.handle, ids, len(experts), _stream()))
+
+    def cache_usage(self) -> list[int]:
+        """The per-expert selection counts (the usage heatmap), [E]."""
+        out = (C.c_uint64 * self.n_experts)()
+        _check(lib().moe_cache_usage(self.handle, out))
+        return [int(v) for v in out]
+
+    def cache_pin_hottest(self, n: int, counts=None) -> None:
+        """Pin the n experts with the largest counts (a saved heatmap of E
+        non-negative integers, or this layer's own when counts is None), ties
+        to the lower id."""
+        arr = None
+        if counts is not None:
+            vals = [int(v) for v in counts]
+            if len(vals) != self.n_experts or min(vals) < 0:
+                raise ValueError(f"counts must be {self.n_experts} non-negative integers")
+            arr = (C.c_uint64 * self.n_experts)(*vals)
+        _check(lib().moe_cache_pin_hottest(self.handle, arr, int(n), _stream()))
 
     def cache_prefetch(self, x_hint: torch.Tensor, n_predict: int | None = None,
                        ws: torch.Tensor | None = None) -> list[int]:

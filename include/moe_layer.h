@@ -289,6 +289,19 @@ moe_status moe_cache_stats(moe_layer_t layer, uint64_t* hits, uint64_t* misses);
  * neither hit nor miss.  Errors: ARG, STATE (no slot cache), HIP. */
 moe_status moe_cache_pin(moe_layer_t layer, const int32_t* experts, int32_t n, void* stream);
 
+/* Usage-learned pinning: the persistent usage heatmap of the Colibri README
+ * ("Learn", `.coli_usage`), which pins the hottest experts at startup.  The
+ * heatmap is the handle's per-expert selection count (+1 per selection, hit
+ * or miss, never decayed: the LFU's own counts).
+ *   moe_cache_usage: counts  host [E], receives the counts.  Errors: ARG, STATE.
+ *   moe_cache_pin_hottest: pins the n experts with the largest counts in
+ *     `counts` (host [E]: a heatmap saved by an earlier run, or NULL for this
+ *     handle's own), ties to the lower id, exactly as moe_cache_pin would pin
+ *     that list (same n limits, slots, copies on `stream`, errors).
+ * Errors: ARG, STATE (no slot cache), HIP. */
+moe_status moe_cache_usage(moe_layer_t layer, uint64_t* counts);
+moe_status moe_cache_pin_hottest(moe_layer_t layer, const uint64_t* counts, int32_t n, void* stream);
+
 /* Router lookahead: starts copying the experts this layer is predicted to
  * select before its own router runs, from a hint vector that is available
  * earlier -- the next layer's router applied to the current layer's state, as

@@ -103,6 +103,9 @@ def test_create_rejects_missing_and_misaligned_pointers():
 def test_null_handles():
     lib = L.lib()
     assert lib.moe_cache_pin(None, None, 0, None) == -1
+    assert lib.moe_cache_pin_hottest(None, None, 0, None) == -1
+    counts = (C.c_uint64 * 4)()
+    assert lib.moe_cache_usage(None, counts) == -1
     assert lib.moe_cache_prefetch(None, None, 8, None, None, None) == -1
     assert lib.moe_cache_prefetch_ids(None, None, 1, None) == -1
     a, b = C.c_uint64(), C.c_uint64()

@@ -89,11 +89,13 @@ def cached_twin(dl, n_slots, policy="lfu"):
 
 @pytest.mark.parametrize("policy,zipf,pin", [
     ("lfu", False, False), ("lfu", True, False), ("lru", True, False),
-    ("lfu", True, True), ("lru", True, True),
+    ("lfu", True, "stats"), ("lru", True, "stats"), ("lfu", True, "learned"), ("lru", True, "learned"),
 ])
 def test_cached_layer_matches_resident_and_policy(orc, policy, zipf, pin):
     """48 decode steps; with `pin`, the 4 most used experts of the first 16
-    steps (a statistics pass) are pinned before step 16."""
+    steps are pinned before step 16: counted here from the oracle's ids
+    ("stats", a statistics pass) or taken by the layer from its own usage
+    heatmap ("learned"), which must equal those counts."""
     H, E, I, k, Is, n_slots = 512, 48, 192, 8, 256, 12
     dl = DeviceLayer(0xB17E0500 + zipf, 0, H, E, I, k, Is, "bf16")
     cached, _, _ = cached_twin(dl, n_slots, policy)
@@ -107,7 +109,11 @@ def test_cached_layer_matches_resident_and_policy(orc, policy, zipf, pin):
         if pin and step == 16:
             counts = np.bincount(np.concatenate(oracle_ids), minlength=E)
             pinned = tuple(int(e) for e in sorted(range(E), key=lambda e: (-counts[e], e))[:n_slots - k])
-            cached.cache_pin(pinned)
+            if pin == "stats":
+                cached.cache_pin(pinned)
+            else:
+                assert cached.cache_usage() == counts.tolist()
+                cached.cache_pin_hottest(n_slots - k)
         if zr is None:
             xq, xd = dl.natural_token(orc, step)
         else:
@@ -240,3 +246,50 @@ def test_cached_layer_large_hidden_matches_resident(orc):
         assert r[0].cpu().numpy()[0].tolist() == rid.tolist()
         worst = max(worst, rel_err(r[2].cpu().numpy()[0], ry))
     assert worst <= Y_TOL, worst
+
+
+def test_saved_heatmap_pins_the_hottest_at_startup(orc, tmp_path):
+    """The pages' persistent usage heatmap: the per-expert counts of one run,
+    saved to a file, pin the hottest experts of a fresh layer before its first
+    token.  Every later selection of a pinned expert is a hit, hits and misses
+    equal the simulation with that pinned set, and outputs stay bit-identical
+    to the resident layer."""
+    H, E, I, k, Is, n_slots = 512, 48, 192, 8, 256, 12
+    dl = DeviceLayer(0xB17E0510, 0, H, E, I, k, Is, "bf16")
+    Wd = dl.rq.astype(np.float64) * dl.rs.view(np.float16).astype(np.float64)[:, None]
+    zr = synth.ZipfRealiser(Wd, 1.1, dl.seed, 0)
+    toks = []
+    for step in range(40):
+        for a in range(50):
+            xq = synth.quantize_act(zr.activations(step, a)[0], "bf16")
+            xd = orc.act_to_f64("bf16", xq)
+            if gap_ok(orc.router_logits(dl.rq, dl.rs, xd), k):
+                break
+        toks.append((xq, orc.route(dl.rq, dl.rs, xd, k)[0]))
+    ws_r = dl.layer_obj.workspace(1)
+    first, _, _ = cached_twin(dl, n_slots, "lfu")
+    ws_1 = first.workspace(1)
+    for xq, _ in toks[:16]:
+        first.forward(to_dev(xq[None], "bf16"), ws_1)
+    heat = first.cache_usage()
+    assert heat == np.bincount(np.concatenate([ids for _, ids in toks[:16]]), minlength=E).tolist()
+    np.save(tmp_path / "usage.npy", np.array(heat, dtype=np.uint64))
+    saved = np.load(tmp_path / "usage.npy").tolist()
+    pinned = tuple(sorted(range(E), key=lambda e: (-saved[e], e))[:n_slots - k])
+    second, _, _ = cached_twin(dl, n_slots, "lfu")
+    second.cache_pin_hottest(n_slots - k, saved)
+    ws_2 = second.workspace(1)
+    for step, (xq, ids) in enumerate(toks[16:]):
+        x = to_dev(xq[None], "bf16")
+        r = dl.layer_obj.forward(x, ws_r)
+        c = second.forward(x, ws_2)
+        for a_, b_ in zip(r, c):
+            assert torch.equal(a_, b_), f"step {16 + step}: cached result differs from resident"
+        assert r[0].cpu().numpy()[0].tolist() == ids.tolist()
+    sim = cache_simulation([ids for _, ids in toks[16:]], n_slots, E, "lfu", pinned, 0)
+    assert second.cache_stats() == sim[:2]
+    later = sum(int(e in pinned) for _, ids in toks[16:] for e in ids)
+    assert sim[2] == later > 0
+    assert second.cache_usage() == np.bincount(np.concatenate([ids for _, ids in toks[16:]]), minlength=E).tolist()
+    print(f"saved heatmap pins {pinned}: {later} selections of them, all hits; "
+          f"hits {sim[0]} misses {sim[1]}")
