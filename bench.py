@@ -445,8 +445,13 @@ def run_cached(args, wl):
     torch.cuda.synchronize()
     if args.pin:
         for l in range(L):
-            top = sorted(range(E), key=lambda e: (-counts[l, e], e))[:args.pin]
-            layers[l].cache_pin(top)
+            if args.pin_source == "learned":  # the layer's own usage heatmap
+                if layers[l].cache_usage() != counts[l].tolist():
+                    raise RuntimeError(f"layer {l}: usage heatmap differs from the warm-up's selections")
+                layers[l].cache_pin_hottest(args.pin)
+            else:
+                top = sorted(range(E), key=lambda e: (-counts[l, e], e))[:args.pin]
+                layers[l].cache_pin(top)
         torch.cuda.synchronize()
     h0 = sum(l_.cache_stats()[0] for l_ in layers)
     m0 = sum(l_.cache_stats()[1] for l_ in layers)
@@ -480,7 +485,9 @@ def run_cached(args, wl):
                    "routing": wl.routing, "gate": gate_desc(args), "n_slots": wl.n_slots,
                    "cache_policy": args.cache_policy, "pinned_per_layer": args.pin,
                    "lookahead": args.lookahead,
-                   "pin_source": f"expert counts over the {W} warm-up steps" if args.pin else None},
+                   "pin_source": (f"expert counts over the {W} warm-up steps" + (
+                       ", from each layer's usage heatmap" if args.pin_source == "learned" else ""))
+                   if args.pin else None},
         "stack_tok_s": round(1e3 / ms_per_step, 2),
         "hit_rate_timed": round(hit_timed, 4), "hit_rate_all_steps": round(hit_all, 4),
         "miss_bytes_per_step": int(miss_bytes_step), "h2d_bytes_per_step": int(h2d_bytes_step),
@@ -694,6 +701,9 @@ def main():
     ap.add_argument("--pin", type=int, default=0,
                     help="slot-cache workloads: pin this many experts per layer, the most used "
                          "during the warm-up steps")
+    ap.add_argument("--pin-source", choices=("stats", "learned"), default="stats",
+                    help="slot-cache workloads: the --pin set counted on the host from the warm-up's "
+                         "selections (stats) or taken by each layer from its own usage heatmap (learned)")
     ap.add_argument("--lookahead", type=int, default=0, metavar="N",
                     help="slot-cache workloads: prefetch each next layer's top N experts "
                          "from a hint (router lookahead); 0 = off")
