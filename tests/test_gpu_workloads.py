@@ -29,11 +29,11 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
+@pytest.mark.timeout(900)
 def test_gemma_stack_full_size(orc):
-    """All 30 layers, 16 decode steps through moe_stack_forward: ids bit-exact
-    and gates within 1e-6 on every token-layer, y within 2e-3 of the oracle on
-    every layer of the first 2 steps (the oracle regenerates each selected
-    record)."""
+    """All 30 layers, 16 decode steps through moe_stack_forward: ids bit-exact,
+    gates within 1e-6 and y within 2e-3 of the oracle on every token-layer (the
+    oracle regenerates each selected record)."""
     wl = synth.WORKLOADS["gemma_a4b_h2816_e128_l30"]
     L, H, S = wl.n_layers, wl.hidden, 16
     layers = [DeviceLayer(wl.seed, l, H, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act)
@@ -46,15 +46,12 @@ def test_gemma_stack_full_size(orc):
         ids, w, y = stack_forward([dl.layer_obj for dl in layers], x, ws)
         ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
         for l, dl in enumerate(layers):
-            if step < 2:
-                rid, rw, ry, _, _ = dl.oracle(orc, toks[l][1])
-                worst_y = max(worst_y, rel_err(y[l, 0], ry))
-            else:
-                rid, rw, _ = orc.route(dl.rq, dl.rs, toks[l][1], wl.top_k)
+            rid, rw, ry, _, _ = dl.oracle(orc, toks[l][1])
+            worst_y = max(worst_y, rel_err(y[l, 0], ry))
             assert ids[l, 0].tolist() == rid.tolist(), f"step {step} layer {l}"
             worst_w = max(worst_w, float(np.max(np.abs(w[l, 0] - rw))))
     print(f"gemma stack: {S} steps x {L} layers, max |w err| {worst_w:.2e}, "
-          f"max rel y err (first 2 steps) {worst_y:.2e}")
+          f"max rel y err {worst_y:.2e}")
     assert worst_w <= W_TOL and worst_y <= Y_TOL
 
 
