@@ -157,14 +157,14 @@ def test_glm_layer_zipf_grouped_path(orc):
     assert worst <= Y_TOL
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("bits", [4, 2])
 def test_glm_prefill_chunk_full_size(orc, bits):
     """GLM-scale 128-token chunk (uniform random routing realised through the
-    router) through the grouped path: every token's ids and
-    gate weights against the oracle router, outputs on 4 sampled tokens (the
-    oracle regenerates each selected record on the CPU, about a second each),
-    and the whole chunk's result permuted exactly with its tokens.  4-bit and
-    2-bit records."""
+    router) through the grouped path: every token's ids, gate weights and
+    output against the oracle (which regenerates each selected record on the
+    CPU), and the whole chunk's result permuted exactly with its tokens.
+    4-bit and 2-bit records."""
     wl = synth.WORKLOADS["glm_prefill_h6144_e256_t128"]
     dl = DeviceLayer(wl.seed, 0, wl.hidden, wl.n_experts, wl.inter, wl.top_k, wl.shared_inter, wl.act,
                      bits=bits)
@@ -192,12 +192,13 @@ def test_glm_prefill_chunk_full_size(orc, bits):
         worst_w = max(worst_w, float(np.max(np.abs(w_h[t] - rw))))
     assert worst_w <= W_TOL
     worst_y = 0.0
-    for t in (0, 41, 86, 127):
+    for t in range(wl.n_tokens):
         _, _, ry, _, _ = dl.oracle(orc, toks[t][1])
         worst_y = max(worst_y, rel_err(y_h[t], ry))
-        print(f"glm prefill token {t}: rel y err {rel_err(y_h[t], ry):.2e}", flush=True)
+        if t % 32 == 31:
+            print(f"glm prefill tokens 0..{t}: max rel y err {worst_y:.2e}", flush=True)
     print(f"{bits}-bit glm prefill chunk: {wl.n_tokens} tokens, max |w err| {worst_w:.2e}, "
-          f"max rel y err (sampled) {worst_y:.2e}")
+          f"max rel y err {worst_y:.2e}")
     assert worst_y <= Y_TOL
     perm = np.random.default_rng(2).permutation(wl.n_tokens)
     ids2, w2, y2 = dl.layer_obj.forward(to_dev(xq[perm], wl.act), ws)
